@@ -1,0 +1,128 @@
+"""Pins for the oracle's swap_in (hit/miss split + LRU hot buffer), CPU only."""
+
+from collections import OrderedDict
+
+import numpy as np
+import pytest
+
+from oracle import HotState, build_hot_state, resolve_topk, swap_in
+from tests.helpers import check_state_invariants, raw
+from workloads import generate, spec
+
+
+def _setup(name, **over):
+    s = spec(name, **over)
+    w = generate(s)
+    pool = raw(w.kv_pool)
+    st = build_hot_state(w.init_pos, w.init_stamp, w.seq_len, w.block_table, s.block_size, pool)
+    slots, _ = resolve_topk(w.topk_pos, w.req_id, w.causal_limit, w.block_table,
+                            s.block_size, s.block_size, s.num_reqs)
+    return s, w, pool, st, slots
+
+
+@pytest.mark.parametrize("name,over", [("tiny", {}), ("tiny", {"seq_rule": ("fixed", [10, 70])}),
+                                       ("mtp_swap", {"num_reqs": 3, "seq_rule": ("const", 6000),
+                                                     "capacity": 1024, "topk": 256}),
+                                       ("mixed_finalize", {"num_reqs": 4, "vocab": 64, "topk": 128,
+                                                           "capacity": 512})])
+def test_swap_invariants_over_waves(name, over):
+    s, w, pool, st, slots = _setup(name, **over)
+    check_state_invariants(st, pool)
+    B = s.num_reqs
+    for r in range(s.rows_per_req):
+        wave = slots[r * B:(r + 1) * B]
+        before = st.copy()
+        hot_idx, mc, mp = swap_in(st, wave, s.tick0 + r, pool)
+        check_state_invariants(st, pool)
+        valid = wave >= 0
+        # every valid entry is resident afterwards, and hot_idx names the slot holding it
+        flat = st.slot_loc.reshape(-1)
+        assert (flat[hot_idx[valid]] == wave[valid]).all()
+        assert (hot_idx[~valid] == -1).all()
+        # hot_idx stays inside the request's own slot range
+        b_of = np.repeat(np.arange(B), s.topk).reshape(B, s.topk)
+        assert ((hot_idx[valid] // s.capacity) == b_of[valid]).all()
+        # hits + misses = valid; misses are exactly the entries absent before the call
+        was_hit = valid & (before.loc_to_hot[np.where(valid, wave, 0)] >= 0)
+        assert np.array_equal(mc, (valid & ~was_hit).sum(1))
+        for b in range(B):
+            assert mp[b, :mc[b]].tolist() == np.nonzero(valid[b] & ~was_hit[b])[0].tolist()
+            assert (mp[b, mc[b]:] == -1).all()
+        # hit entries keep their slot; touched slots carry the tick
+        assert (hot_idx[was_hit] == before.loc_to_hot[wave[was_hit]]).all()
+        assert (st.slot_stamp.reshape(-1)[hot_idx[valid]] == s.tick0 + r).all()
+        # slots not touched by this wave keep their stamps unless they were evicted to host a miss
+        untouched = np.ones(B * s.capacity, dtype=bool)
+        untouched[hot_idx[valid]] = False
+        assert (st.slot_stamp.reshape(-1)[untouched] == before.slot_stamp.reshape(-1)[untouched]).all()
+
+
+def _empty_state(B, cap, host_rows, d):
+    return HotState(cap, np.full((B, cap), -1, np.int32), np.full((B, cap), -1, np.int32),
+                    np.full(host_rows, -1, np.int32), np.zeros((B * cap, d), np.float32))
+
+
+def test_swap_empty_buffer_misses_fill_slots_in_order():
+    rng = np.random.default_rng(0)
+    pool = rng.standard_normal((200, 8)).astype(np.float32)
+    st = _empty_state(2, 10, 200, 8)
+    wave = np.array([[50, -1, 3, 77, 12, -1], [150, 151, 199, -1, -1, 160]], np.int32)
+    hot_idx, mc, mp = swap_in(st, wave, 5, pool)
+    assert mc.tolist() == [4, 4]
+    assert hot_idx.tolist() == [[0, -1, 1, 2, 3, -1], [10, 11, 12, -1, -1, 13]]
+    assert mp.tolist() == [[0, 2, 3, 4, -1, -1], [0, 1, 2, 5, -1, -1]]
+    assert np.array_equal(st.hot_kv[[0, 1, 2, 3]], pool[[50, 3, 77, 12]])
+    check_state_invariants(st, pool)
+
+
+def test_swap_all_resident_only_stamps_change():
+    s, w, pool, st, slots = _setup("tiny")
+    B = s.num_reqs
+    # make a wave of rows the buffer already holds
+    wave = np.full((B, s.topk), -1, np.int32)
+    for b in range(B):
+        held = st.slot_loc[b][st.slot_loc[b] >= 0][: s.topk]
+        wave[b, :len(held)] = held
+    before = st.copy()
+    hot_idx, mc, _ = swap_in(st, wave, 77, pool)
+    assert (mc == 0).all()
+    assert np.array_equal(st.slot_loc, before.slot_loc)
+    assert np.array_equal(st.loc_to_hot, before.loc_to_hot)
+    assert np.array_equal(st.hot_kv, before.hot_kv)
+    touched = np.zeros(B * s.capacity, dtype=bool)
+    touched[hot_idx[wave >= 0]] = True
+    assert (st.slot_stamp.reshape(-1)[touched] == 77).all()
+    assert np.array_equal(st.slot_stamp.reshape(-1)[~touched], before.slot_stamp.reshape(-1)[~touched])
+
+
+def test_swap_victim_set_matches_textbook_lru():
+    """With distinct stamps, the evicted set equals an OrderedDict LRU's evictions."""
+    rng = np.random.default_rng(3)
+    for trial in range(40):
+        cap, host_rows, K = 12, 60, 8
+        pool = rng.standard_normal((host_rows, 4)).astype(np.float32)
+        st = _empty_state(1, cap, host_rows, 4)
+        n_occ = int(rng.integers(0, cap + 1))
+        rows_held = rng.choice(host_rows, n_occ, replace=False)
+        slots_used = rng.choice(cap, n_occ, replace=False)
+        stamps = rng.permutation(100)[:n_occ]                 # distinct
+        lru = OrderedDict()
+        for i in np.argsort(stamps):                          # oldest first
+            st.slot_loc[0, slots_used[i]] = rows_held[i]
+            st.slot_stamp[0, slots_used[i]] = stamps[i]
+            st.loc_to_hot[rows_held[i]] = slots_used[i]
+            st.hot_kv[slots_used[i]] = pool[rows_held[i]]
+            lru[int(rows_held[i])] = True
+        wave = rng.choice(host_rows, K, replace=False).astype(np.int32)[None, :]
+        # textbook LRU: hits are protected, then misses evict from the cold end;
+        # free capacity is used before anything is evicted
+        hits = [int(x) for x in wave[0] if int(x) in lru]
+        misses = [int(x) for x in wave[0] if int(x) not in lru]
+        free = cap - len(lru)
+        n_evict = max(0, len(misses) - free)
+        evicted = [k for k in lru if k not in hits][:n_evict]
+        before = set(int(x) for x in st.slot_loc[0] if x >= 0)
+        swap_in(st, wave, 1000, pool)
+        after = set(int(x) for x in st.slot_loc[0] if x >= 0)
+        assert before - after == set(evicted), trial
+        assert after == (before - set(evicted)) | set(misses)
