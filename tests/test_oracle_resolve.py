@@ -89,3 +89,11 @@ def test_resolve_physical_block_stride():
     pos = np.array([[0, 1, 2, 3]], dtype=np.int32)
     out, _ = resolve_topk(pos, np.array([0], np.int32), np.array([4], np.int32), bt, 2, 8, 1)
     assert out[0].tolist() == [16, 17, 0, 1]
+
+
+def test_resolve_masks_position_at_causal_limit():
+    # the limit is exclusive: a query row at position p may see positions <= p only
+    bt = np.array([[0, 1, 2]], dtype=np.int32)
+    pos = np.array([[8, 9, 10]], dtype=np.int32)
+    out, v = resolve_topk(pos, np.array([0], np.int32), np.array([9], np.int32), bt, 4, 4, 1)
+    assert out[0].tolist() == [8, -1, -1] and v.tolist() == [1]

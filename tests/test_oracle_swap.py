@@ -126,3 +126,22 @@ def test_swap_victim_set_matches_textbook_lru():
         after = set(int(x) for x in st.slot_loc[0] if x >= 0)
         assert before - after == set(evicted), trial
         assert after == (before - set(evicted)) | set(misses)
+
+
+def test_swap_pairs_misses_with_victims_in_slot_order():
+    """Misses (in entry order) take the victims in ascending slot order, not LRU order."""
+    pool = np.arange(100 * 2, dtype=np.float32).reshape(100, 2)
+    st = _empty_state(1, 4, 100, 2)
+    # slot s holds host row 10+s; stamps make LRU order slot 2 (1), slot 1 (2), slot 0 (5), slot 3 (9)
+    for s, stamp in enumerate([5, 2, 1, 9]):
+        st.slot_loc[0, s], st.slot_stamp[0, s] = 10 + s, stamp
+        st.loc_to_hot[10 + s] = s
+        st.hot_kv[s] = pool[10 + s]
+    wave = np.array([[60, 13, 70]], np.int32)       # 13 hits slot 3; 60 and 70 miss
+    hot_idx, mc, mp = swap_in(st, wave, 20, pool)
+    assert mc.tolist() == [2] and mp[0, :2].tolist() == [0, 2]
+    # victims {2, 1}; ascending slot order pairs 60 -> slot 1 and 70 -> slot 2
+    assert hot_idx.tolist() == [[1, 3, 2]]
+    assert st.slot_loc[0].tolist() == [10, 60, 70, 13]
+    assert st.slot_stamp[0].tolist() == [5, 20, 20, 20]
+    assert st.loc_to_hot[11] == -1 and st.loc_to_hot[12] == -1
