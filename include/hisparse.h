@@ -1,0 +1,224 @@
+/*
+ * hisparse.h -- C ABI of the MI355X (gfx950) HiSparse sparse-decode library.
+ *
+ * The path, per decode step and per query row (the decode anchor plus any draft rows
+ * being verified):
+ *
+ *   hs_resolve_topk       request-local top-k token positions -> physical KV rows
+ *   hs_swap_in            hit/miss split against the per-request hot buffer, LRU
+ *                         victim choice, copy of the misses from the pinned host pool
+ *   hs_sparse_decode_attn attention over only the selected latent KV rows
+ *   hs_finalize_accepted  greedy acceptance of the draft rows, then keep exactly the
+ *                         target-verified prefix's KV (host pool + hot buffer)
+ *
+ * Sources (web pages describing the method):
+ *   P1  Notion page "hiSparse-MTP" -- summary (six-stage main line ending in accepted-KV
+ *       finalize) and "1. 启动阶段" (startup: the coordinator's device buffer, host
+ *       pool, LRU slots and async stream; the core-state maps).
+ *   P2  blog post "投机解码的 KV 流转：prefill 阶段 DFlash 也要吃下整个 prompt" --
+ *       worked example, sections ④ (target verify, greedy acceptance, kept KV) and ⑥.
+ *   P3  CSDN post "vllm 分析（十二）——Hisparse下篇" -- HiSparseCacheHandle.resolve_topk
+ *       listing (fully-resident conversion vs. swap-in), HiSparseHotSpec (fixed hot
+ *       blocks per request), "数据 back up" (block-row address arithmetic, pinned host
+ *       pool), build_offload_command (fully-resident batch predicate).
+ *
+ * Conventions for every call:
+ *   - All pointers are caller-owned; the library allocates nothing and keeps no state.
+ *     Pointers are DEVICE pointers unless marked HOST or PINNED HOST.
+ *   - Every call is asynchronous on `stream` (a hipStream_t; NULL = the null stream) and
+ *     returns after the launches are queued.  Validation failures return before any
+ *     launch and leave every buffer untouched.
+ *   - Query rows are laid out wave-major: row r*num_reqs + b is row r (0 = anchor) of
+ *     request b.
+ *   - Data-dependent conditions are values, not errors: positions outside the causal
+ *     limit, unmapped pages and out-of-range rows become -1 entries.
+ *   - Device buffers must not overlap unless stated.  Calls that share state buffers
+ *     must be ordered by the caller (same stream, or events).
+ */
+#ifndef HISPARSE_H
+#define HISPARSE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  HS_OK = 0,
+  HS_ERR_INVALID_ARG = -1,  /* null pointer, bad size, misaligned buffer, bad dtype      */
+  HS_ERR_CAPACITY = -2,     /* topk exceeds the hot-buffer capacity; nothing was changed */
+  HS_ERR_UNSUPPORTED = -3,  /* shape/dtype combination the kernels are not built for    */
+  HS_ERR_HIP = -4           /* a HIP runtime call or kernel launch failed                */
+} hs_status;
+
+typedef enum { HS_BF16 = 0, HS_F32 = 1 } hs_dtype;
+
+/*
+ * Per-request hot buffer ("device buffer" + "LRU slots" of P1 "1. 启动阶段"; fixed
+ * blocks per request as P3's HiSparseHotSpec).  Request b owns global slots
+ * [b*capacity, (b+1)*capacity).
+ *
+ *   slot_loc   [num_reqs*capacity] int32  host-pool row held by the slot, -1 = empty
+ *                                         (P1: slot -> physical KV loc)
+ *   slot_stamp [num_reqs*capacity] int32  tick of the slot's last use, -1 = empty
+ *                                         (P1: LRU slots)
+ *   loc_to_hot [host_rows]         int32  global slot holding the host row, or -1
+ *                                         (P1: logical loc -> physical HiSparse slot)
+ *   hot_kv     [num_reqs*capacity, row_elems] of dtype  the KV rows in the slots
+ *   host_pool  PINNED HOST [host_rows, row_elems] of dtype, device-accessible
+ *              (P3 "数据 back up": host cache in pinned DRAM)
+ *
+ * Invariants kept by hs_swap_in / hs_finalize_accepted: slot_loc and loc_to_hot are
+ * inverse on occupied slots; hot_kv[s] equals host_pool[slot_loc[s]] bit for bit.
+ * Each host row belongs to at most one request.
+ */
+typedef struct hs_hot_state {
+  int32_t num_reqs;
+  int32_t capacity;
+  int32_t *slot_loc;
+  int32_t *slot_stamp;
+  int32_t *loc_to_hot;
+  int64_t host_rows;
+  int32_t row_elems;
+  int32_t dtype;          /* hs_dtype */
+  void *hot_kv;
+  void *host_pool;
+} hs_hot_state;
+
+/*
+ * hs_resolve_topk -- P3, HiSparseCacheHandle.resolve_topk: in the fully-resident case
+ * the request-local top-k indices are converted to global cache slots through the
+ * request's block table (block size, physical block stride), with optional per-row
+ * valid counts.  P3 "数据 back up" fixes the rows of block p as p*block_size + offset.
+ *
+ *   topk_pos      [num_rows, topk] int32  token positions, -1 = padding
+ *   req_id        [num_rows] int32        request of each row
+ *   causal_limit  [num_rows] int32        positions >= limit are masked (future tokens)
+ *   block_table   [num_reqs, bt_stride] int32  physical page per logical page, -1 = none
+ *   out_slots     [num_rows, topk] int32  physical row, or -1 (in place, no compaction)
+ *   out_valid     [num_rows] int32 or NULL   number of non-negative out_slots entries
+ *
+ * Entry j of row i maps to block_table[b, t/block_size]*physical_block_stride +
+ * t%block_size when 0 <= t < causal_limit[i], t/block_size < bt_stride, the table entry
+ * is >= 0 and 0 <= b=req_id[i] < num_reqs; otherwise to -1.
+ * Errors: HS_ERR_INVALID_ARG for null required pointers or non-positive sizes
+ * (num_rows == 0 is a no-op returning HS_OK).
+ */
+hs_status hs_resolve_topk(const int32_t *topk_pos, int32_t num_rows, int32_t topk,
+                          const int32_t *req_id, const int32_t *causal_limit, int32_t num_reqs,
+                          const int32_t *block_table, int32_t bt_stride, int32_t block_size,
+                          int32_t physical_block_stride, int32_t *out_slots, int32_t *out_valid,
+                          void *stream);
+
+/*
+ * hs_swap_in -- P3 resolve_topk listing: when the batch is not fully resident the
+ * selected KV is swapped into the hot cache and indices into it are returned; P1
+ * startup: device buffer, pinned host pool, LRU slots, async stream.  One call handles
+ * one wave: row b of wave_rows holds request b's resolved host rows (all -1 if the
+ * request has no row in this wave).
+ *
+ *   wave_rows      [num_reqs, topk] int32  host rows (hs_resolve_topk output), -1 = none
+ *   tick           LRU clock value stamped on every slot this wave uses
+ *   out_hot_idx    [num_reqs, topk] int32  b*capacity + slot holding the entry, or -1
+ *   out_miss_count [num_reqs] int32        number of misses copied for the request
+ *   out_miss_pos   [num_reqs, topk] int32 or NULL  entry indices of the misses in
+ *                                          ascending order, -1 after miss_count
+ *
+ * Rule (the pages print none; this is the library's definition): an entry hits iff
+ * loc_to_hot[row] >= 0; hit slots are pinned; the victims are the #misses unpinned slots
+ * with the smallest (stamp, slot); miss m (ascending entry index) takes the m-th victim
+ * in ascending slot order, the evicted row's loc_to_hot entry is cleared and the host
+ * row is copied bit for bit into hot_kv; every used slot gets stamp `tick`.
+ * Entries of one row must be distinct host rows (top-k sets are); with duplicates the
+ * resulting state is unspecified but every access stays in bounds.
+ * hot_kv is written only by work queued on `stream`; it may run concurrently with
+ * attention over an earlier wave when capacity >= 2*topk (victims are then never slots
+ * the previous wave used).
+ * Errors: HS_ERR_CAPACITY if topk > capacity; HS_ERR_INVALID_ARG for null pointers,
+ * non-positive sizes, row bytes not a multiple of 16 or misaligned hot_kv/host_pool,
+ * or a host_pool that is not device-accessible pinned memory; HS_ERR_UNSUPPORTED for
+ * capacity > 16384.
+ */
+hs_status hs_swap_in(const hs_hot_state *st, const int32_t *wave_rows, int32_t topk, int32_t tick,
+                     int32_t *out_hot_idx, int32_t *out_miss_count, int32_t *out_miss_pos,
+                     void *stream);
+
+/*
+ * hs_sparse_decode_attn -- P1 startup: the DSA attention backend reads KV through
+ * HiSparse; P3 resolve_topk: attention receives the cache and per-row indices.  For each
+ * row i and head h, over S_i = {j : 0 <= indices[i,j] < kv_rows}:
+ *   s_j = scale * <q[i,h,:d_qk], kv[indices[i,j], :d_qk]>,  p = softmax(s),
+ *   out[i,h,:] = sum_j p_j * kv[indices[i,j], :d_v]   (value = leading d_v entries),
+ *   lse[i,h] = log(sum_j exp(s_j)).
+ * An empty S_i gives out = 0 and lse = -inf.  Duplicate indices count as separate keys.
+ *
+ *   q        [num_rows, num_heads, d_qk] of dtype (row stride num_heads*d_qk)
+ *   kv       [kv_rows, d_qk] of dtype (the paged device pool, or hs_hot_state.hot_kv)
+ *   indices  [num_rows, topk] int32 (hs_resolve_topk or hs_swap_in output)
+ *   out      [num_rows, num_heads, d_v] of dtype
+ *   lse      [num_rows, num_heads] float32 or NULL (natural log)
+ *   workspace, workspace_bytes  device scratch of at least hs_attn_workspace_bytes(...)
+ *            bytes (may be NULL when that is 0)
+ *
+ * Supported: dtype HS_BF16 with d_qk = 576, d_v = 512, num_heads a multiple of 32 (MFMA
+ * path, fp32 accumulation, bf16 output); dtype HS_F32 with d_qk <= 1024, d_v <= d_qk,
+ * topk <= 8192 (fp32 path).  KV rows referenced by indices must hold finite values.
+ * Errors: HS_ERR_INVALID_ARG (null pointers, sizes, workspace too small, misalignment);
+ * HS_ERR_UNSUPPORTED (other shapes).
+ */
+hs_status hs_sparse_decode_attn(const void *q, const void *kv, int64_t kv_rows,
+                                const int32_t *indices, int32_t num_rows, int32_t num_heads,
+                                int32_t d_qk, int32_t d_v, int32_t topk, float scale,
+                                int32_t dtype, void *out, float *lse, void *workspace,
+                                size_t workspace_bytes, void *stream);
+
+/* Device workspace hs_sparse_decode_attn needs for these sizes (0 when none). */
+size_t hs_attn_workspace_bytes(int32_t num_rows, int32_t num_heads, int32_t d_qk, int32_t d_v,
+                               int32_t topk, int32_t dtype);
+
+/*
+ * hs_finalize_accepted -- P2 ④: the target verifies [anchor, drafts] in one causal pass;
+ * row r's logits judge draft r+1; drafts are kept while they equal the target's greedy
+ * choice; only the accepted prefix's KV is kept and the replacement (or bonus) token has
+ * no KV yet.  P2 ⑥/timeline table: the next anchor follows the kept prefix.  P1 summary:
+ * accepted-KV finalize ends the main line.
+ *
+ *   logits        [rows, vocab] bf16, rows = st->num_reqs * rows_per_req (wave-major)
+ *   draft_ids     [rows] int32 (the anchor rows' entries are ignored)
+ *   new_kv        [rows, st->row_elems] of st->dtype: the verified KV of each row
+ *   seq_len       [num_reqs] int32: committed length + rows_per_req (row r of request b
+ *                 sits at position seq_len[b] - rows_per_req + r)
+ *   block_table   [num_reqs, bt_stride] int32 (physical block stride = block_size)
+ *   out_argmax    [rows] int32: lowest index of each row's maximum (NaN never wins)
+ *   out_accept_len [num_reqs] int32: L_b = longest l <= rows_per_req-1 with
+ *                 draft_ids[row(b,k)] == argmax[row(b,k-1)] for 1 <= k <= l
+ *   out_next_token [num_reqs] int32: argmax[row(b, L_b)]
+ *
+ * Then per request: rows r > L_b are dropped (a hot slot holding that position is
+ * emptied; the host row is left as is); rows r <= L_b have new_kv written to their
+ * host-pool row (PINNED HOST, device stores) and to the hot buffer (overwrite if
+ * resident, else installed with the hs_swap_in victim rule, the slots of the request's
+ * resident kept rows pinned), stamp `tick`.  Dropped rows are processed first.
+ * Errors: HS_ERR_INVALID_ARG (null pointers, sizes, rows_per_req < 1 or >
+ * st->capacity, vocab < 1); HS_ERR_UNSUPPORTED (rows_per_req > 64).
+ */
+hs_status hs_finalize_accepted(const hs_hot_state *st, const void *logits, int32_t vocab,
+                               const int32_t *draft_ids, const void *new_kv, int32_t rows_per_req,
+                               const int32_t *seq_len, const int32_t *block_table,
+                               int32_t bt_stride, int32_t block_size, int32_t tick,
+                               int32_t *out_argmax, int32_t *out_accept_len,
+                               int32_t *out_next_token, void *stream);
+
+/* Static description of a status code. */
+const char *hs_status_string(int32_t status);
+
+/* Library version string. */
+const char *hs_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HISPARSE_H */

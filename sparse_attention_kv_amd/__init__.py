@@ -1,0 +1,207 @@
+"""Python binding of libhisparse.so (MI355X / gfx950 HiSparse sparse-decode path).
+
+Argument marshalling only: every function takes torch tensors, checks their dtype,
+device and contiguity, and forwards raw pointers, sizes and the current HIP stream to
+the C ABI declared in include/hisparse.h.  All computation runs in the library's HIP
+kernels.  Importing this module fails loudly when the library has not been built.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libhisparse.so")
+
+HS_OK, HS_ERR_INVALID_ARG, HS_ERR_CAPACITY, HS_ERR_UNSUPPORTED, HS_ERR_HIP = 0, -1, -2, -3, -4
+HS_BF16, HS_F32 = 0, 1
+
+EXPORTED = ("hs_resolve_topk", "hs_swap_in", "hs_sparse_decode_attn", "hs_attn_workspace_bytes",
+            "hs_finalize_accepted", "hs_status_string", "hs_version")
+
+
+class HsError(RuntimeError):
+    def __init__(self, fn: str, status: int, msg: str):
+        super().__init__(f"{fn} failed: {msg} ({status})")
+        self.status = status
+
+
+class HsHotState(ctypes.Structure):
+    _fields_ = [("num_reqs", ctypes.c_int32), ("capacity", ctypes.c_int32),
+                ("slot_loc", ctypes.c_void_p), ("slot_stamp", ctypes.c_void_p),
+                ("loc_to_hot", ctypes.c_void_p), ("host_rows", ctypes.c_int64),
+                ("row_elems", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("hot_kv", ctypes.c_void_p), ("host_pool", ctypes.c_void_p)]
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it first "
+                          "(python -m sparse_attention_kv_amd.build)")
+    lib = ctypes.CDLL(LIB_PATH)
+    i32, i64, vp, f32, sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p, ctypes.c_float, ctypes.c_size_t
+    lib.hs_resolve_topk.argtypes = [vp, i32, i32, vp, vp, i32, vp, i32, i32, i32, vp, vp, vp]
+    lib.hs_resolve_topk.restype = i32
+    lib.hs_swap_in.argtypes = [ctypes.POINTER(HsHotState), vp, i32, i32, vp, vp, vp, vp]
+    lib.hs_swap_in.restype = i32
+    lib.hs_sparse_decode_attn.argtypes = [vp, vp, i64, vp, i32, i32, i32, i32, i32, f32, i32,
+                                          vp, vp, vp, sz, vp]
+    lib.hs_sparse_decode_attn.restype = i32
+    lib.hs_attn_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32]
+    lib.hs_attn_workspace_bytes.restype = sz
+    lib.hs_finalize_accepted.argtypes = [ctypes.POINTER(HsHotState), vp, i32, vp, vp, i32, vp, vp,
+                                         i32, i32, i32, vp, vp, vp, vp]
+    lib.hs_finalize_accepted.restype = i32
+    lib.hs_status_string.argtypes = [i32]
+    lib.hs_status_string.restype = ctypes.c_char_p
+    lib.hs_version.argtypes = []
+    lib.hs_version.restype = ctypes.c_char_p
+    return lib
+
+
+_lib = _load()
+
+
+def version() -> str:
+    return _lib.hs_version().decode()
+
+
+def status_string(status: int) -> str:
+    return _lib.hs_status_string(status).decode()
+
+
+def _check(fn: str, status: int):
+    if status != HS_OK:
+        raise HsError(fn, status, status_string(status))
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dev(t: torch.Tensor, name: str, dtype=None):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    return t
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dtype_code(dt: torch.dtype) -> int:
+    if dt == torch.bfloat16:
+        return HS_BF16
+    if dt == torch.float32:
+        return HS_F32
+    raise ValueError(f"unsupported dtype {dt}")
+
+
+# ------------------------------------------------------------------------------------
+def hs_resolve_topk(topk_pos: torch.Tensor, req_id: torch.Tensor, causal_limit: torch.Tensor,
+                    block_table: torch.Tensor, block_size: int, physical_block_stride: int,
+                    out_slots: torch.Tensor, out_valid: Optional[torch.Tensor] = None,
+                    stream=None):
+    """Top-k token positions [rows, topk] -> physical KV rows (see include/hisparse.h)."""
+    i32 = torch.int32
+    _dev(topk_pos, "topk_pos", i32); _dev(req_id, "req_id", i32)
+    _dev(causal_limit, "causal_limit", i32); _dev(block_table, "block_table", i32)
+    _dev(out_slots, "out_slots", i32)
+    if out_valid is not None:
+        _dev(out_valid, "out_valid", i32)
+    rows, topk = topk_pos.shape
+    num_reqs, bt_stride = block_table.shape
+    _check("hs_resolve_topk", _lib.hs_resolve_topk(
+        _ptr(topk_pos), rows, topk, _ptr(req_id), _ptr(causal_limit), num_reqs,
+        _ptr(block_table), bt_stride, block_size, physical_block_stride, _ptr(out_slots),
+        _ptr(out_valid), _stream(stream)))
+
+
+@dataclass
+class HotState:
+    """Device tensors of one hot buffer plus the pinned host pool (hs_hot_state)."""
+    slot_loc: torch.Tensor     # int32 [num_reqs, capacity]
+    slot_stamp: torch.Tensor   # int32 [num_reqs, capacity]
+    loc_to_hot: torch.Tensor   # int32 [host_rows]
+    hot_kv: torch.Tensor       # [num_reqs * capacity, row_elems]
+    host_pool: torch.Tensor    # pinned host [host_rows, row_elems] (or device)
+
+    def as_struct(self) -> HsHotState:
+        for name in ("slot_loc", "slot_stamp", "loc_to_hot", "hot_kv"):
+            _dev(getattr(self, name), name)
+        if not self.host_pool.is_contiguous():
+            raise ValueError("host_pool must be contiguous")
+        if self.host_pool.dtype != self.hot_kv.dtype:
+            raise ValueError("host_pool and hot_kv dtypes differ")
+        num_reqs, cap = self.slot_loc.shape
+        return HsHotState(num_reqs, cap, self.slot_loc.data_ptr(), self.slot_stamp.data_ptr(),
+                          self.loc_to_hot.data_ptr(), self.host_pool.shape[0],
+                          self.hot_kv.shape[1], _dtype_code(self.hot_kv.dtype),
+                          self.hot_kv.data_ptr(), self.host_pool.data_ptr())
+
+
+def hs_swap_in(state: HotState, wave_rows: torch.Tensor, tick: int, out_hot_idx: torch.Tensor,
+               out_miss_count: torch.Tensor, out_miss_pos: Optional[torch.Tensor] = None,
+               stream=None):
+    """One wave of swap-in: wave_rows [num_reqs, topk] host rows (see include/hisparse.h)."""
+    i32 = torch.int32
+    _dev(wave_rows, "wave_rows", i32); _dev(out_hot_idx, "out_hot_idx", i32)
+    _dev(out_miss_count, "out_miss_count", i32)
+    if out_miss_pos is not None:
+        _dev(out_miss_pos, "out_miss_pos", i32)
+    st = state.as_struct()
+    _check("hs_swap_in", _lib.hs_swap_in(ctypes.byref(st), _ptr(wave_rows), wave_rows.shape[1],
+                                         tick, _ptr(out_hot_idx), _ptr(out_miss_count),
+                                         _ptr(out_miss_pos), _stream(stream)))
+
+
+def hs_attn_workspace_bytes(num_rows: int, num_heads: int, d_qk: int, d_v: int, topk: int,
+                            dtype: torch.dtype) -> int:
+    return int(_lib.hs_attn_workspace_bytes(num_rows, num_heads, d_qk, d_v, topk, _dtype_code(dtype)))
+
+
+def hs_sparse_decode_attn(q: torch.Tensor, kv: torch.Tensor, indices: torch.Tensor, scale: float,
+                          d_v: int, out: torch.Tensor, lse: Optional[torch.Tensor] = None,
+                          workspace: Optional[torch.Tensor] = None, stream=None):
+    """Sparse attention of q [rows, H, d_qk] over kv[indices] (see include/hisparse.h)."""
+    _dev(q, "q"); _dev(kv, "kv"); _dev(indices, "indices", torch.int32); _dev(out, "out", q.dtype)
+    if kv.dtype != q.dtype:
+        raise ValueError("q and kv dtypes differ")
+    if lse is not None:
+        _dev(lse, "lse", torch.float32)
+    if workspace is not None:
+        _dev(workspace, "workspace")
+    rows, heads, d_qk = q.shape
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("hs_sparse_decode_attn", _lib.hs_sparse_decode_attn(
+        _ptr(q), _ptr(kv), kv.shape[0], _ptr(indices), rows, heads, d_qk, d_v, indices.shape[1],
+        float(scale), _dtype_code(q.dtype), _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes,
+        _stream(stream)))
+
+
+def hs_finalize_accepted(state: HotState, logits: torch.Tensor, draft_ids: torch.Tensor,
+                         new_kv: torch.Tensor, rows_per_req: int, seq_len: torch.Tensor,
+                         block_table: torch.Tensor, block_size: int, tick: int,
+                         out_argmax: torch.Tensor, out_accept_len: torch.Tensor,
+                         out_next_token: torch.Tensor, stream=None):
+    """Greedy accept + accepted-prefix KV keep (see include/hisparse.h)."""
+    i32 = torch.int32
+    _dev(logits, "logits", torch.bfloat16); _dev(draft_ids, "draft_ids", i32)
+    _dev(new_kv, "new_kv", state.hot_kv.dtype); _dev(seq_len, "seq_len", i32)
+    _dev(block_table, "block_table", i32); _dev(out_argmax, "out_argmax", i32)
+    _dev(out_accept_len, "out_accept_len", i32); _dev(out_next_token, "out_next_token", i32)
+    st = state.as_struct()
+    _check("hs_finalize_accepted", _lib.hs_finalize_accepted(
+        ctypes.byref(st), _ptr(logits), logits.shape[1], _ptr(draft_ids), _ptr(new_kv),
+        rows_per_req, _ptr(seq_len), _ptr(block_table), block_table.shape[1], block_size, tick,
+        _ptr(out_argmax), _ptr(out_accept_len), _ptr(out_next_token), _stream(stream)))

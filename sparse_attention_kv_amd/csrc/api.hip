@@ -1,0 +1,166 @@
+// C ABI entry points: argument validation, then kernel launches on the caller's stream.
+// Validation never launches anything, so every error return leaves all buffers untouched.
+
+#include <cstring>
+
+#include "common.h"
+
+namespace hs {
+int attn_f32_max_topk();
+int attn_f32_max_d();
+int finalize_max_rows_per_req();
+}  // namespace hs
+
+namespace {
+
+inline bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+inline hs_status from_hip(hipError_t e) { return e == hipSuccess ? HS_OK : HS_ERR_HIP; }
+
+// Device-visible address of a buffer the kernels will read/write directly: device memory
+// as is, pinned host memory through its device mapping.  Pageable host memory is refused
+// (a kernel touching it would fault).
+hs_status device_view(const void *p, const void **out) {
+  hipPointerAttribute_t attr;
+  std::memset(&attr, 0, sizeof(attr));
+  hipError_t e = hipPointerGetAttributes(&attr, p);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();  // clear the sticky error of the failed query
+    return HS_ERR_INVALID_ARG;
+  }
+  if (attr.type == hipMemoryTypeDevice || attr.type == hipMemoryTypeManaged) {
+    *out = p;
+    return HS_OK;
+  }
+  if (attr.type == hipMemoryTypeHost && attr.devicePointer != nullptr) {
+    *out = attr.devicePointer;
+    return HS_OK;
+  }
+  return HS_ERR_INVALID_ARG;
+}
+
+hs_status check_state(const hs_hot_state *st) {
+  if (st == nullptr) return HS_ERR_INVALID_ARG;
+  if (st->num_reqs <= 0 || st->capacity <= 0 || st->host_rows <= 0 || st->row_elems <= 0)
+    return HS_ERR_INVALID_ARG;
+  if (st->host_rows > 0x7fffffffLL) return HS_ERR_INVALID_ARG;
+  if (st->dtype != HS_BF16 && st->dtype != HS_F32) return HS_ERR_INVALID_ARG;
+  if (!st->slot_loc || !st->slot_stamp || !st->loc_to_hot || !st->hot_kv || !st->host_pool)
+    return HS_ERR_INVALID_ARG;
+  const int elem = st->dtype == HS_BF16 ? 2 : 4;
+  if ((static_cast<int64_t>(st->row_elems) * elem) % 16 != 0) return HS_ERR_INVALID_ARG;
+  if (!aligned16(st->hot_kv) || !aligned16(st->host_pool)) return HS_ERR_INVALID_ARG;
+  if (static_cast<int64_t>(st->num_reqs) * st->capacity > 0x7fffffffLL) return HS_ERR_INVALID_ARG;
+  return HS_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+hs_status hs_resolve_topk(const int32_t *topk_pos, int32_t num_rows, int32_t topk,
+                          const int32_t *req_id, const int32_t *causal_limit, int32_t num_reqs,
+                          const int32_t *block_table, int32_t bt_stride, int32_t block_size,
+                          int32_t physical_block_stride, int32_t *out_slots, int32_t *out_valid,
+                          void *stream) {
+  if (num_rows < 0 || topk <= 0 || num_reqs <= 0 || bt_stride <= 0 || block_size <= 0 ||
+      physical_block_stride <= 0)
+    return HS_ERR_INVALID_ARG;
+  if (num_rows == 0) return HS_OK;
+  if (!topk_pos || !req_id || !causal_limit || !block_table || !out_slots) return HS_ERR_INVALID_ARG;
+  return from_hip(hs::launch_resolve_topk(topk_pos, num_rows, topk, req_id, causal_limit, num_reqs,
+                                          block_table, bt_stride, block_size, physical_block_stride,
+                                          out_slots, out_valid, static_cast<hipStream_t>(stream)));
+}
+
+hs_status hs_swap_in(const hs_hot_state *st, const int32_t *wave_rows, int32_t topk, int32_t tick,
+                     int32_t *out_hot_idx, int32_t *out_miss_count, int32_t *out_miss_pos,
+                     void *stream) {
+  hs_status s = check_state(st);
+  if (s != HS_OK) return s;
+  if (topk <= 0 || !wave_rows || !out_hot_idx || !out_miss_count) return HS_ERR_INVALID_ARG;
+  if (st->capacity > hs::kMaxCapacity) return HS_ERR_UNSUPPORTED;
+  if (topk > st->capacity) return HS_ERR_CAPACITY;
+  if (topk > hs::kMaxSwapTopk) return HS_ERR_UNSUPPORTED;
+  const void *pool = nullptr;
+  s = device_view(st->host_pool, &pool);
+  if (s != HS_OK) return s;
+  return from_hip(hs::launch_swap_in(*st, pool, wave_rows, topk, tick, out_hot_idx, out_miss_count,
+                                     out_miss_pos, static_cast<hipStream_t>(stream)));
+}
+
+size_t hs_attn_workspace_bytes(int32_t num_rows, int32_t num_heads, int32_t d_qk, int32_t d_v,
+                               int32_t topk, int32_t dtype) {
+  if (dtype != HS_BF16 || num_rows <= 0 || topk <= 0 || num_heads <= 0 || num_heads % 32 != 0 ||
+      d_qk != 576 || d_v != 512)
+    return 0;
+  return hs::plan_attn_bf16(num_rows, num_heads, topk).workspace;
+}
+
+hs_status hs_sparse_decode_attn(const void *q, const void *kv, int64_t kv_rows,
+                                const int32_t *indices, int32_t num_rows, int32_t num_heads,
+                                int32_t d_qk, int32_t d_v, int32_t topk, float scale,
+                                int32_t dtype, void *out, float *lse, void *workspace,
+                                size_t workspace_bytes, void *stream) {
+  if (num_rows < 0 || num_heads <= 0 || d_qk <= 0 || d_v <= 0 || topk <= 0 || kv_rows < 0)
+    return HS_ERR_INVALID_ARG;
+  if (dtype != HS_BF16 && dtype != HS_F32) return HS_ERR_INVALID_ARG;
+  if (num_rows == 0) return HS_OK;
+  if (!q || !kv || !indices || !out) return HS_ERR_INVALID_ARG;
+  if (kv_rows > 0x7fffffffLL) return HS_ERR_INVALID_ARG;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (dtype == HS_BF16) {
+    if (d_qk != 576 || d_v != 512 || num_heads % 32 != 0) return HS_ERR_UNSUPPORTED;
+    if (!aligned16(q) || !aligned16(kv) || !aligned16(out)) return HS_ERR_INVALID_ARG;
+    const hs::AttnPlan plan = hs::plan_attn_bf16(num_rows, num_heads, topk);
+    if (plan.workspace > 0 && (workspace == nullptr || workspace_bytes < plan.workspace ||
+                               !aligned16(workspace)))
+      return HS_ERR_INVALID_ARG;
+    return from_hip(hs::launch_attn_bf16(q, kv, kv_rows, indices, num_rows, num_heads, topk, scale,
+                                         out, lse, workspace, plan, st));
+  }
+  if (d_qk > hs::attn_f32_max_d() || d_v > d_qk || topk > hs::attn_f32_max_topk())
+    return HS_ERR_UNSUPPORTED;
+  return from_hip(hs::launch_attn_f32(static_cast<const float *>(q), static_cast<const float *>(kv),
+                                      kv_rows, indices, num_rows, num_heads, d_qk, d_v, topk, scale,
+                                      static_cast<float *>(out), lse, st));
+}
+
+hs_status hs_finalize_accepted(const hs_hot_state *st, const void *logits, int32_t vocab,
+                               const int32_t *draft_ids, const void *new_kv, int32_t rows_per_req,
+                               const int32_t *seq_len, const int32_t *block_table,
+                               int32_t bt_stride, int32_t block_size, int32_t tick,
+                               int32_t *out_argmax, int32_t *out_accept_len,
+                               int32_t *out_next_token, void *stream) {
+  hs_status s = check_state(st);
+  if (s != HS_OK) return s;
+  if (vocab <= 0 || rows_per_req <= 0 || bt_stride <= 0 || block_size <= 0) return HS_ERR_INVALID_ARG;
+  if (!logits || !draft_ids || !new_kv || !seq_len || !block_table || !out_argmax ||
+      !out_accept_len || !out_next_token)
+    return HS_ERR_INVALID_ARG;
+  if (rows_per_req > st->capacity) return HS_ERR_INVALID_ARG;
+  if (rows_per_req > hs::finalize_max_rows_per_req()) return HS_ERR_UNSUPPORTED;
+  if (!aligned16(new_kv) || !aligned16(logits)) return HS_ERR_INVALID_ARG;
+  const void *pool = nullptr;
+  s = device_view(st->host_pool, &pool);
+  if (s != HS_OK) return s;
+  return from_hip(hs::launch_finalize(*st, pool, logits, vocab, draft_ids, new_kv, rows_per_req,
+                                      seq_len, block_table, bt_stride, block_size, tick, out_argmax,
+                                      out_accept_len, out_next_token,
+                                      static_cast<hipStream_t>(stream)));
+}
+
+const char *hs_status_string(int32_t status) {
+  switch (status) {
+    case HS_OK: return "ok";
+    case HS_ERR_INVALID_ARG: return "invalid argument";
+    case HS_ERR_CAPACITY: return "top-k exceeds hot-buffer capacity";
+    case HS_ERR_UNSUPPORTED: return "unsupported shape or dtype";
+    case HS_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char *hs_version(void) { return "hisparse-gfx950 0.1.0"; }
+
+}  // extern "C"

@@ -1,0 +1,471 @@
+// sparse_decode_attn: attention over only the selected latent KV rows (gfx950).
+//
+// P1 "hiSparse-MTP", "1. 启动阶段": the DSA attention backend reads KV through
+// HiSparse.  P3 "vllm 分析（十二）——Hisparse下篇", resolve_topk listing: attention gets
+// the cache plus per-row indices (-1 padded) and reads only those rows.
+//
+// bf16 path (MLA decode shape: 576-wide latent rows, value = leading 512 entries, heads
+// share the row):
+//   * workgroup = 4 waves = (query row, group of 32 heads, key split).  The four head
+//     groups of one (row, split) are placed on the same XCD (consecutive dispatches on
+//     one XCD) so the selected rows are fetched from HBM once and re-read from L2.
+//   * the split's valid indices are compacted into LDS first; KV tiles of 64 selected
+//     rows (72 KiB) are gathered with direct-to-LDS 16-byte loads, double buffered, and
+//     XOR-swizzled in 16-byte units so MFMA operand reads are bank-conflict free.
+//   * S^T = K Q^T with v_mfma_f32_16x16x32_bf16 (keys as M, 16 heads as N, Q resident
+//     in registers); each wave owns 16 keys of the tile for all 32 heads.
+//   * online softmax in the exp2 domain, max shared across waves through LDS.
+//   * O = P V with v_mfma_f32_32x32x16_bf16 (32 heads as M); each wave owns 128 of the
+//     512 value dims; V is read with ds_read_b64_tr_b16 (LDS transpose) so no second
+//     copy of the tile is needed.
+//   * with several key splits, normalised fp32 partials + (max, sum) go to a workspace
+//     and a combine kernel merges them (log-sum-exp weights).
+//
+// f32 path: straightforward vector-ALU kernel (one wave per (row, head)), used for the
+// small fp32 validation shapes.
+
+#include "common.h"
+
+namespace hs {
+namespace {
+
+constexpr int kD = 576;                       // latent row width (q . k)
+constexpr int kDV = 512;                      // value width
+constexpr int kHG = 32;                       // heads per workgroup
+constexpr int kTK = 64;                       // keys per tile
+constexpr int kThreads = 256;
+constexpr int kRowBytes = kD * 2;             // 1152
+constexpr int kRowChunks = kRowBytes / 16;    // 72
+constexpr int kTileBytes = kTK * kRowBytes;   // 73728
+constexpr int kLoadsPerThread = kTK * kRowChunks / kThreads;  // 18
+constexpr int kPStride = kTK * 2 + 16;        // P tile row stride in bytes (padded)
+constexpr int kMaxKeysPerSplit = 2048;
+constexpr float kLn2 = 0.69314718055994530942f;
+
+// LDS-only barrier: waits for this wave's LDS traffic, then s_barrier.  Outstanding
+// global loads (the next tile's direct-to-LDS gathers) are deliberately not waited for.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x3f70); }  // vmcnt(0)
+
+__device__ __forceinline__ float fmax3(float a, float b) { return a > b ? a : b; }
+
+// Gather tile t (selected rows t*64 .. t*64+63 of the compacted list) into LDS buffer dst.
+// Physical 16-byte chunk c of the tile holds (key c/72, logical part (c%72) ^ (key&7)).
+// Keys past n_valid re-load the last valid row; their scores are masked to -inf.
+__device__ __forceinline__ void gather_tile(const uint8_t *__restrict__ kv,
+                                            const int32_t *sidx, int n_valid, int t,
+                                            uint8_t *dst, int w, int l) {
+  // All row-index reads first: the DMA writes LDS, so the compiler will not hoist a
+  // later LDS read above an earlier DMA issue.
+  int rows[kLoadsPerThread];
+#pragma unroll
+  for (int i = 0; i < kLoadsPerThread; ++i) {
+    const int c = (w * kLoadsPerThread + i) * 64 + l;
+    int kk = t * kTK + c / kRowChunks;
+    kk = kk < n_valid ? kk : n_valid - 1;
+    rows[i] = sidx[kk];
+  }
+#pragma unroll
+  for (int i = 0; i < kLoadsPerThread; ++i) {
+    const int n = w * kLoadsPerThread + i;   // 1 KiB wave-instruction slot
+    const int c = n * 64 + l;
+    const int key = c / kRowChunks;
+    const int part = (c - key * kRowChunks) ^ (key & 7);
+    const uint8_t *src = kv + (int64_t)rows[i] * kRowBytes + part * 16;
+    __builtin_amdgcn_global_load_lds(src, (HS_LDS void *)(dst + n * 1024), 16, 0, 0);
+  }
+}
+
+template <bool kSplit>
+__global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(
+    const __bf16 *__restrict__ q, const uint8_t *__restrict__ kv, int64_t kv_rows,
+    const int32_t *__restrict__ indices, int32_t num_rows, int32_t num_heads, int32_t topk,
+    int32_t keys_per_split, int32_t splits, float scale_log2, __bf16 *__restrict__ out,
+    float *__restrict__ lse, float *__restrict__ ws_o, float *__restrict__ ws_ml) {
+  __shared__ __attribute__((aligned(16))) uint8_t s_kv0[kTileBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t s_kv1[kTileBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t s_p[kHG * kPStride];
+  __shared__ __attribute__((aligned(16))) int32_t s_sidx[kMaxKeysPerSplit];
+  __shared__ __attribute__((aligned(16))) float s_red[4][kHG];
+  __shared__ __attribute__((aligned(16))) float s_alpha[kHG];
+  __shared__ __attribute__((aligned(16))) float s_fm[kHG];
+  __shared__ __attribute__((aligned(16))) float s_fl[kHG];
+  __shared__ int s_scan[8];
+
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+  const int n_hg = num_heads / kHG;
+  // XCD-aware decode: dispatch i lands on XCD i % 8; the n_hg head groups of one
+  // (row, split) unit are consecutive dispatches on the same XCD.
+  const int xcd = blockIdx.x & 7;
+  const int k_on_xcd = blockIdx.x >> 3;
+  const int unit = (k_on_xcd / n_hg) * 8 + xcd;
+  const int hg = k_on_xcd % n_hg;
+  if (unit >= num_rows * splits) return;
+  const int row = unit / splits;
+  const int split = unit - row * splits;
+  const int h0 = hg * kHG;
+  const int kbeg = split * keys_per_split;
+  const int kcnt = max(0, min(keys_per_split, topk - kbeg));
+
+  // ---- Q (32 heads x 576) into registers as the B operand of S^T = K Q^T ----
+  bf16x8 qreg[2][kD / 32];
+  {
+    const __bf16 *qrow = q + ((int64_t)row * num_heads + h0) * kD;
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+      for (int ks = 0; ks < kD / 32; ++ks)
+        qreg[hb][ks] = *reinterpret_cast<const bf16x8 *>(qrow + (16 * hb + (l & 15)) * kD +
+                                                         32 * ks + 8 * (l >> 4));
+  }
+
+  // ---- compact this split's valid indices into LDS (order preserved) ----
+  int n_valid;
+  {
+    const int32_t *irow = indices + (int64_t)row * topk + kbeg;
+    const int per = (kcnt + kThreads - 1) / kThreads;  // <= 8
+    int vals[kMaxKeysPerSplit / kThreads];
+    int cnt = 0;
+#pragma unroll
+    for (int k = 0; k < kMaxKeysPerSplit / kThreads; ++k) {
+      vals[k] = -1;
+      if (k < per) {
+        const int j = tid * per + k;
+        const int v = j < kcnt ? irow[j] : -1;
+        if (v >= 0 && v < kv_rows) { vals[k] = v; ++cnt; }
+      }
+    }
+    int wave_total;
+    const int ex = wave_exclusive_scan(cnt, wave_total);
+    if (l == 0) s_scan[w] = wave_total;
+    __syncthreads();
+    int base = 0, total = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int c = s_scan[i];
+      base += i < w ? c : 0;
+      total += c;
+    }
+    int pos = base + ex;
+#pragma unroll
+    for (int k = 0; k < kMaxKeysPerSplit / kThreads; ++k)
+      if (vals[k] >= 0) s_sidx[pos++] = vals[k];
+    n_valid = total;
+    __syncthreads();
+  }
+
+  const int ntiles = (n_valid + kTK - 1) / kTK;
+  float m_run[2] = {-INFINITY, -INFINITY};
+  float l_run[2] = {0.f, 0.f};
+  f32x16 oacc[4];
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) oacc[nb][i] = 0.f;
+
+  if (ntiles > 0) gather_tile(kv, s_sidx, n_valid, 0, s_kv0, w, l);
+
+  for (int t = 0; t < ntiles; ++t) {
+    uint8_t *cur = (t & 1) ? s_kv1 : s_kv0;
+    uint8_t *nxt = (t & 1) ? s_kv0 : s_kv1;
+    wait_vmem();
+    lds_barrier();
+    if (t + 1 < ntiles) gather_tile(kv, s_sidx, n_valid, t + 1, nxt, w, l);
+
+    // ---- S^T (16 keys of this wave x 32 heads) ----
+    f32x4 sacc[2];
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sacc[hb][i] = 0.f;
+    {
+      const int key = 16 * w + (l & 15);
+      const uint8_t *krow = cur + key * kRowBytes;
+      const int sw = key & 7;
+      bf16x8 kf[kD / 32];
+#pragma unroll
+      for (int ks = 0; ks < kD / 32; ++ks)
+        kf[ks] = *reinterpret_cast<const bf16x8 *>(krow + (((4 * ks + (l >> 4)) ^ sw) << 4));
+#pragma unroll
+      for (int ks = 0; ks < kD / 32; ++ks) {
+        sacc[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[ks], qreg[0][ks], sacc[0], 0, 0, 0);
+        sacc[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[ks], qreg[1][ks], sacc[1], 0, 0, 0);
+      }
+    }
+
+    // ---- online softmax (lane holds keys 4*(l>>4)+i of this wave, head l&15 (+16)) ----
+    const int kfirst = t * kTK + 16 * w + 4 * (l >> 4);
+    float s[2][4];
+    float mw[2];
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb) {
+      mw[hb] = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        s[hb][i] = (kfirst + i < n_valid) ? sacc[hb][i] * scale_log2 : -INFINITY;
+        mw[hb] = fmax3(mw[hb], s[hb][i]);
+      }
+      mw[hb] = fmax3(mw[hb], __shfl_xor(mw[hb], 16, 64));
+      mw[hb] = fmax3(mw[hb], __shfl_xor(mw[hb], 32, 64));
+      if (l < 16) s_red[w][16 * hb + l] = mw[hb];
+    }
+    lds_barrier();
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb) {
+      const int h = 16 * hb + (l & 15);
+      float tm = fmax3(fmax3(s_red[0][h], s_red[1][h]), fmax3(s_red[2][h], s_red[3][h]));
+      const float m_new = fmax3(m_run[hb], tm);
+      const bool none = m_new == -INFINITY;
+      const float alpha = none ? 1.f : __builtin_amdgcn_exp2f(m_run[hb] - m_new);
+      float psum = 0.f;
+      bf16x4 pk;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float p = none ? 0.f : __builtin_amdgcn_exp2f(s[hb][i] - m_new);
+        psum += p;
+        pk[i] = (__bf16)p;
+      }
+      l_run[hb] = l_run[hb] * alpha + psum;
+      m_run[hb] = m_new;
+      *reinterpret_cast<bf16x4 *>(s_p + h * kPStride + (16 * w + 4 * (l >> 4)) * 2) = pk;
+      if (w == 0 && l < 16) s_alpha[h] = alpha;
+    }
+    lds_barrier();
+
+    // ---- O (32 heads x this wave's 128 dims) = alpha * O + P V ----
+    {
+      f32x4 a4[4];
+#pragma unroll
+      for (int qd = 0; qd < 4; ++qd)
+        a4[qd] = *reinterpret_cast<const f32x4 *>(s_alpha + 8 * qd + 4 * (l >> 5));
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) oacc[nb][i] *= a4[i >> 2][i & 3];
+      const int g = l >> 4, j = l & 15, r = j >> 2, c = j & 3;
+#pragma unroll
+      for (int ks = 0; ks < kTK / 16; ++ks) {
+        const bf16x8 pa = *reinterpret_cast<const bf16x8 *>(s_p + (l & 31) * kPStride +
+                                                            (16 * ks + 8 * (l >> 5)) * 2);
+        const int key0 = 16 * ks + 8 * (g >> 1) + r;
+        const int key1 = key0 + 4;
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) {
+          const int dim = 128 * w + 32 * nb + 16 * (g & 1) + 4 * c;
+          const int part = dim >> 3, off = (dim & 7) * 2;
+          const uint8_t *p0 = cur + key0 * kRowBytes + ((part ^ (key0 & 7)) << 4) + off;
+          const uint8_t *p1 = cur + key1 * kRowBytes + ((part ^ (key1 & 7)) << 4) + off;
+          typedef short s16x4 __attribute__((ext_vector_type(4)));
+          const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((HS_LDS s16x4 *)p0);
+          const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((HS_LDS s16x4 *)p1);
+          typedef short s16x8 __attribute__((ext_vector_type(8)));
+          const s16x8 vv = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+          oacc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa, __builtin_bit_cast(bf16x8, vv),
+                                                             oacc[nb], 0, 0, 0);
+        }
+      }
+    }
+  }
+
+  // ---- epilogue: total softmax sums, normalise, write ----
+#pragma unroll
+  for (int hb = 0; hb < 2; ++hb) {
+    float lr = l_run[hb];
+    lr += __shfl_xor(lr, 16, 64);
+    lr += __shfl_xor(lr, 32, 64);
+    if (l < 16) s_red[w][16 * hb + l] = lr;
+    if (w == 0 && l < 16) s_fm[16 * hb + l] = m_run[hb];
+  }
+  lds_barrier();
+  if (tid < kHG) s_fl[tid] = s_red[0][tid] + s_red[1][tid] + s_red[2][tid] + s_red[3][tid];
+  lds_barrier();
+
+  f32x4 fl4[4];
+#pragma unroll
+  for (int qd = 0; qd < 4; ++qd) fl4[qd] = *reinterpret_cast<const f32x4 *>(s_fl + 8 * qd + 4 * (l >> 5));
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb) {
+    const int dim = 128 * w + 32 * nb + (l & 31);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int h = 8 * (i >> 2) + 4 * (l >> 5) + (i & 3);
+      const float lt = fl4[i >> 2][i & 3];
+      const float val = lt > 0.f ? oacc[nb][i] / lt : 0.f;
+      const int64_t o = ((int64_t)row * num_heads + h0 + h) * kDV + dim;
+      if constexpr (kSplit) {
+        ws_o[(int64_t)split * num_rows * num_heads * kDV + o] = val;
+      } else {
+        out[o] = (__bf16)val;
+      }
+    }
+  }
+  if (tid < kHG) {
+    const float m = s_fm[tid], lt = s_fl[tid];
+    const int64_t hi = (int64_t)row * num_heads + h0 + tid;
+    if constexpr (kSplit) {
+      ws_ml[((int64_t)split * num_rows * num_heads + hi) * 2 + 0] = m;
+      ws_ml[((int64_t)split * num_rows * num_heads + hi) * 2 + 1] = lt;
+    } else if (lse != nullptr) {
+      lse[hi] = lt > 0.f ? (m + __log2f(lt)) * kLn2 : -INFINITY;
+    }
+  }
+}
+
+// Merge key-split partials: o = sum_s w_s o_s / sum_s w_s, w_s = l_s * 2^(m_s - max m).
+__global__ __launch_bounds__(64) void attn_combine_kernel(const float *__restrict__ ws_o,
+                                                          const float *__restrict__ ws_ml,
+                                                          int32_t splits, int32_t num_rows,
+                                                          int32_t num_heads,
+                                                          __bf16 *__restrict__ out,
+                                                          float *__restrict__ lse) {
+  const int64_t hi = blockIdx.x;  // row * num_heads + head
+  const int l = threadIdx.x;
+  const int64_t plane = (int64_t)num_rows * num_heads;
+  float M = -INFINITY;
+  for (int s = 0; s < splits; ++s) M = fmax3(M, ws_ml[(s * plane + hi) * 2]);
+  float wsum = 0.f;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int s = 0; s < splits; ++s) {
+    const float m = ws_ml[(s * plane + hi) * 2];
+    const float lt = ws_ml[(s * plane + hi) * 2 + 1];
+    const float wgt = lt > 0.f ? lt * __builtin_amdgcn_exp2f(m - M) : 0.f;
+    wsum += wgt;
+    const float *src = ws_o + (s * plane + hi) * kDV + 8 * l;
+    const f32x4 a = *reinterpret_cast<const f32x4 *>(src);
+    const f32x4 b = *reinterpret_cast<const f32x4 *>(src + 4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) { acc[e] += wgt * a[e]; acc[4 + e] += wgt * b[e]; }
+  }
+  const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+  bf16x8 o;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) o[e] = (__bf16)(acc[e] * inv);
+  *reinterpret_cast<bf16x8 *>(out + hi * kDV + 8 * l) = o;
+  if (lse != nullptr && l == 0) lse[hi] = wsum > 0.f ? (M + __log2f(wsum)) * kLn2 : -INFINITY;
+}
+
+// ---- fp32 path: one wave per (row, head) ----
+constexpr int kF32MaxTopk = 8192;
+constexpr int kF32MaxD = 1024;
+
+__global__ __launch_bounds__(64) void attn_f32_kernel(const float *__restrict__ q,
+                                                      const float *__restrict__ kv, int64_t kv_rows,
+                                                      const int32_t *__restrict__ indices,
+                                                      int32_t num_heads, int32_t d_qk, int32_t d_v,
+                                                      int32_t topk, float scale,
+                                                      float *__restrict__ out,
+                                                      float *__restrict__ lse) {
+  __shared__ float s_score[kF32MaxTopk];
+  const int64_t hi = blockIdx.x;  // row * num_heads + head
+  const int64_t row = hi / num_heads;
+  const int l = threadIdx.x;
+  const float *qv = q + hi * d_qk;
+  const int32_t *idx = indices + row * topk;
+  float qr[kF32MaxD / 64];
+#pragma unroll
+  for (int k = 0; k < kF32MaxD / 64; ++k) qr[k] = (64 * k + l < d_qk) ? qv[64 * k + l] : 0.f;
+
+  float m = -INFINITY;
+  for (int j = 0; j < topk; ++j) {
+    const int r = idx[j];
+    float sc = -INFINITY;
+    if (r >= 0 && r < kv_rows) {
+      const float *kr = kv + (int64_t)r * d_qk;
+      float part = 0.f;
+#pragma unroll
+      for (int k = 0; k < kF32MaxD / 64; ++k)
+        if (64 * k + l < d_qk) part = fmaf(qr[k], kr[64 * k + l], part);
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) part += __shfl_xor(part, off, 64);
+      sc = part * scale;
+    }
+    if (l == 0) s_score[j] = sc;
+    m = fmax3(m, sc);
+  }
+  __syncthreads();
+  float lsum = 0.f;
+  for (int j = l; j < topk; j += 64) lsum += s_score[j] == -INFINITY ? 0.f : expf(s_score[j] - m);
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) lsum += __shfl_xor(lsum, off, 64);
+  float acc[kF32MaxD / 64];
+#pragma unroll
+  for (int k = 0; k < kF32MaxD / 64; ++k) acc[k] = 0.f;
+  for (int j = 0; j < topk; ++j) {
+    const float sc = s_score[j];
+    if (sc == -INFINITY) continue;
+    const float p = expf(sc - m);
+    const float *vr = kv + (int64_t)idx[j] * d_qk;
+#pragma unroll
+    for (int k = 0; k < kF32MaxD / 64; ++k)
+      if (64 * k + l < d_v) acc[k] = fmaf(p, vr[64 * k + l], acc[k]);
+  }
+  const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+#pragma unroll
+  for (int k = 0; k < kF32MaxD / 64; ++k)
+    if (64 * k + l < d_v) out[hi * d_v + 64 * k + l] = acc[k] * inv;
+  if (lse != nullptr && l == 0) lse[hi] = lsum > 0.f ? m + logf(lsum) : -INFINITY;
+}
+
+}  // namespace
+
+AttnPlan plan_attn_bf16(int32_t num_rows, int32_t num_heads, int32_t topk) {
+  AttnPlan p;
+  const int groups = num_rows * (num_heads / kHG);
+  int splits = (topk + kMaxKeysPerSplit - 1) / kMaxKeysPerSplit;
+  // Enough workgroups to cover the 256 CUs once, but keep every split >= 4 tiles.
+  while (groups * splits < 256 && (topk + 2 * splits - 1) / (2 * splits) >= 4 * kTK) splits *= 2;
+  int kps = (topk + splits - 1) / splits;
+  kps = (kps + kTK - 1) / kTK * kTK;
+  splits = (topk + kps - 1) / kps;
+  p.splits = splits;
+  p.keys_per_split = kps;
+  p.workspace = splits > 1 ? (size_t)splits * num_rows * num_heads * (kDV + 2) * sizeof(float) : 0;
+  return p;
+}
+
+hipError_t launch_attn_bf16(const void *q, const void *kv, int64_t kv_rows, const int32_t *indices,
+                            int32_t num_rows, int32_t num_heads, int32_t topk, float scale,
+                            void *out, float *lse, void *workspace, const AttnPlan &plan,
+                            hipStream_t stream) {
+  const int n_hg = num_heads / kHG;
+  const int units = num_rows * plan.splits;
+  const int grid = (units + 7) / 8 * 8 * n_hg;
+  const float scale_log2 = scale * 1.44269504088896340736f;
+  const __bf16 *qb = static_cast<const __bf16 *>(q);
+  const uint8_t *kvb = static_cast<const uint8_t *>(kv);
+  __bf16 *ob = static_cast<__bf16 *>(out);
+  if (plan.splits == 1) {
+    hipLaunchKernelGGL(attn_bf16_kernel<false>, dim3(grid), dim3(kThreads), 0, stream, qb, kvb,
+                       kv_rows, indices, num_rows, num_heads, topk, plan.keys_per_split, 1,
+                       scale_log2, ob, lse, nullptr, nullptr);
+    return hipGetLastError();
+  }
+  float *ws_o = static_cast<float *>(workspace);
+  float *ws_ml = ws_o + (size_t)plan.splits * num_rows * num_heads * kDV;
+  hipLaunchKernelGGL(attn_bf16_kernel<true>, dim3(grid), dim3(kThreads), 0, stream, qb, kvb,
+                     kv_rows, indices, num_rows, num_heads, topk, plan.keys_per_split, plan.splits,
+                     scale_log2, ob, lse, ws_o, ws_ml);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(attn_combine_kernel, dim3(num_rows * num_heads), dim3(64), 0, stream, ws_o,
+                     ws_ml, plan.splits, num_rows, num_heads, ob, lse);
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_f32(const float *q, const float *kv, int64_t kv_rows, const int32_t *indices,
+                           int32_t num_rows, int32_t num_heads, int32_t d_qk, int32_t d_v,
+                           int32_t topk, float scale, float *out, float *lse, hipStream_t stream) {
+  hipLaunchKernelGGL(attn_f32_kernel, dim3(num_rows * num_heads), dim3(64), 0, stream, q, kv,
+                     kv_rows, indices, num_heads, d_qk, d_v, topk, scale, out, lse);
+  return hipGetLastError();
+}
+
+int attn_f32_max_topk() { return kF32MaxTopk; }
+int attn_f32_max_d() { return kF32MaxD; }
+
+}  // namespace hs

@@ -1,0 +1,74 @@
+// Internal declarations shared by the library's translation units (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "hisparse.h"
+
+namespace hs {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+
+#define HS_LDS __attribute__((address_space(3)))
+
+// Largest hot-buffer capacity the swap-in kernel's LDS arrays are sized for.
+constexpr int kMaxCapacity = 16384;
+// Largest top-k a swap-in call accepts (it is also bounded by the capacity); the
+// per-entry LDS arrays of the swap-in kernel are sized by it.
+constexpr int kMaxSwapTopk = 4096;
+
+// ---- launchers (one per kernel family); return hipSuccess or the launch error ----
+hipError_t launch_resolve_topk(const int32_t *topk_pos, int32_t num_rows, int32_t topk,
+                               const int32_t *req_id, const int32_t *causal_limit,
+                               int32_t num_reqs, const int32_t *block_table, int32_t bt_stride,
+                               int32_t block_size, int32_t physical_block_stride,
+                               int32_t *out_slots, int32_t *out_valid, hipStream_t stream);
+
+hipError_t launch_swap_in(const hs_hot_state &st, const void *host_pool_dev,
+                          const int32_t *wave_rows, int32_t topk, int32_t tick,
+                          int32_t *out_hot_idx, int32_t *out_miss_count, int32_t *out_miss_pos,
+                          hipStream_t stream);
+
+struct AttnPlan {
+  int splits;          // key splits per (row, head group); 1 = no combine pass
+  int keys_per_split;  // multiple of the key tile
+  size_t workspace;    // bytes
+};
+AttnPlan plan_attn_bf16(int32_t num_rows, int32_t num_heads, int32_t topk);
+
+hipError_t launch_attn_bf16(const void *q, const void *kv, int64_t kv_rows, const int32_t *indices,
+                            int32_t num_rows, int32_t num_heads, int32_t topk, float scale,
+                            void *out, float *lse, void *workspace, const AttnPlan &plan,
+                            hipStream_t stream);
+
+hipError_t launch_attn_f32(const float *q, const float *kv, int64_t kv_rows, const int32_t *indices,
+                           int32_t num_rows, int32_t num_heads, int32_t d_qk, int32_t d_v,
+                           int32_t topk, float scale, float *out, float *lse, hipStream_t stream);
+
+hipError_t launch_finalize(const hs_hot_state &st, const void *host_pool_dev, const void *logits,
+                           int32_t vocab, const int32_t *draft_ids, const void *new_kv,
+                           int32_t rows_per_req, const int32_t *seq_len, const int32_t *block_table,
+                           int32_t bt_stride, int32_t block_size, int32_t tick, int32_t *out_argmax,
+                           int32_t *out_accept_len, int32_t *out_next_token, hipStream_t stream);
+
+// ---- small device helpers ----
+__device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+// Exclusive prefix sum of `v` across the 64 lanes of a wave; `total` receives the sum.
+__device__ __forceinline__ int wave_exclusive_scan(int v, int &total) {
+  int x = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    int y = __shfl_up(x, off, 64);
+    if (lane_id() >= off) x += y;
+  }
+  total = __shfl(x, 63, 64);
+  return x - v;
+}
+
+}  // namespace hs

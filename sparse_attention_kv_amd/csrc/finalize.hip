@@ -1,0 +1,246 @@
+// finalize_accepted: greedy acceptance of the verified draft rows, then keep exactly the
+// accepted prefix's KV (gfx950).
+//
+// P2 "投机解码的 KV 流转：prefill 阶段 DFlash 也要吃下整个 prompt", ④: the target runs the
+// anchor and the drafts through one causal pass; the logits of row r decide draft r+1;
+// drafts are accepted while they match the target's greedy choice, the first mismatch
+// is replaced by that choice and the rest is dropped; only the accepted prefix keeps its
+// KV, the replacement token has none yet.  ⑥ and the timeline table: the next anchor is
+// the position right after the kept prefix.  P1 "hiSparse-MTP", summary: accepted-KV
+// finalize closes the main line.
+//
+// Kernel 1 (one workgroup per row): argmax over the vocabulary, lowest index on ties,
+//   16-byte loads of 8 bf16 logits (HBM-bound streaming read).
+// Kernel 2 (one workgroup per request): acceptance length, then
+//   dropped rows -> hot slots holding them are emptied;
+//   kept rows    -> new KV stored to the pinned host pool (device stores over the host
+//                   link) and into the hot buffer (overwrite, or install into the LRU
+//                   victim with the kept hits pinned).
+
+#include "common.h"
+
+namespace hs {
+namespace {
+
+constexpr int kArgThreads = 512;
+constexpr int kFinThreads = 256;
+constexpr int kMaxRowsPerReq = 64;
+
+__device__ __forceinline__ float bf16_bits_to_float(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+__device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
+  return v > bv || (v == bv && i < bi);
+}
+
+__global__ __launch_bounds__(kArgThreads) void argmax_kernel(const uint16_t *__restrict__ logits,
+                                                             int32_t vocab,
+                                                             int32_t *__restrict__ out_argmax) {
+  __shared__ float s_v[kArgThreads / 64];
+  __shared__ int s_i[kArgThreads / 64];
+  const int64_t row = blockIdx.x;
+  const uint16_t *lr = logits + row * vocab;
+  const int tid = threadIdx.x;
+  float bv = -INFINITY;
+  int bi = 0x7fffffff;
+  if ((vocab & 7) == 0) {
+    const int chunks = vocab >> 3;
+    for (int c = tid; c < chunks; c += kArgThreads) {
+      const i32x4 raw = *reinterpret_cast<const i32x4 *>(lr + 8 * c);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint16_t bits = static_cast<uint16_t>(static_cast<uint32_t>(raw[e >> 1]) >> (16 * (e & 1)));
+        float v = bf16_bits_to_float(bits);
+        v = v != v ? -INFINITY : v;  // NaN never wins
+        if (better(v, 8 * c + e, bv, bi)) { bv = v; bi = 8 * c + e; }
+      }
+    }
+  } else {
+    for (int i = tid; i < vocab; i += kArgThreads) {
+      float v = bf16_bits_to_float(lr[i]);
+      v = v != v ? -INFINITY : v;
+      if (better(v, i, bv, bi)) { bv = v; bi = i; }
+    }
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    const float ov = __shfl_xor(bv, off, 64);
+    const int oi = __shfl_xor(bi, off, 64);
+    if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
+  }
+  if (lane_id() == 0) { s_v[tid >> 6] = bv; s_i[tid >> 6] = bi; }
+  __syncthreads();
+  if (tid == 0) {
+    for (int wv = 1; wv < kArgThreads / 64; ++wv)
+      if (better(s_v[wv], s_i[wv], bv, bi)) { bv = s_v[wv]; bi = s_i[wv]; }
+    out_argmax[row] = bi == 0x7fffffff ? 0 : bi;
+  }
+}
+
+// Block-wide minimum of (stamp, slot) keys packed in 64 bits.
+__device__ __forceinline__ uint64_t block_min_u64(uint64_t v, uint64_t *s_red) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    const uint64_t o = __shfl_xor(v, off, 64);
+    v = o < v ? o : v;
+  }
+  if (lane_id() == 0) s_red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  uint64_t r = s_red[0];
+  for (int wv = 1; wv < kFinThreads / 64; ++wv) r = s_red[wv] < r ? s_red[wv] : r;
+  __syncthreads();
+  return r;
+}
+
+__global__ __launch_bounds__(kFinThreads) void finalize_kernel(
+    int32_t num_reqs, int32_t capacity, int32_t *__restrict__ slot_loc,
+    int32_t *__restrict__ slot_stamp, int32_t *__restrict__ loc_to_hot, int64_t host_rows,
+    int32_t row_bytes, uint8_t *__restrict__ hot_kv, uint8_t *__restrict__ host_pool,
+    const int32_t *__restrict__ draft_ids, const uint8_t *__restrict__ new_kv,
+    int32_t rows_per_req, const int32_t *__restrict__ seq_len,
+    const int32_t *__restrict__ block_table, int32_t bt_stride, int32_t block_size, int32_t tick,
+    const int32_t *__restrict__ argmax, int32_t *__restrict__ out_accept_len,
+    int32_t *__restrict__ out_next_token) {
+  __shared__ int s_L;
+  __shared__ int s_loc[kMaxRowsPerReq];
+  __shared__ int s_slot[kMaxRowsPerReq];   // slot within the request for kept rows, -1 none
+  __shared__ int s_miss[kMaxRowsPerReq];   // kept rows that must be installed
+  __shared__ int s_nmiss;
+  __shared__ uint64_t s_red[kFinThreads / 64];
+
+  const int b = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int R = rows_per_req;
+  const int64_t slot_base = (int64_t)b * capacity;
+
+  if (tid == 0) {
+    int L = 0;
+    while (L < R - 1 && draft_ids[(int64_t)(L + 1) * num_reqs + b] == argmax[(int64_t)L * num_reqs + b]) ++L;
+    out_accept_len[b] = L;
+    out_next_token[b] = argmax[(int64_t)L * num_reqs + b];
+    s_L = L;
+    s_nmiss = 0;
+  }
+  if (tid < R) {
+    // host row of position seq_len - R + tid (same block-table mapping as resolve_topk)
+    const int pos = seq_len[b] - R + tid;
+    int loc = -1;
+    if (pos >= 0) {
+      const int pi = pos / block_size;
+      if (pi < bt_stride) {
+        const int page = block_table[(int64_t)b * bt_stride + pi];
+        if (page >= 0) {
+          const int64_t r = (int64_t)page * block_size + (pos - pi * block_size);
+          loc = r < host_rows ? (int)r : -1;
+        }
+      }
+    }
+    s_loc[tid] = loc;
+    s_slot[tid] = -1;
+  }
+  __syncthreads();
+  const int L = s_L;
+
+  // dropped rows: empty the slot that holds them (host rows untouched)
+  if (tid < R && tid > L) {
+    const int loc = s_loc[tid];
+    if (loc >= 0) {
+      const int g = loc_to_hot[loc];
+      if (g >= slot_base && g < slot_base + capacity) {
+        slot_loc[g] = -1;
+        slot_stamp[g] = -1;
+        loc_to_hot[loc] = -1;
+      }
+    }
+  }
+  __syncthreads();
+  // kept rows: hit -> its slot (pinned), miss -> queued for install
+  if (tid == 0) {
+    int nm = 0;
+    for (int r = 0; r <= L; ++r) {
+      const int loc = s_loc[r];
+      if (loc < 0) continue;
+      const int g = loc_to_hot[loc];
+      if (g >= slot_base && g < slot_base + capacity) s_slot[r] = (int)(g - slot_base);
+      else s_miss[nm++] = r;
+    }
+    s_nmiss = nm;
+  }
+  __syncthreads();
+  const int nmiss = s_nmiss;
+
+  // victims: repeatedly the least-recently-used unpinned, unchosen slot (nmiss <= R)
+  for (int k = 0; k < nmiss; ++k) {
+    uint64_t best = ~0ull;
+    for (int s = tid; s < capacity; s += kFinThreads) {
+      bool taken = false;
+      for (int r = 0; r <= L; ++r) taken |= s_slot[r] == s;
+      if (taken) continue;
+      const uint64_t key = (static_cast<uint64_t>(static_cast<uint32_t>(slot_stamp[slot_base + s]) ^ 0x80000000u) << 32) |
+                           static_cast<uint32_t>(s);
+      best = key < best ? key : best;
+    }
+    best = block_min_u64(best, s_red);
+    // (a candidate always exists when rows_per_req <= capacity, which the host checks)
+    if (tid == 0) s_slot[s_miss[k]] = best == ~0ull ? -1 : static_cast<int>(best & 0xffffffffu);
+    __syncthreads();
+  }
+  // Victims were chosen in LRU order; pair them with the misses in ascending slot order.
+  if (tid == 0 && nmiss > 1) {
+    int vs[kMaxRowsPerReq];
+    for (int k = 0; k < nmiss; ++k) vs[k] = s_slot[s_miss[k]];
+    for (int i = 1; i < nmiss; ++i)
+      for (int j = i; j > 0 && vs[j - 1] > vs[j]; --j) { const int t = vs[j]; vs[j] = vs[j - 1]; vs[j - 1] = t; }
+    for (int k = 0; k < nmiss; ++k) s_slot[s_miss[k]] = vs[k];
+  }
+  __syncthreads();
+  if (tid < nmiss && s_slot[s_miss[tid]] >= 0) {
+    const int r = s_miss[tid];
+    const int v = s_slot[r];
+    const int64_t g = slot_base + v;
+    const int old = slot_loc[g];
+    if (old >= 0 && old < host_rows) loc_to_hot[old] = -1;
+    slot_loc[g] = s_loc[r];
+    loc_to_hot[s_loc[r]] = (int32_t)g;
+  }
+  if (tid <= L && tid < R && s_slot[tid] >= 0) slot_stamp[slot_base + s_slot[tid]] = tick;
+  // row copies: new KV -> host pool row and hot slot (16 bytes per lane access)
+  const int chunks = row_bytes >> 4;
+  for (int c = tid; c < (L + 1) * chunks; c += kFinThreads) {
+    const int r = c / chunks;
+    const int part = c - r * chunks;
+    const int loc = s_loc[r];
+    if (loc < 0) continue;
+    const i32x4 v = *reinterpret_cast<const i32x4 *>(new_kv + ((int64_t)r * num_reqs + b) * row_bytes + part * 16);
+    *reinterpret_cast<i32x4 *>(host_pool + (int64_t)loc * row_bytes + part * 16) = v;
+    if (s_slot[r] >= 0)
+      *reinterpret_cast<i32x4 *>(hot_kv + (slot_base + s_slot[r]) * row_bytes + part * 16) = v;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_finalize(const hs_hot_state &st, const void *host_pool_dev, const void *logits,
+                           int32_t vocab, const int32_t *draft_ids, const void *new_kv,
+                           int32_t rows_per_req, const int32_t *seq_len, const int32_t *block_table,
+                           int32_t bt_stride, int32_t block_size, int32_t tick, int32_t *out_argmax,
+                           int32_t *out_accept_len, int32_t *out_next_token, hipStream_t stream) {
+  const int rows = st.num_reqs * rows_per_req;
+  hipLaunchKernelGGL(argmax_kernel, dim3(rows), dim3(kArgThreads), 0, stream,
+                     static_cast<const uint16_t *>(logits), vocab, out_argmax);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int elem = st.dtype == HS_BF16 ? 2 : 4;
+  hipLaunchKernelGGL(finalize_kernel, dim3(st.num_reqs), dim3(kFinThreads), 0, stream, st.num_reqs,
+                     st.capacity, st.slot_loc, st.slot_stamp, st.loc_to_hot, st.host_rows,
+                     st.row_elems * elem, static_cast<uint8_t *>(st.hot_kv),
+                     static_cast<uint8_t *>(const_cast<void *>(host_pool_dev)), draft_ids,
+                     static_cast<const uint8_t *>(new_kv), rows_per_req, seq_len, block_table,
+                     bt_stride, block_size, tick, out_argmax, out_accept_len, out_next_token);
+  return hipGetLastError();
+}
+
+int finalize_max_rows_per_req() { return kMaxRowsPerReq; }
+
+}  // namespace hs

@@ -1,0 +1,143 @@
+"""Decode-step driver over the C ABI: buffers, streams and events for one step.
+
+Per step (P1 "hiSparse-MTP" summary: decode, then MTP verify, then accepted-KV
+finalize; P3 "vllm 分析（十二）——Hisparse下篇" resolve_topk listing: the fully
+resident batch reads the paged device cache directly, otherwise KV is swapped in):
+
+  resident batch:  hs_resolve_topk(all rows) -> hs_sparse_decode_attn(paged pool)
+  swap batch:      hs_resolve_topk(all rows) on the main stream, then for each wave r
+                   (row r of every request): hs_swap_in on the copy stream, attention
+                   of wave r on the main stream once that swap has landed; the swap of
+                   wave r+1 overlaps the attention of wave r.  hs_finalize_accepted
+                   closes the step when draft rows are verified.
+
+The copy stream waits for the attention of wave r-2 before swapping wave r (victims of
+wave r are never slots wave r-1 used when capacity >= 2*topk); with a smaller hot
+buffer it waits for wave r-1.  Both streams run at the default priority.
+"""
+
+from __future__ import annotations
+
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+from . import (HotState, hs_attn_workspace_bytes, hs_finalize_accepted, hs_resolve_topk,
+               hs_sparse_decode_attn, hs_swap_in)
+
+
+def build_hot_state(init_pos: torch.Tensor, init_stamp: torch.Tensor, seq_len: torch.Tensor,
+                    block_table: torch.Tensor, block_size: int, host_pool: torch.Tensor,
+                    device: torch.device) -> HotState:
+    """Hot buffer from a slot -> token-position description (a request admitted with
+    some of its KV already resident).  Positions are mapped to host rows with
+    hs_resolve_topk; the reverse map and the resident rows are filled with plain torch
+    indexing (setup, not part of a step)."""
+    B, cap = init_pos.shape
+    pos = init_pos.to(device=device, dtype=torch.int32).contiguous()
+    req = torch.arange(B, dtype=torch.int32, device=device)
+    slot_loc = torch.empty((B, cap), dtype=torch.int32, device=device)
+    hs_resolve_topk(pos, req, seq_len.to(device=device, dtype=torch.int32).contiguous(),
+                    block_table, block_size, block_size, slot_loc)
+    stamps = torch.where(slot_loc >= 0, init_stamp.to(device=device, dtype=torch.int32),
+                         torch.full_like(slot_loc, -1)).contiguous()
+    host_rows = host_pool.shape[0]
+    loc_to_hot = torch.full((host_rows,), -1, dtype=torch.int32, device=device)
+    flat = slot_loc.view(-1)
+    occ = flat >= 0
+    gidx = torch.arange(B * cap, dtype=torch.int32, device=device)
+    loc_to_hot[flat[occ].long()] = gidx[occ]
+    hot_kv = torch.zeros((B * cap, host_pool.shape[1]), dtype=host_pool.dtype, device=device)
+    rows_cpu = flat[occ].long().cpu()
+    if rows_cpu.numel():
+        hot_kv[occ] = host_pool.index_select(0, rows_cpu).to(device)
+    return HotState(slot_loc, stamps, loc_to_hot, hot_kv, host_pool)
+
+
+@dataclass
+class StepBuffers:
+    slots: torch.Tensor          # [rows, topk] int32
+    valid: torch.Tensor          # [rows] int32
+    hot_idx: Optional[torch.Tensor]
+    miss_count: Optional[torch.Tensor]  # [R, B]
+    miss_pos: Optional[torch.Tensor]
+    out: torch.Tensor            # [rows, H, d_v]
+    lse: torch.Tensor            # [rows, H] fp32
+    workspace: Optional[torch.Tensor]
+    argmax: Optional[torch.Tensor] = None
+    accept_len: Optional[torch.Tensor] = None
+    next_token: Optional[torch.Tensor] = None
+
+
+class DecodeStep:
+    """Preallocated buffers + streams for repeated decode steps of one shape."""
+
+    def __init__(self, *, num_reqs: int, rows_per_req: int, topk: int, num_heads: int,
+                 d_qk: int, d_v: int, dtype: torch.dtype, capacity: int = 0,
+                 finalize: bool = False, want_miss_pos: bool = False,
+                 device: torch.device = torch.device("cuda")):
+        self.B, self.R, self.K = num_reqs, rows_per_req, topk
+        self.H, self.d_qk, self.d_v, self.dtype = num_heads, d_qk, d_v, dtype
+        self.capacity, self.device = capacity, device
+        rows = num_reqs * rows_per_req
+        i32 = dict(dtype=torch.int32, device=device)
+        swap = capacity > 0
+        # attention runs per wave on the swap path, over all rows on the resident path
+        attn_rows = num_reqs if swap else rows
+        ws = hs_attn_workspace_bytes(attn_rows, num_heads, d_qk, d_v, topk, dtype)
+        self.buf = StepBuffers(
+            slots=torch.empty((rows, topk), **i32),
+            valid=torch.empty((rows,), **i32),
+            hot_idx=torch.empty((rows, topk), **i32) if swap else None,
+            miss_count=torch.empty((rows_per_req, num_reqs), **i32) if swap else None,
+            miss_pos=torch.empty((rows, topk), **i32) if (swap and want_miss_pos) else None,
+            out=torch.empty((rows, num_heads, d_v), dtype=dtype, device=device),
+            lse=torch.empty((rows, num_heads), dtype=torch.float32, device=device),
+            workspace=torch.empty((max(ws, 16),), dtype=torch.uint8, device=device) if ws else None,
+            argmax=torch.empty((rows,), **i32) if finalize else None,
+            accept_len=torch.empty((num_reqs,), **i32) if finalize else None,
+            next_token=torch.empty((num_reqs,), **i32) if finalize else None,
+        )
+        self.copy_stream = torch.cuda.Stream(device=device) if swap else None
+        self.e_resolve = torch.cuda.Event()
+        self.e_swap = [torch.cuda.Event() for _ in range(rows_per_req)]
+        self.e_attn = [torch.cuda.Event() for _ in range(rows_per_req)]
+
+    # -- resident batch ---------------------------------------------------------------
+    def run_resident(self, topk_pos, req_id, causal_limit, block_table, block_size, q, kv_pool,
+                     scale):
+        b = self.buf
+        hs_resolve_topk(topk_pos, req_id, causal_limit, block_table, block_size, block_size,
+                        b.slots, b.valid)
+        hs_sparse_decode_attn(q, kv_pool, b.slots, scale, self.d_v, b.out, b.lse, b.workspace)
+
+    # -- swap batch (waves) -------------------------------------------------------------
+    def run_swap(self, state: HotState, topk_pos, req_id, causal_limit, block_table, block_size,
+                 q, scale, tick0: int, finalize: Optional[dict] = None):
+        b, B, R = self.buf, self.B, self.R
+        main = torch.cuda.current_stream()
+        copy = self.copy_stream
+        serialize = self.capacity < 2 * self.K
+        hs_resolve_topk(topk_pos, req_id, causal_limit, block_table, block_size, block_size,
+                        b.slots, b.valid)
+        self.e_resolve.record(main)
+        copy.wait_event(self.e_resolve)
+        for r in range(R):
+            lo, hi = r * B, (r + 1) * B
+            if r >= 1 and serialize:
+                copy.wait_event(self.e_attn[r - 1])
+            elif r >= 2:
+                copy.wait_event(self.e_attn[r - 2])
+            hs_swap_in(state, b.slots[lo:hi], tick0 + r, b.hot_idx[lo:hi], b.miss_count[r],
+                       None if b.miss_pos is None else b.miss_pos[lo:hi], stream=copy)
+            self.e_swap[r].record(copy)
+            main.wait_event(self.e_swap[r])
+            hs_sparse_decode_attn(q[lo:hi], state.hot_kv, b.hot_idx[lo:hi], scale, self.d_v,
+                                  b.out[lo:hi], b.lse[lo:hi], b.workspace, stream=main)
+            self.e_attn[r].record(main)
+        if finalize is not None:
+            hs_finalize_accepted(state, finalize["logits"], finalize["draft_ids"],
+                                 finalize["new_kv"], R, finalize["seq_len"], block_table,
+                                 block_size, tick0 + R, b.argmax, b.accept_len, b.next_token,
+                                 stream=main)

@@ -1,0 +1,126 @@
+"""GPU parity of hs_sparse_decode_attn against the oracle (float64).
+
+bf16 path: |gpu - ref| <= 2e-2 + 1e-2 |ref| elementwise; fp32 path: 1e-5 + 1e-5 |ref|.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from tests.gpu_cases import (BF16_TOL, F32_TOL, assert_close, dev, gpu_inputs, log, make,
+                             oracle_resolve, out_f64, to_dev)
+from tests.helpers import raw
+
+pytestmark = pytest.mark.gpu
+LSE_TOL = (1e-3, 1e-4)
+
+
+def _attn(q, kv, idx, scale, d_v, lse=True):
+    import sparse_attention_kv_amd as hs
+    rows, H, _ = q.shape
+    out = torch.full((rows, H, d_v), float("nan"), dtype=q.dtype, device=dev())
+    l = torch.full((rows, H), float("nan"), dtype=torch.float32, device=dev()) if lse else None
+    ws_bytes = hs.hs_attn_workspace_bytes(rows, H, q.shape[2], d_v, idx.shape[1], q.dtype)
+    ws = torch.empty((ws_bytes,), dtype=torch.uint8, device=dev()) if ws_bytes else None
+    hs.hs_sparse_decode_attn(q, kv, idx, scale, d_v, out, l, ws)
+    torch.cuda.synchronize()
+    return out, l
+
+
+def _check(q, kv, idx, scale, d_v, tol, what, lse_check=True):
+    log(f"attn {what}: rows={q.shape[0]} H={q.shape[1]} topk={idx.shape[1]} kv_rows={kv.shape[0]}")
+    out, lse = _attn(q, kv, idx, scale, d_v)
+    ref, rlse = oracle.sparse_decode_attn(raw(q.cpu()), raw(kv.cpu()), idx.cpu().numpy(), scale, d_v)
+    assert_close(out_f64(out), ref, tol, what)
+    if lse_check:
+        g = lse.cpu().double().numpy()
+        fin = np.isfinite(rlse)
+        assert np.array_equal(np.isfinite(g), fin), what
+        assert_close(g[fin], rlse[fin], LSE_TOL, what + " lse")
+    return out, lse
+
+
+def test_attn_tiny_f32():
+    s, w = make("tiny")
+    g = gpu_inputs(s, w)
+    ref_slots, _ = oracle_resolve(s, w)
+    kv = w.kv_pool.to(dev())
+    _check(g["q"], kv, to_dev(ref_slots), s.scale, s.d_v, F32_TOL, "tiny f32")
+
+
+def test_attn_resident_full_bf16():
+    """The resident decode workload at full size: 8 rows x 128 heads x top-k 2048."""
+    s, w = make("resident")
+    g = gpu_inputs(s, w)
+    ref_slots, _ = oracle_resolve(s, w)
+    _check(g["q"], w.kv_pool, to_dev(ref_slots), s.scale, s.d_v, BF16_TOL, "resident full")
+
+
+def _rand_bf16(shape, seed):
+    gen = torch.Generator(device="cpu").manual_seed(seed)
+    return torch.randn(shape, generator=gen).to(torch.bfloat16).to(dev())
+
+
+@pytest.mark.parametrize("topk", [1, 16, 63, 64, 65, 200, 2047, 2048, 3000, 4500])
+def test_attn_bf16_ragged_topk(topk):
+    rows, H, kv_rows = 3, 32, 5000
+    rng = np.random.default_rng(topk)
+    q = _rand_bf16((rows, H, 576), topk)
+    kv = _rand_bf16((kv_rows, 576), topk + 1)
+    idx = np.stack([rng.choice(kv_rows, topk, replace=False) for _ in range(rows)]).astype(np.int32)
+    # scatter some padding and out-of-range entries through the rows
+    idx[1, rng.random(topk) < 0.3] = -1
+    idx[2, rng.random(topk) < 0.2] = kv_rows + 7
+    _check(q, kv, to_dev(idx), 1 / 24, 512, BF16_TOL, f"ragged topk={topk}")
+
+
+def test_attn_bf16_empty_single_duplicate_and_zero_query():
+    rows, H, kv_rows, topk = 5, 64, 300, 96
+    q = _rand_bf16((rows, H, 576), 11)
+    kv = _rand_bf16((kv_rows, 576), 12)
+    idx = np.full((rows, topk), -1, np.int32)
+    idx[1, 50] = 17                       # a single selected key
+    idx[2, :40] = np.arange(40)           # 40 keys listed twice: duplicates count twice
+    idx[2, 40:80] = np.arange(40)
+    idx[3, :96] = np.arange(100, 196)
+    q[4] = 0                              # zero query: uniform weights
+    idx[4, :90] = np.arange(200, 290)
+    out, lse = _check(q, kv, to_dev(idx), 1 / 24, 512, BF16_TOL, "edge rows")
+    o = out.cpu()
+    assert (o[0] == 0).all() and torch.isneginf(lse[0].cpu()).all()        # empty row
+    assert torch.equal(o[1], kv[17, :512].cpu().expand(H, 512))           # p = 1 exactly
+    mean = kv[200:290, :512].double().mean(0).cpu()
+    assert_close(o[4].double().numpy(), mean.expand(H, 512).numpy(), BF16_TOL, "zero query mean")
+
+
+def test_attn_split_and_unsplit_agree():
+    """One row alone (key-split + combine) vs the same row in a large batch (no split)."""
+    import sparse_attention_kv_amd as hs
+    H, kv_rows, topk = 128, 20000, 2048
+    assert hs.hs_attn_workspace_bytes(1, H, 576, 512, topk, torch.bfloat16) > 0
+    assert hs.hs_attn_workspace_bytes(64, H, 576, 512, topk, torch.bfloat16) == 0
+    q = _rand_bf16((64, H, 576), 21)
+    kv = _rand_bf16((kv_rows, 576), 22)
+    rng = np.random.default_rng(5)
+    idx = to_dev(np.stack([rng.choice(kv_rows, topk, replace=False) for _ in range(64)]).astype(np.int32))
+    log("attn split vs unsplit")
+    big, big_lse = _attn(q, kv, idx, 1 / 24, 512)
+    for r in (0, 33, 63):
+        one, one_lse = _attn(q[r:r + 1].contiguous(), kv, idx[r:r + 1].contiguous(), 1 / 24, 512)
+        assert_close(out_f64(one[0]), out_f64(big[r]), (1e-2, 1e-2), "split vs unsplit")
+        assert_close(one_lse[0].cpu().double().numpy(), big_lse[r].cpu().double().numpy(), LSE_TOL, "lse")
+
+
+def test_attn_deterministic_and_index_order_invariant():
+    s, w = make("resident", num_reqs=4)
+    g = gpu_inputs(s, w)
+    ref_slots, _ = oracle_resolve(s, w)
+    idx = to_dev(ref_slots)
+    log("attn determinism")
+    a, _ = _attn(g["q"], w.kv_pool, idx, s.scale, s.d_v)
+    b, _ = _attn(g["q"], w.kv_pool, idx, s.scale, s.d_v)
+    assert torch.equal(a, b)
+    perm = torch.randperm(idx.shape[1], generator=torch.Generator().manual_seed(0)).to(dev())
+    c, _ = _attn(g["q"], w.kv_pool, idx[:, perm].contiguous(), s.scale, s.d_v)
+    assert_close(out_f64(c), out_f64(a), (1e-2, 1e-2), "permuted indices")

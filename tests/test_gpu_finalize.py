@@ -1,0 +1,148 @@
+"""GPU parity of hs_finalize_accepted on the pages' worked example and on edge cases,
+and cross-path identity of attention (resident pool vs swapped-in hot buffer)."""
+
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from tests.gpu_cases import dev, gpu_inputs, log, make, oracle_resolve, to_dev
+from tests.helpers import check_state_invariants, raw
+
+pytestmark = pytest.mark.gpu
+GOLD = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "worked_example.json")))
+
+
+def _pinned(a: np.ndarray) -> torch.Tensor:
+    t = torch.empty(a.shape, dtype=torch.float32, pin_memory=True)
+    t.copy_(torch.from_numpy(a))
+    return t
+
+
+def _run_finalize(B, R, cap, seq, bt, bs, pool, init_pos, init_stamp, logits, draft, new_kv, tick):
+    """Run GPU and oracle finalize on the same inputs; return both results."""
+    import sparse_attention_kv_amd as hs
+    from sparse_attention_kv_amd.pipeline import build_hot_state
+    ost = oracle.build_hot_state(init_pos, init_stamp, seq, bt, bs, pool.copy())
+    opool = pool.copy()
+    acc, nxt, am = oracle.greedy_accept(raw(logits), draft, B, R)
+    committed = oracle.finalize_accepted(ost, opool, new_kv, acc, seq, bt, bs, R, tick)
+    hpool = _pinned(pool)
+    gst = build_hot_state(torch.from_numpy(init_pos), torch.from_numpy(init_stamp), to_dev(seq),
+                          to_dev(bt), bs, hpool, dev())
+    g_am = torch.empty((B * R,), dtype=torch.int32, device=dev())
+    g_acc = torch.empty((B,), dtype=torch.int32, device=dev())
+    g_nxt = torch.empty((B,), dtype=torch.int32, device=dev())
+    log(f"finalize B={B} R={R} cap={cap} vocab={logits.shape[1]}")
+    hs.hs_finalize_accepted(gst, logits.to(dev()), to_dev(draft), torch.from_numpy(new_kv).to(dev()),
+                            R, to_dev(seq), to_dev(bt), bs, tick, g_am, g_acc, g_nxt)
+    torch.cuda.synchronize()
+    assert np.array_equal(g_am.cpu().numpy(), am)
+    assert np.array_equal(g_acc.cpu().numpy(), acc)
+    assert np.array_equal(g_nxt.cpu().numpy(), nxt)
+    assert np.array_equal(gst.slot_loc.cpu().numpy(), ost.slot_loc)
+    assert np.array_equal(gst.slot_stamp.cpu().numpy(), ost.slot_stamp)
+    assert np.array_equal(gst.loc_to_hot.cpu().numpy(), ost.loc_to_hot)
+    occ = np.nonzero(ost.slot_loc.reshape(-1) >= 0)[0]
+    assert np.array_equal(gst.hot_kv.cpu().numpy()[occ], ost.hot_kv[occ])
+    assert np.array_equal(hpool.numpy(), opool)
+    check_state_invariants(ost, opool)
+    return acc, nxt, committed, ost, opool
+
+
+def test_worked_example_on_gpu():
+    names = GOLD["token_names"]
+    R, P = len(GOLD["verify_rows"]), GOLD["prompt_len"]
+    seq = np.array([P + R], np.int32)
+    bt = np.array([[2, -1]], np.int32)
+    bs, cap = 16, 12
+    rng = np.random.default_rng(0)
+    pool = rng.standard_normal((3 * bs, 8)).astype(np.float32)
+    init_pos = np.full((1, cap), -1, np.int32)
+    init_stamp = np.full((1, cap), -1, np.int32)
+    init_pos[0, :9] = np.arange(9)
+    init_stamp[0, :9] = np.arange(9)
+    gen = torch.Generator().manual_seed(0)
+    logits = torch.randn(R, 64, generator=gen).to(torch.bfloat16)
+    for i, c in enumerate(GOLD["target_greedy_choice_per_row"]):
+        logits[i, names[c]] = 8.0
+    draft = np.array([names[r] for r in GOLD["verify_rows"]], np.int32)
+    new_kv = rng.standard_normal((R, 8)).astype(np.float32)
+    acc, nxt, committed, ost, _ = _run_finalize(1, R, cap, seq, bt, bs, pool, init_pos, init_stamp,
+                                                logits, draft, new_kv, tick=100)
+    exp = GOLD["expected"]
+    assert acc[0] == exp["accept_len"] and nxt[0] == names[exp["next_token"]]
+    assert committed[0] == exp["committed_len"]
+    kept = sorted(int(x) - 2 * bs for x in ost.slot_loc[0] if x >= 0)
+    assert kept == exp["kept_kv_positions"]
+
+
+@pytest.mark.parametrize("vocab", [61, 1000, 129280])
+def test_finalize_random_requests(vocab):
+    """Several requests: mixed accept lengths, ties, misses installed with the LRU rule."""
+    rng = np.random.default_rng(vocab)
+    B, R, cap, bs, width = 9, 4, 40, 8, 12
+    bt = rng.permutation(B * width).astype(np.int32).reshape(B, width)
+    seq = rng.integers(R + 1, width * bs, size=B).astype(np.int32)
+    pool = rng.standard_normal((B * width * bs, 16)).astype(np.float32)
+    init_pos = np.full((B, cap), -1, np.int32)
+    init_stamp = np.full((B, cap), -1, np.int32)
+    for b in range(B):
+        cnt = int(rng.integers(0, min(cap, seq[b]) + 1))
+        pos = rng.choice(int(seq[b]), cnt, replace=False)
+        sl = rng.permutation(cap)[:cnt]
+        init_pos[b, sl] = pos
+        init_stamp[b, sl] = rng.integers(0, 4, size=cnt)
+    gen = torch.Generator().manual_seed(vocab)
+    logits = torch.randn(B * R, vocab, generator=gen).to(torch.bfloat16)
+    plant = rng.integers(0, vocab, size=B * R)
+    logits[torch.arange(B * R), torch.from_numpy(plant)] = 9.0
+    for i in range(0, B * R, 3):                 # ties: a second maximum in some rows
+        logits[i, int(rng.integers(0, vocab))] = 9.0
+    draft = rng.integers(0, vocab, size=B * R).astype(np.int32)
+    for r in range(1, R):
+        for b in range(B):
+            if rng.random() < 0.75:
+                draft[r * B + b] = plant[(r - 1) * B + b]
+    new_kv = rng.standard_normal((B * R, 16)).astype(np.float32)
+    acc, *_ = _run_finalize(B, R, cap, seq, bt, bs, pool, init_pos, init_stamp, logits, draft,
+                            new_kv, tick=50)
+    log(f"accept lengths {acc.tolist()}")
+
+
+def test_attention_identical_on_resident_and_swap_paths():
+    """Same rows, same index order: the paged pool and the hot buffer give equal bits."""
+    import sparse_attention_kv_amd as hs
+    from sparse_attention_kv_amd.pipeline import DecodeStep
+    for name, over in (("tiny", {}), ("mtp_swap", dict(num_reqs=4, seq_rule=("const", 5000)))):
+        s, w = make(name, **over)
+        g = gpu_inputs(s, w)
+        from tests.test_gpu_swap import _both_states
+        ost, gst, pool = _both_states(s, w, g)
+        step = DecodeStep(num_reqs=s.num_reqs, rows_per_req=s.rows_per_req, topk=s.topk,
+                          num_heads=s.num_heads, d_qk=s.d_qk, d_v=s.d_v, dtype=w.q.dtype,
+                          capacity=s.capacity, device=dev())
+        log(f"cross-path {name}: swap path")
+        step.run_swap(gst, g["topk_pos"], g["req_id"], g["causal_limit"], g["block_table"],
+                      s.block_size, g["q"], s.scale, s.tick0)
+        torch.cuda.synchronize()
+        dev_pool = w.kv_pool.to(dev())
+        res = DecodeStep(num_reqs=s.num_reqs, rows_per_req=s.rows_per_req, topk=s.topk,
+                         num_heads=s.num_heads, d_qk=s.d_qk, d_v=s.d_v, dtype=w.q.dtype, device=dev())
+        # the resident path runs all rows at once; run it per wave so the split plan matches
+        B = s.num_reqs
+        log(f"cross-path {name}: resident path")
+        res.run_resident(g["topk_pos"], g["req_id"], g["causal_limit"], g["block_table"],
+                         s.block_size, g["q"], dev_pool, s.scale)
+        out_wave = torch.empty_like(res.buf.out)
+        for r in range(s.rows_per_req):
+            lo, hi = r * B, (r + 1) * B
+            ws_b = hs.hs_attn_workspace_bytes(B, s.num_heads, s.d_qk, s.d_v, s.topk, w.q.dtype)
+            ws = torch.empty((max(ws_b, 16),), dtype=torch.uint8, device=dev()) if ws_b else None
+            hs.hs_sparse_decode_attn(g["q"][lo:hi], dev_pool, res.buf.slots[lo:hi], s.scale, s.d_v,
+                                     out_wave[lo:hi], None, ws)
+        torch.cuda.synchronize()
+        assert torch.equal(out_wave, step.buf.out), name

@@ -1,0 +1,167 @@
+"""GPU parity of hs_swap_in and of a whole swap-path decode step against the oracle.
+
+Bit-exact: hot indices, miss counts and positions, slot_loc, slot_stamp, loc_to_hot and
+the hot-buffer rows of every occupied slot, after every wave.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from tests.gpu_cases import (BF16_TOL, F32_TOL, assert_close, dev, gpu_inputs, log, make,
+                             oracle_resolve, out_f64, to_dev)
+from tests.helpers import check_state_invariants, raw
+
+pytestmark = pytest.mark.gpu
+
+
+def _both_states(s, w, g):
+    from sparse_attention_kv_amd.pipeline import build_hot_state
+    pool = raw(w.kv_pool)
+    ost = oracle.build_hot_state(w.init_pos, w.init_stamp, w.seq_len, w.block_table, s.block_size, pool)
+    gst = build_hot_state(torch.from_numpy(w.init_pos), torch.from_numpy(w.init_stamp), g["seq_len"],
+                          g["block_table"], s.block_size, w.kv_pool, dev())
+    torch.cuda.synchronize()
+    return ost, gst, pool
+
+
+def _compare_state(ost, gst, what, with_kv=True):
+    assert np.array_equal(gst.slot_loc.cpu().numpy(), ost.slot_loc), what + " slot_loc"
+    assert np.array_equal(gst.slot_stamp.cpu().numpy(), ost.slot_stamp), what + " slot_stamp"
+    assert np.array_equal(gst.loc_to_hot.cpu().numpy(), ost.loc_to_hot), what + " loc_to_hot"
+    if with_kv:
+        occ = np.nonzero(ost.slot_loc.reshape(-1) >= 0)[0]
+        got = raw(gst.hot_kv.cpu())
+        assert np.array_equal(got[occ], ost.hot_kv[occ]), what + " hot_kv"
+
+
+@pytest.mark.parametrize("name", ["tiny", "mtp_swap", "long", "mixed_finalize"])
+def test_swap_waves_bit_exact(name):
+    import sparse_attention_kv_amd as hs
+    s, w = make(name)
+    g = gpu_inputs(s, w)
+    ost, gst, pool = _both_states(s, w, g)
+    _compare_state(ost, gst, f"{name} initial state")
+    slots, _ = oracle_resolve(s, w)
+    B, K = s.num_reqs, s.topk
+    for r in range(s.rows_per_req):
+        wave = slots[r * B:(r + 1) * B]
+        hot = torch.full((B, K), 7, dtype=torch.int32, device=dev())
+        mc = torch.full((B,), 7, dtype=torch.int32, device=dev())
+        mp = torch.full((B, K), 7, dtype=torch.int32, device=dev())
+        log(f"swap {name} wave {r}")
+        hs.hs_swap_in(gst, to_dev(wave), s.tick0 + r, hot, mc, mp)
+        torch.cuda.synchronize()
+        oh, omc, omp = oracle.swap_in(ost, wave, s.tick0 + r, pool)
+        assert np.array_equal(hot.cpu().numpy(), oh), f"{name} wave {r} hot_idx"
+        assert np.array_equal(mc.cpu().numpy(), omc), f"{name} wave {r} miss_count"
+        assert np.array_equal(mp.cpu().numpy(), omp), f"{name} wave {r} miss_pos"
+        _compare_state(ost, gst, f"{name} wave {r}", with_kv=(r == s.rows_per_req - 1 or name == "tiny"))
+        log(f"swap {name} wave {r}: misses/row {omc.mean():.1f} hit rate "
+            f"{1 - omc.sum() / max(1, (wave >= 0).sum()):.3f}")
+    check_state_invariants(ost, pool)
+
+
+def test_swap_capacity_error_leaves_state():
+    import sparse_attention_kv_amd as hs
+    s, w = make("tiny")
+    g = gpu_inputs(s, w)
+    ost, gst, pool = _both_states(s, w, g)
+    before = [t.clone() for t in (gst.slot_loc, gst.slot_stamp, gst.loc_to_hot, gst.hot_kv)]
+    wide = torch.zeros((s.num_reqs, s.capacity + 1), dtype=torch.int32, device=dev())
+    out = torch.empty_like(wide)
+    mc = torch.empty((s.num_reqs,), dtype=torch.int32, device=dev())
+    with pytest.raises(hs.HsError) as e:
+        hs.hs_swap_in(gst, wide, 5, out, mc)
+    assert e.value.status == hs.HS_ERR_CAPACITY
+    torch.cuda.synchronize()
+    after = (gst.slot_loc, gst.slot_stamp, gst.loc_to_hot, gst.hot_kv)
+    assert all(torch.equal(a, b) for a, b in zip(before, after))
+
+
+def test_swap_rejects_pageable_host_pool():
+    import sparse_attention_kv_amd as hs
+    s, w = make("tiny")
+    g = gpu_inputs(s, w)
+    _, gst, _ = _both_states(s, w, g)
+    gst.host_pool = w.kv_pool.clone()     # ordinary (pageable) host memory
+    assert not gst.host_pool.is_pinned()
+    out = torch.empty((s.num_reqs, s.topk), dtype=torch.int32, device=dev())
+    mc = torch.empty((s.num_reqs,), dtype=torch.int32, device=dev())
+    with pytest.raises(hs.HsError) as e:
+        hs.hs_swap_in(gst, torch.zeros_like(out), 5, out, mc)
+    assert e.value.status == hs.HS_ERR_INVALID_ARG
+
+
+def _pipeline_case(name, sample_rows_per_wave=6):
+    """Whole step through DecodeStep.run_swap (copy stream overlapped with attention)."""
+    from sparse_attention_kv_amd.pipeline import DecodeStep
+    s, w = make(name)
+    g = gpu_inputs(s, w)
+    ost, gst, pool = _both_states(s, w, g)
+    B, R = s.num_reqs, s.rows_per_req
+    fin = None
+    snap = None
+    if s.finalize:
+        # host rows the finalize step may overwrite: the verify rows' positions
+        locs = np.concatenate([oracle.resolve_topk(
+            (w.seq_len[b] - R + np.arange(R, dtype=np.int32))[None, :], np.array([b], np.int32),
+            np.array([w.seq_len[b]], np.int32), w.block_table, s.block_size, s.block_size, B)[0][0]
+            for b in range(B)])
+        locs = locs[locs >= 0]
+        snap = (locs, w.kv_pool[torch.from_numpy(locs).long()].clone())
+        fin = dict(logits=w.logits.to(dev()), draft_ids=to_dev(w.draft_ids),
+                   new_kv=w.new_kv.to(dev()), seq_len=g["seq_len"])
+    step = DecodeStep(num_reqs=B, rows_per_req=R, topk=s.topk, num_heads=s.num_heads, d_qk=s.d_qk,
+                      d_v=s.d_v, dtype=w.q.dtype, capacity=s.capacity, finalize=s.finalize,
+                      want_miss_pos=True, device=dev())
+    log(f"pipeline {name}: run_swap")
+    step.run_swap(gst, g["topk_pos"], g["req_id"], g["causal_limit"], g["block_table"],
+                  s.block_size, g["q"], s.scale, s.tick0, finalize=fin)
+    torch.cuda.synchronize()
+    log(f"pipeline {name}: oracle")
+    gpu_fin_rows = None
+    if snap is not None:
+        locs, orig = snap
+        gpu_fin_rows = w.kv_pool[torch.from_numpy(locs).long()].clone()
+        w.kv_pool[torch.from_numpy(locs).long()] = orig        # oracle starts from the original rows
+    slots, valid = oracle_resolve(s, w)
+    assert np.array_equal(step.buf.slots.cpu().numpy(), slots)
+    assert np.array_equal(step.buf.valid.cpu().numpy(), valid)
+    hot_all = np.empty_like(slots)
+    for r in range(R):
+        oh, omc, omp = oracle.swap_in(ost, slots[r * B:(r + 1) * B], s.tick0 + r, pool)
+        hot_all[r * B:(r + 1) * B] = oh
+        assert np.array_equal(step.buf.miss_count[r].cpu().numpy(), omc)
+        assert np.array_equal(step.buf.miss_pos[r * B:(r + 1) * B].cpu().numpy(), omp)
+    assert np.array_equal(step.buf.hot_idx.cpu().numpy(), hot_all)
+    # attention on sampled rows of every wave, against the oracle over the host pool
+    rng = np.random.default_rng(0)
+    q_raw = raw(w.q)
+    sample = np.concatenate([r * B + rng.choice(B, min(B, sample_rows_per_wave), replace=False)
+                             for r in range(R)])
+    ref, rlse = oracle.sparse_decode_attn(q_raw[sample], pool, slots[sample], s.scale, s.d_v)
+    tol = F32_TOL if s.dtype == "f32" else BF16_TOL
+    assert_close(out_f64(step.buf.out[torch.from_numpy(sample).to(dev())]), ref, tol, f"{name} attention")
+    if s.finalize:
+        acc, nxt, am = oracle.greedy_accept(raw(w.logits), w.draft_ids, B, R)
+        assert np.array_equal(step.buf.argmax.cpu().numpy(), am)
+        assert np.array_equal(step.buf.accept_len.cpu().numpy(), acc)
+        assert np.array_equal(step.buf.next_token.cpu().numpy(), nxt)
+        oracle.finalize_accepted(ost, pool, raw(w.new_kv), acc, w.seq_len, w.block_table,
+                                 s.block_size, R, s.tick0 + R)
+        locs, _ = snap
+        assert np.array_equal(raw(gpu_fin_rows), pool[locs]), "host rows after finalize"
+        log(f"finalize {name}: accept-length histogram {np.bincount(acc, minlength=R).tolist()}")
+    _compare_state(ost, gst, f"{name} after step")
+    check_state_invariants(ost, pool)
+
+
+@pytest.mark.parametrize("name", ["tiny", "mtp_swap"])
+def test_pipeline_step(name):
+    _pipeline_case(name)
+
+
+def test_pipeline_step_with_finalize_full():
+    _pipeline_case("mixed_finalize", sample_rows_per_wave=4)

@@ -1,0 +1,123 @@
+"""The C-ABI library loads and exports every symbol include/hisparse.h declares; its host
+validation rejects bad arguments before any HIP call (runs without a GPU)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "hisparse.h")
+LIB = os.path.join(ROOT, "sparse_attention_kv_amd", "libhisparse.so")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(LIB), reason="libhisparse.so not built")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(hs_[a-z_0-9]+)\s*\(", src)))
+
+
+def test_header_declares_the_four_calls():
+    names = _declared()
+    for n in ("hs_resolve_topk", "hs_swap_in", "hs_sparse_decode_attn", "hs_finalize_accepted"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(LIB)
+    missing = [n for n in _declared() if not hasattr(lib, n)]
+    assert not missing, missing
+
+
+def test_binding_exports_match_header():
+    import sparse_attention_kv_amd as hs
+    assert sorted(hs.EXPORTED) == _declared()
+    assert hs.version().startswith("hisparse-gfx950")
+    assert hs.status_string(hs.HS_ERR_CAPACITY) == "top-k exceeds hot-buffer capacity"
+
+
+def _lib():
+    import sparse_attention_kv_amd as hs
+    return hs, hs._lib
+
+
+def test_resolve_validation():
+    hs, lib = _lib()
+    p = ctypes.c_void_p(16)
+    # num_rows == 0 is a no-op
+    assert lib.hs_resolve_topk(None, 0, 16, None, None, 1, None, 4, 16, 16, None, None, None) == hs.HS_OK
+    assert lib.hs_resolve_topk(p, -1, 16, p, p, 1, p, 4, 16, 16, p, None, None) == hs.HS_ERR_INVALID_ARG
+    assert lib.hs_resolve_topk(p, 2, 0, p, p, 1, p, 4, 16, 16, p, None, None) == hs.HS_ERR_INVALID_ARG
+    assert lib.hs_resolve_topk(p, 2, 16, p, p, 1, p, 4, 0, 16, p, None, None) == hs.HS_ERR_INVALID_ARG
+    assert lib.hs_resolve_topk(None, 2, 16, p, p, 1, p, 4, 16, 16, p, None, None) == hs.HS_ERR_INVALID_ARG
+    assert lib.hs_resolve_topk(p, 2, 16, p, p, 1, p, 4, 16, 16, None, None, None) == hs.HS_ERR_INVALID_ARG
+
+
+def _state(hs, **kw):
+    d = dict(num_reqs=2, capacity=24, slot_loc=16, slot_stamp=32, loc_to_hot=48, host_rows=256,
+             row_elems=64, dtype=hs.HS_F32, hot_kv=64, host_pool=128)
+    d.update(kw)
+    return hs.HsHotState(**d)
+
+
+def test_swap_validation():
+    hs, lib = _lib()
+    p = ctypes.c_void_p(16)
+    st = _state(hs)
+    # top-k beyond the hot-buffer capacity -> capacity error, nothing touched
+    assert lib.hs_swap_in(ctypes.byref(st), p, 25, 1, p, p, None, None) == hs.HS_ERR_CAPACITY
+    assert lib.hs_swap_in(None, p, 16, 1, p, p, None, None) == hs.HS_ERR_INVALID_ARG
+    assert lib.hs_swap_in(ctypes.byref(st), None, 16, 1, p, p, None, None) == hs.HS_ERR_INVALID_ARG
+    assert lib.hs_swap_in(ctypes.byref(st), p, 0, 1, p, p, None, None) == hs.HS_ERR_INVALID_ARG
+    bad = _state(hs, row_elems=6)         # 24-byte rows are not a multiple of 16
+    assert lib.hs_swap_in(ctypes.byref(bad), p, 16, 1, p, p, None, None) == hs.HS_ERR_INVALID_ARG
+    bad = _state(hs, hot_kv=72)           # misaligned hot buffer
+    assert lib.hs_swap_in(ctypes.byref(bad), p, 16, 1, p, p, None, None) == hs.HS_ERR_INVALID_ARG
+    bad = _state(hs, dtype=7)
+    assert lib.hs_swap_in(ctypes.byref(bad), p, 16, 1, p, p, None, None) == hs.HS_ERR_INVALID_ARG
+    big = _state(hs, capacity=20000)
+    assert lib.hs_swap_in(ctypes.byref(big), p, 16, 1, p, p, None, None) == hs.HS_ERR_UNSUPPORTED
+    wide = _state(hs, capacity=8192)
+    assert lib.hs_swap_in(ctypes.byref(wide), p, 5000, 1, p, p, None, None) == hs.HS_ERR_UNSUPPORTED
+
+
+def test_attn_validation_and_workspace():
+    hs, lib = _lib()
+    p = ctypes.c_void_p(16)
+    assert lib.hs_sparse_decode_attn(p, p, 10, p, 0, 128, 576, 512, 2048, 1.0, hs.HS_BF16, p, None,
+                                      None, 0, None) == hs.HS_OK
+    # unsupported shapes of the bf16 MFMA path
+    assert lib.hs_sparse_decode_attn(p, p, 10, p, 2, 128, 512, 512, 2048, 1.0, hs.HS_BF16, p, None,
+                                      None, 0, None) == hs.HS_ERR_UNSUPPORTED
+    assert lib.hs_sparse_decode_attn(p, p, 10, p, 2, 100, 576, 512, 2048, 1.0, hs.HS_BF16, p, None,
+                                      None, 0, None) == hs.HS_ERR_UNSUPPORTED
+    assert lib.hs_sparse_decode_attn(p, p, 10, p, 2, 4, 2048, 48, 16, 1.0, hs.HS_F32, p, None,
+                                      None, 0, None) == hs.HS_ERR_UNSUPPORTED
+    assert lib.hs_sparse_decode_attn(p, p, 10, p, 2, 4, 64, 48, 16, 1.0, 9, p, None,
+                                      None, 0, None) == hs.HS_ERR_INVALID_ARG
+    # split-KV shapes need the workspace the library asks for
+    ws = lib.hs_attn_workspace_bytes(8, 128, 576, 512, 2048, hs.HS_BF16)
+    assert ws > 0
+    assert lib.hs_sparse_decode_attn(p, p, 10, p, 8, 128, 576, 512, 2048, 1.0, hs.HS_BF16, p, None,
+                                      None, 0, None) == hs.HS_ERR_INVALID_ARG
+    assert lib.hs_sparse_decode_attn(p, p, 10, p, 8, 128, 576, 512, 2048, 1.0, hs.HS_BF16, p, None,
+                                      p, ws - 16, None) == hs.HS_ERR_INVALID_ARG
+    # large batches need no split and no workspace
+    assert lib.hs_attn_workspace_bytes(256, 128, 576, 512, 2048, hs.HS_BF16) == 0
+    assert lib.hs_attn_workspace_bytes(4, 4, 64, 48, 16, hs.HS_F32) == 0
+
+
+def test_finalize_validation():
+    hs, lib = _lib()
+    p = ctypes.c_void_p(16)
+    st = _state(hs)
+    args = lambda **k: [ctypes.byref(k.get("st", st)), p, k.get("vocab", 100), p, p,
+                        k.get("R", 3), p, p, 4, 16, 1, p, p, p, None]
+    assert lib.hs_finalize_accepted(*args(vocab=0)) == hs.HS_ERR_INVALID_ARG
+    assert lib.hs_finalize_accepted(*args(R=0)) == hs.HS_ERR_INVALID_ARG
+    assert lib.hs_finalize_accepted(*args(R=25)) == hs.HS_ERR_INVALID_ARG   # > capacity
+    big = _state(hs, capacity=200)
+    assert lib.hs_finalize_accepted(*args(st=big, R=65)) == hs.HS_ERR_UNSUPPORTED

@@ -211,12 +211,15 @@ def _topk_row(rng, c: int, K: int, prev: Optional[np.ndarray], p: float) -> np.n
     return row
 
 
-def generate(s: WorkloadSpec, big_device: str = "cpu", pin_host_pool: bool = False) -> Workload:
+def generate(s: WorkloadSpec, big_device: str = "cpu", pin_host_pool: bool = False,
+             tensors: bool = True) -> Workload:
     """Draw one step's inputs for workload `s`.
 
     `big_device` is where the KV pool is drawn ("cpu" or "cuda"); for swap workloads
     the pool is then delivered in pinned host memory when `pin_host_pool`, and for
     the resident workload it stays on `big_device` (it is the paged device pool).
+    With `tensors=False` only the index structure is drawn (kv_pool, q, logits and
+    new_kv are None); every index array is the same as with tensors.
     """
     ss = np.random.SeedSequence(ROOT_SEED).spawn(len(CONFIGS) + 8)[s.index]
     r_seq, r_bt, r_topk, r_hot, r_tensor, r_acc = [np.random.default_rng(x) for x in ss.spawn(6)]
@@ -266,7 +269,9 @@ def generate(s: WorkloadSpec, big_device: str = "cpu", pin_host_pool: bool = Fal
 
     dt = _torch_dtype(s.dtype)
     host_rows = num_pages * s.block_size
-    if s.resident:
+    if not tensors:
+        kv_pool = q = None
+    elif s.resident:
         kv_pool = _randn((host_rows, s.d_qk), dt, tseeds[0], device=big_device)
     else:
         kv_pool = _randn((host_rows, s.d_qk), dt, tseeds[0], device=big_device,
@@ -275,7 +280,8 @@ def generate(s: WorkloadSpec, big_device: str = "cpu", pin_host_pool: bool = Fal
             host = torch.empty((host_rows, s.d_qk), dtype=dt, pin_memory=pin_host_pool)
             host.copy_(kv_pool)
             kv_pool = host
-    q = _randn((rows, s.num_heads, s.d_qk), dt, tseeds[1])
+    if tensors:
+        q = _randn((rows, s.num_heads, s.d_qk), dt, tseeds[1])
 
     w = Workload(spec=s, seq_len=seq, block_table=bt, num_pages=num_pages, req_id=req_id,
                  causal_limit=causal, topk_pos=topk, kv_pool=kv_pool, q=q,
@@ -283,18 +289,20 @@ def generate(s: WorkloadSpec, big_device: str = "cpu", pin_host_pool: bool = Fal
 
     if s.finalize:
         V = s.vocab
-        logits = _randn((rows, V), torch.bfloat16, tseeds[2])
+        logits = _randn((rows, V), torch.bfloat16, tseeds[2]) if tensors else None
         # Plant a maximum per row (a value no N(0,1) bf16 draw reaches), and in a
         # fraction of rows a second, equal maximum: the accept rule then has to break
         # the tie.  Draft ids copy the planted id of the previous row with
         # probability q_acc, so acceptance lengths spread over 0..R-1.
         plant = r_acc.integers(0, V, size=rows)
-        logits[torch.arange(rows), torch.from_numpy(plant)] = 16.0
+        if tensors:
+            logits[torch.arange(rows), torch.from_numpy(plant)] = 16.0
         tie_rows = np.nonzero(r_acc.random(rows) < s.tie_frac)[0]
         for i in tie_rows:
             other = int(r_acc.integers(0, V - 1))
             other += other >= plant[i]
-            logits[int(i), other] = 16.0
+            if tensors:
+                logits[int(i), other] = 16.0
         draft = r_acc.integers(0, V, size=rows).astype(np.int64)
         for r in range(1, R):
             for b in range(B):
@@ -306,5 +314,5 @@ def generate(s: WorkloadSpec, big_device: str = "cpu", pin_host_pool: bool = Fal
                     draft[r * B + b] = d + (d >= src)
         w.logits = logits
         w.draft_ids = draft.astype(np.int32)
-        w.new_kv = _randn((rows, s.d_qk), dt, tseeds[3])
+        w.new_kv = _randn((rows, s.d_qk), dt, tseeds[3]) if tensors else None
     return w
