@@ -55,31 +55,46 @@ __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x3f70)
 __device__ __forceinline__ float fmax3(float a, float b) { return a > b ? a : b; }
 
 // Gather tile t (selected rows t*64 .. t*64+63 of the compacted list) into LDS buffer dst.
-// Physical 16-byte chunk c of the tile holds (key c/72, logical part (c%72) ^ (key&7)).
+// Physical 16-byte chunk c of the tile holds (key c/72, logical part (c%72) ^ ((key>>1)&7));
+// with a 1152-byte row stride this puts any 16 consecutive keys' chunk p in 16 distinct
+// 16-byte bank groups.
 // Keys past n_valid re-load the last valid row; their scores are masked to -inf.
+// Wave w issues the 18 consecutive 1 KiB slots n = 18w .. 18w+17; lane l's chunk in slot
+// n is c = 64n + l, so (key, part) advance by (+0/+1, +64 mod 72) from slot to slot.
 __device__ __forceinline__ void gather_tile(const uint8_t *__restrict__ kv,
                                             const int32_t *sidx, int n_valid, int t,
                                             uint8_t *dst, int w, int l) {
+  const int c0 = w * kLoadsPerThread * 64 + l;
+  int key = c0 / kRowChunks;
+  int part = c0 - key * kRowChunks;
+  const int last = n_valid - 1;
   // All row-index reads first: the DMA writes LDS, so the compiler will not hoist a
   // later LDS read above an earlier DMA issue.
-  int rows[kLoadsPerThread];
+  int rows[kLoadsPerThread], parts[kLoadsPerThread];
 #pragma unroll
   for (int i = 0; i < kLoadsPerThread; ++i) {
-    const int c = (w * kLoadsPerThread + i) * 64 + l;
-    int kk = t * kTK + c / kRowChunks;
-    kk = kk < n_valid ? kk : n_valid - 1;
-    rows[i] = sidx[kk];
+    const int kk = t * kTK + key;
+    rows[i] = sidx[kk < last ? kk : last];
+    parts[i] = part ^ ((key >> 1) & 7);
+    part += 64;
+    const bool wrap = part >= kRowChunks;
+    part = wrap ? part - kRowChunks : part;
+    key += wrap ? 1 : 0;
   }
 #pragma unroll
   for (int i = 0; i < kLoadsPerThread; ++i) {
-    const int n = w * kLoadsPerThread + i;   // 1 KiB wave-instruction slot
-    const int c = n * 64 + l;
-    const int key = c / kRowChunks;
-    const int part = (c - key * kRowChunks) ^ (key & 7);
-    const uint8_t *src = kv + (int64_t)rows[i] * kRowBytes + part * 16;
-    __builtin_amdgcn_global_load_lds(src, (HS_LDS void *)(dst + n * 1024), 16, 0, 0);
+    const uint8_t *src = kv + (int64_t)rows[i] * kRowBytes + parts[i] * 16;
+    __builtin_amdgcn_global_load_lds(src, (HS_LDS void *)(dst + (w * kLoadsPerThread + i) * 1024),
+                                     16, 0, 0);
   }
 }
+
+// Scores are kept relative to a reference max m_ref per head (log2 domain).  P is formed
+// as 2^(s - m_ref) without re-normalising O every tile; only when a score exceeds m_ref
+// by more than kRescaleSlack (P would exceed 2^kRescaleSlack) do all waves agree on a
+// new reference and rescale O and the running sum.  The arithmetic is exact for any
+// reference; the slack only bounds P (bf16) and the fp32 accumulators.
+constexpr float kRescaleSlack = 64.f;
 
 template <bool kSplit>
 __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(
@@ -96,6 +111,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(
   __shared__ __attribute__((aligned(16))) float s_fm[kHG];
   __shared__ __attribute__((aligned(16))) float s_fl[kHG];
   __shared__ int s_scan[8];
+  __shared__ int s_flag[4];
 
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
   const int n_hg = num_heads / kHG;
@@ -112,6 +128,16 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(
   const int kbeg = split * keys_per_split;
   const int kcnt = max(0, min(keys_per_split, topk - kbeg));
 
+  // ---- indices of this split (issued first: they gate the first KV gather) ----
+  const int32_t *irow = indices + (int64_t)row * topk + kbeg;
+  const int per = (kcnt + kThreads - 1) / kThreads;  // <= 8
+  int vals[kMaxKeysPerSplit / kThreads];
+#pragma unroll
+  for (int k = 0; k < kMaxKeysPerSplit / kThreads; ++k) {
+    const int j = tid * per + k;
+    vals[k] = (k < per && j < kcnt) ? irow[j] : -1;
+  }
+
   // ---- Q (32 heads x 576) into registers as the B operand of S^T = K Q^T ----
   bf16x8 qreg[2][kD / 32];
   {
@@ -124,21 +150,15 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(
                                                          32 * ks + 8 * (l >> 4));
   }
 
-  // ---- compact this split's valid indices into LDS (order preserved) ----
+  // ---- compact the valid indices into LDS (order preserved) ----
   int n_valid;
   {
-    const int32_t *irow = indices + (int64_t)row * topk + kbeg;
-    const int per = (kcnt + kThreads - 1) / kThreads;  // <= 8
-    int vals[kMaxKeysPerSplit / kThreads];
     int cnt = 0;
 #pragma unroll
     for (int k = 0; k < kMaxKeysPerSplit / kThreads; ++k) {
-      vals[k] = -1;
-      if (k < per) {
-        const int j = tid * per + k;
-        const int v = j < kcnt ? irow[j] : -1;
-        if (v >= 0 && v < kv_rows) { vals[k] = v; ++cnt; }
-      }
+      const bool ok = vals[k] >= 0 && vals[k] < kv_rows;
+      vals[k] = ok ? vals[k] : -1;
+      cnt += ok;
     }
     int wave_total;
     const int ex = wave_exclusive_scan(cnt, wave_total);
@@ -156,11 +176,11 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(
     for (int k = 0; k < kMaxKeysPerSplit / kThreads; ++k)
       if (vals[k] >= 0) s_sidx[pos++] = vals[k];
     n_valid = total;
-    __syncthreads();
+    lds_barrier();
   }
 
   const int ntiles = (n_valid + kTK - 1) / kTK;
-  float m_run[2] = {-INFINITY, -INFINITY};
+  float m_ref[2] = {-INFINITY, -INFINITY};
   float l_run[2] = {0.f, 0.f};
   f32x16 oacc[4];
 #pragma unroll
@@ -168,77 +188,171 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(
 #pragma unroll
     for (int i = 0; i < 16; ++i) oacc[nb][i] = 0.f;
 
+  // O (32 heads x this wave's 128 dims) += P V for the tile in `cur`.  Operands of the
+  // next 16-key step (one P fragment, eight transposed V reads) are issued before the
+  // four MFMAs of the current step.
+  auto pv_tile = [&](const uint8_t *cur) {
+    typedef short s16x4 __attribute__((ext_vector_type(4)));
+    const int g = l >> 4, j = l & 15, r = j >> 2, c = j & 3;
+    const uint8_t *prow = s_p + (l & 31) * kPStride + 16 * (l >> 5);
+    int voff[4];
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) voff[nb] = 128 * w + 32 * nb + 16 * (g & 1) + 4 * c;
+    bf16x8 pa[2];
+    s16x4 vlo[2][4], vhi[2][4];
+    auto load_step = [&](int ks, int buf) {
+      pa[buf] = *reinterpret_cast<const bf16x8 *>(prow + 32 * ks);
+      const int key0 = 16 * ks + 8 * (g >> 1) + r;
+      const int key1 = key0 + 4;
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) {
+        const int part = voff[nb] >> 3, off = (voff[nb] & 7) * 2;
+        vlo[buf][nb] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (HS_LDS s16x4 *)(cur + key0 * kRowBytes + ((part ^ ((key0 >> 1) & 7)) << 4) + off));
+        vhi[buf][nb] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (HS_LDS s16x4 *)(cur + key1 * kRowBytes + ((part ^ ((key1 >> 1) & 7)) << 4) + off));
+      }
+    };
+    load_step(0, 0);
+#pragma unroll
+    for (int ks = 0; ks < kTK / 16; ++ks) {
+      if (ks + 1 < kTK / 16) load_step(ks + 1, (ks + 1) & 1);
+      __builtin_amdgcn_sched_barrier(0);
+      const int b = ks & 1;
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) {
+        typedef short s16x8 __attribute__((ext_vector_type(8)));
+        const s16x8 vv = {vlo[b][nb][0], vlo[b][nb][1], vlo[b][nb][2], vlo[b][nb][3],
+                          vhi[b][nb][0], vhi[b][nb][1], vhi[b][nb][2], vhi[b][nb][3]};
+        oacc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa[b], __builtin_bit_cast(bf16x8, vv),
+                                                           oacc[nb], 0, 0, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
   if (ntiles > 0) gather_tile(kv, s_sidx, n_valid, 0, s_kv0, w, l);
 
-  for (int t = 0; t < ntiles; ++t) {
-    uint8_t *cur = (t & 1) ? s_kv1 : s_kv0;
-    uint8_t *nxt = (t & 1) ? s_kv0 : s_kv1;
-    wait_vmem();
-    lds_barrier();
-    if (t + 1 < ntiles) gather_tile(kv, s_sidx, n_valid, t + 1, nxt, w, l);
+  // The inner loop touches O only through MFMA; a tile whose scores need a new reference
+  // (always the first one) leaves it, O is rescaled once outside, and the loop resumes.
+  int t = 0;
+  while (t < ntiles) {
+    bool renorm = false;
+    for (; t < ntiles; ++t) {
+      const uint8_t *cur = (t & 1) ? s_kv1 : s_kv0;
+      uint8_t *nxt = (t & 1) ? s_kv0 : s_kv1;
+      wait_vmem();
+      lds_barrier();
+      if (t + 1 < ntiles) gather_tile(kv, s_sidx, n_valid, t + 1, nxt, w, l);
 
-    // ---- S^T (16 keys of this wave x 32 heads) ----
-    f32x4 sacc[2];
+      // ---- S^T (16 keys of this wave x 32 heads), K fragments read 6 at a time ahead ----
+      f32x4 sacc[2];
 #pragma unroll
-    for (int hb = 0; hb < 2; ++hb)
+      for (int hb = 0; hb < 2; ++hb)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) sacc[hb][i] = 0.f;
-    {
-      const int key = 16 * w + (l & 15);
-      const uint8_t *krow = cur + key * kRowBytes;
-      const int sw = key & 7;
-      bf16x8 kf[kD / 32];
+        for (int i = 0; i < 4; ++i) sacc[hb][i] = 0.f;
+      {
+        const int key = 16 * w + (l & 15);
+        const uint8_t *krow = cur + key * kRowBytes;
+        const int sw = (key >> 1) & 7;
+        constexpr int kB = 6;
+        bf16x8 kf[2][kB];
 #pragma unroll
-      for (int ks = 0; ks < kD / 32; ++ks)
-        kf[ks] = *reinterpret_cast<const bf16x8 *>(krow + (((4 * ks + (l >> 4)) ^ sw) << 4));
+        for (int j = 0; j < kB; ++j)
+          kf[0][j] = *reinterpret_cast<const bf16x8 *>(krow + (((4 * j + (l >> 4)) ^ sw) << 4));
 #pragma unroll
-      for (int ks = 0; ks < kD / 32; ++ks) {
-        sacc[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[ks], qreg[0][ks], sacc[0], 0, 0, 0);
-        sacc[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[ks], qreg[1][ks], sacc[1], 0, 0, 0);
+        for (int bt = 0; bt < kD / 32 / kB; ++bt) {
+          if (bt + 1 < kD / 32 / kB) {
+#pragma unroll
+            for (int j = 0; j < kB; ++j) {
+              const int ks = (bt + 1) * kB + j;
+              kf[(bt + 1) & 1][j] =
+                  *reinterpret_cast<const bf16x8 *>(krow + (((4 * ks + (l >> 4)) ^ sw) << 4));
+            }
+          }
+          __builtin_amdgcn_sched_barrier(0);  // keep the next batch's reads ahead of these MFMAs
+#pragma unroll
+          for (int j = 0; j < kB; ++j) {
+            const int ks = bt * kB + j;
+            sacc[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[bt & 1][j], qreg[0][ks], sacc[0], 0, 0, 0);
+            sacc[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[bt & 1][j], qreg[1][ks], sacc[1], 0, 0, 0);
+          }
+        }
       }
-    }
 
-    // ---- online softmax (lane holds keys 4*(l>>4)+i of this wave, head l&15 (+16)) ----
-    const int kfirst = t * kTK + 16 * w + 4 * (l >> 4);
-    float s[2][4];
-    float mw[2];
+      // ---- softmax numerators against the reference max ----
+      const int kfirst = t * kTK + 16 * w + 4 * (l >> 4);
+      float s[2][4];
+      float mw[2];
+      bool over = false;
 #pragma unroll
-    for (int hb = 0; hb < 2; ++hb) {
-      mw[hb] = -INFINITY;
+      for (int hb = 0; hb < 2; ++hb) {
+        mw[hb] = -INFINITY;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        s[hb][i] = (kfirst + i < n_valid) ? sacc[hb][i] * scale_log2 : -INFINITY;
-        mw[hb] = fmax3(mw[hb], s[hb][i]);
+        for (int i = 0; i < 4; ++i) {
+          s[hb][i] = (kfirst + i < n_valid) ? sacc[hb][i] * scale_log2 : -INFINITY;
+          mw[hb] = fmax3(mw[hb], s[hb][i]);
+        }
+        over |= mw[hb] > m_ref[hb] + kRescaleSlack;
       }
-      mw[hb] = fmax3(mw[hb], __shfl_xor(mw[hb], 16, 64));
-      mw[hb] = fmax3(mw[hb], __shfl_xor(mw[hb], 32, 64));
-      if (l < 16) s_red[w][16 * hb + l] = mw[hb];
-    }
-    lds_barrier();
+      const bool any_over = __builtin_amdgcn_ballot_w64(over) != 0;
+      float psum[2] = {0.f, 0.f};
+      if (!any_over) {
 #pragma unroll
-    for (int hb = 0; hb < 2; ++hb) {
-      const int h = 16 * hb + (l & 15);
-      float tm = fmax3(fmax3(s_red[0][h], s_red[1][h]), fmax3(s_red[2][h], s_red[3][h]));
-      const float m_new = fmax3(m_run[hb], tm);
-      const bool none = m_new == -INFINITY;
-      const float alpha = none ? 1.f : __builtin_amdgcn_exp2f(m_run[hb] - m_new);
-      float psum = 0.f;
-      bf16x4 pk;
+        for (int hb = 0; hb < 2; ++hb) {
+          const int h = 16 * hb + (l & 15);
+          bf16x4 pk;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float p = none ? 0.f : __builtin_amdgcn_exp2f(s[hb][i] - m_new);
-        psum += p;
-        pk[i] = (__bf16)p;
+          for (int i = 0; i < 4; ++i) {
+            const float p = __builtin_amdgcn_exp2f(s[hb][i] - m_ref[hb]);
+            psum[hb] += p;
+            pk[i] = (__bf16)p;
+          }
+          *reinterpret_cast<bf16x4 *>(s_p + h * kPStride + (16 * w + 4 * (l >> 4)) * 2) = pk;
+        }
       }
-      l_run[hb] = l_run[hb] * alpha + psum;
-      m_run[hb] = m_new;
-      *reinterpret_cast<bf16x4 *>(s_p + h * kPStride + (16 * w + 4 * (l >> 4)) * 2) = pk;
-      if (w == 0 && l < 16) s_alpha[h] = alpha;
+      // publish this wave's per-head maxima and whether it needs a new reference
+#pragma unroll
+      for (int hb = 0; hb < 2; ++hb) {
+        mw[hb] = fmax3(mw[hb], __shfl_xor(mw[hb], 16, 64));
+        mw[hb] = fmax3(mw[hb], __shfl_xor(mw[hb], 32, 64));
+        if (l < 16) s_red[w][16 * hb + l] = mw[hb];
+      }
+      if (l == 0) s_flag[w] = any_over;
+      lds_barrier();
+      if (s_flag[0] | s_flag[1] | s_flag[2] | s_flag[3]) {
+        // new reference from all waves' maxima; running sums rescaled, P redone
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb) {
+          const int h = 16 * hb + (l & 15);
+          const float tm = fmax3(fmax3(s_red[0][h], s_red[1][h]), fmax3(s_red[2][h], s_red[3][h]));
+          const float m_new = fmax3(m_ref[hb], tm);
+          const bool none = m_new == -INFINITY;
+          const float alpha = none ? 1.f : __builtin_amdgcn_exp2f(m_ref[hb] - m_new);
+          float ps = 0.f;
+          bf16x4 pk;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float p = none ? 0.f : __builtin_amdgcn_exp2f(s[hb][i] - m_new);
+            ps += p;
+            pk[i] = (__bf16)p;
+          }
+          l_run[hb] = l_run[hb] * alpha + ps;
+          m_ref[hb] = m_new;
+          *reinterpret_cast<bf16x4 *>(s_p + h * kPStride + (16 * w + 4 * (l >> 4)) * 2) = pk;
+          if (w == 0 && l < 16) s_alpha[h] = alpha;
+        }
+        renorm = true;
+        break;
+      }
+      l_run[0] += psum[0];
+      l_run[1] += psum[1];
+      pv_tile(cur);
     }
+    if (!renorm) break;
+    // ---- rare path: rescale O by alpha (O is still zero on the first tile), then PV ----
     lds_barrier();
-
-    // ---- O (32 heads x this wave's 128 dims) = alpha * O + P V ----
-    {
+    if (t > 0) {
       f32x4 a4[4];
 #pragma unroll
       for (int qd = 0; qd < 4; ++qd)
@@ -247,29 +361,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(
       for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) oacc[nb][i] *= a4[i >> 2][i & 3];
-      const int g = l >> 4, j = l & 15, r = j >> 2, c = j & 3;
-#pragma unroll
-      for (int ks = 0; ks < kTK / 16; ++ks) {
-        const bf16x8 pa = *reinterpret_cast<const bf16x8 *>(s_p + (l & 31) * kPStride +
-                                                            (16 * ks + 8 * (l >> 5)) * 2);
-        const int key0 = 16 * ks + 8 * (g >> 1) + r;
-        const int key1 = key0 + 4;
-#pragma unroll
-        for (int nb = 0; nb < 4; ++nb) {
-          const int dim = 128 * w + 32 * nb + 16 * (g & 1) + 4 * c;
-          const int part = dim >> 3, off = (dim & 7) * 2;
-          const uint8_t *p0 = cur + key0 * kRowBytes + ((part ^ (key0 & 7)) << 4) + off;
-          const uint8_t *p1 = cur + key1 * kRowBytes + ((part ^ (key1 & 7)) << 4) + off;
-          typedef short s16x4 __attribute__((ext_vector_type(4)));
-          const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((HS_LDS s16x4 *)p0);
-          const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((HS_LDS s16x4 *)p1);
-          typedef short s16x8 __attribute__((ext_vector_type(8)));
-          const s16x8 vv = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
-          oacc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa, __builtin_bit_cast(bf16x8, vv),
-                                                             oacc[nb], 0, 0, 0);
-        }
-      }
     }
+    pv_tile((t & 1) ? s_kv1 : s_kv0);
+    ++t;
   }
 
   // ---- epilogue: total softmax sums, normalise, write ----
@@ -279,7 +373,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(
     lr += __shfl_xor(lr, 16, 64);
     lr += __shfl_xor(lr, 32, 64);
     if (l < 16) s_red[w][16 * hb + l] = lr;
-    if (w == 0 && l < 16) s_fm[16 * hb + l] = m_run[hb];
+    if (w == 0 && l < 16) s_fm[16 * hb + l] = m_ref[hb];
   }
   lds_barrier();
   if (tid < kHG) s_fl[tid] = s_red[0][tid] + s_red[1][tid] + s_red[2][tid] + s_red[3][tid];
@@ -295,7 +389,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(
     for (int i = 0; i < 16; ++i) {
       const int h = 8 * (i >> 2) + 4 * (l >> 5) + (i & 3);
       const float lt = fl4[i >> 2][i & 3];
-      const float val = lt > 0.f ? oacc[nb][i] / lt : 0.f;
+      const float val = lt > 0.f ? oacc[nb][i] * __builtin_amdgcn_rcpf(lt) : 0.f;
       const int64_t o = ((int64_t)row * num_heads + h0 + h) * kDV + dim;
       if constexpr (kSplit) {
         ws_o[(int64_t)split * num_rows * num_heads * kDV + o] = val;
