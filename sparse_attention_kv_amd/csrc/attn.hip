@@ -18,8 +18,8 @@
 //   * O = P V with v_mfma_f32_32x32x16_bf16 (32 heads as M); each wave owns 128 of the
 //     512 value dims; V is read with ds_read_b64_tr_b16 (LDS transpose) so no second
 //     copy of the tile is needed.
-//   * with several key splits, normalised fp32 partials + (max, sum) go to a workspace
-//     and a combine kernel merges them (log-sum-exp weights).
+//   * with several key splits, normalised bf16 partials + fp32 (max, sum) go to a
+//     workspace and a combine kernel merges them (log-sum-exp weights).
 //
 // f32 path: straightforward vector-ALU kernel (one wave per (row, head)), used for the
 // small fp32 validation shapes.
@@ -41,6 +41,15 @@ constexpr int kLoadsPerThread = kTK * kRowChunks / kThreads;  // 18
 constexpr int kPStride = kTK * 2 + 16;        // P tile row stride in bytes (padded)
 constexpr int kMaxKeysPerSplit = 2048;
 constexpr float kLn2 = 0.69314718055994530942f;
+// The next tile's 18 DMA issues per wave are split into three groups placed at the top of
+// the tile, after QK^T and before PV.
+#ifndef HS_GATHER_G0
+#define HS_GATHER_G0 9
+#endif
+#ifndef HS_GATHER_G1
+#define HS_GATHER_G1 9
+#endif
+constexpr int kG0 = HS_GATHER_G0, kG1 = HS_GATHER_G1, kG2 = kLoadsPerThread - kG0 - kG1;
 
 // LDS-only barrier: waits for this wave's LDS traffic, then s_barrier.  Outstanding
 // global loads (the next tile's direct-to-LDS gathers) are deliberately not waited for.
@@ -55,38 +64,38 @@ __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x3f70)
 __device__ __forceinline__ float fmax3(float a, float b) { return a > b ? a : b; }
 
 // Gather tile t (selected rows t*64 .. t*64+63 of the compacted list) into LDS buffer dst.
-// Physical 16-byte chunk c of the tile holds (key c/72, logical part (c%72) ^ ((key>>1)&7));
-// with a 1152-byte row stride this puts any 16 consecutive keys' chunk p in 16 distinct
-// 16-byte bank groups.
+// Physical 16-byte chunk c of the tile holds (key c/72, logical part (c%72) ^ ((key>>1)&7)).
 // Keys past n_valid re-load the last valid row; their scores are masked to -inf.
-// Wave w issues the 18 consecutive 1 KiB slots n = 18w .. 18w+17; lane l's chunk in slot
-// n is c = 64n + l, so (key, part) advance by (+0/+1, +64 mod 72) from slot to slot.
-__device__ __forceinline__ void gather_tile(const uint8_t *__restrict__ kv,
-                                            const int32_t *sidx, int n_valid, int t,
-                                            uint8_t *dst, int w, int l) {
-  const int c0 = w * kLoadsPerThread * 64 + l;
-  int key = c0 / kRowChunks;
-  int part = c0 - key * kRowChunks;
-  const int last = n_valid - 1;
+// Wave w issues the 18 consecutive 1 KiB slots n = 18w .. 18w+17 (lane l's chunk in slot
+// n is c = 64n + l).  Inside the tile loop the 18 issues are spread over three points of
+// the tile's computation so the texture-address path drains while MFMAs run.
+template <int kFirst, int kCount>
+__device__ __forceinline__ void gather_part(const uint8_t *__restrict__ kv, const int32_t *sidx,
+                                            int n_valid, int t, uint8_t *dst, int w, int l) {
   // All row-index reads first: the DMA writes LDS, so the compiler will not hoist a
   // later LDS read above an earlier DMA issue.
-  int rows[kLoadsPerThread], parts[kLoadsPerThread];
+  const int last = n_valid - 1;
+  int rows[kCount], parts[kCount];
 #pragma unroll
-  for (int i = 0; i < kLoadsPerThread; ++i) {
+  for (int i = 0; i < kCount; ++i) {
+    const int c = (w * kLoadsPerThread + kFirst + i) * 64 + l;
+    const int key = c / kRowChunks;
     const int kk = t * kTK + key;
     rows[i] = sidx[kk < last ? kk : last];
-    parts[i] = part ^ ((key >> 1) & 7);
-    part += 64;
-    const bool wrap = part >= kRowChunks;
-    part = wrap ? part - kRowChunks : part;
-    key += wrap ? 1 : 0;
+    parts[i] = (c - key * kRowChunks) ^ ((key >> 1) & 7);
   }
 #pragma unroll
-  for (int i = 0; i < kLoadsPerThread; ++i) {
+  for (int i = 0; i < kCount; ++i) {
     const uint8_t *src = kv + (int64_t)rows[i] * kRowBytes + parts[i] * 16;
-    __builtin_amdgcn_global_load_lds(src, (HS_LDS void *)(dst + (w * kLoadsPerThread + i) * 1024),
-                                     16, 0, 0);
+    __builtin_amdgcn_global_load_lds(
+        src, (HS_LDS void *)(dst + (w * kLoadsPerThread + kFirst + i) * 1024), 16, 0, 0);
   }
+}
+
+// Whole tile at once (prologue).
+__device__ __forceinline__ void gather_tile(const uint8_t *__restrict__ kv, const int32_t *sidx,
+                                            int n_valid, int t, uint8_t *dst, int w, int l) {
+  gather_part<0, kLoadsPerThread>(kv, sidx, n_valid, t, dst, w, l);
 }
 
 // Scores are kept relative to a reference max m_ref per head (log2 domain).  P is formed
@@ -101,7 +110,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(
     const __bf16 *__restrict__ q, const uint8_t *__restrict__ kv, int64_t kv_rows,
     const int32_t *__restrict__ indices, int32_t num_rows, int32_t num_heads, int32_t topk,
     int32_t keys_per_split, int32_t splits, float scale_log2, __bf16 *__restrict__ out,
-    float *__restrict__ lse, float *__restrict__ ws_o, float *__restrict__ ws_ml) {
+    float *__restrict__ lse, __bf16 *__restrict__ ws_o, float *__restrict__ ws_ml) {
   __shared__ __attribute__((aligned(16))) uint8_t s_kv0[kTileBytes];
   __shared__ __attribute__((aligned(16))) uint8_t s_kv1[kTileBytes];
   __shared__ __attribute__((aligned(16))) uint8_t s_p[kHG * kPStride];
@@ -243,7 +252,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(
       uint8_t *nxt = (t & 1) ? s_kv0 : s_kv1;
       wait_vmem();
       lds_barrier();
-      if (t + 1 < ntiles) gather_tile(kv, s_sidx, n_valid, t + 1, nxt, w, l);
+      const bool more = t + 1 < ntiles;
+      if constexpr (kG0 > 0) if (more) gather_part<0, kG0>(kv, s_sidx, n_valid, t + 1, nxt, w, l);
 
       // ---- S^T (16 keys of this wave x 32 heads), K fragments read 6 at a time ahead ----
       f32x4 sacc[2];
@@ -279,6 +289,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(
           }
         }
       }
+
+      if constexpr (kG1 > 0) if (more) gather_part<kG0, kG1>(kv, s_sidx, n_valid, t + 1, nxt, w, l);
 
       // ---- softmax numerators against the reference max ----
       const int kfirst = t * kTK + 16 * w + 4 * (l >> 4);
@@ -342,11 +354,13 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(
           *reinterpret_cast<bf16x4 *>(s_p + h * kPStride + (16 * w + 4 * (l >> 4)) * 2) = pk;
           if (w == 0 && l < 16) s_alpha[h] = alpha;
         }
+        if constexpr (kG2 > 0) if (more) gather_part<kG0 + kG1, kG2>(kv, s_sidx, n_valid, t + 1, nxt, w, l);
         renorm = true;
         break;
       }
       l_run[0] += psum[0];
       l_run[1] += psum[1];
+      if constexpr (kG2 > 0) if (more) gather_part<kG0 + kG1, kG2>(kv, s_sidx, n_valid, t + 1, nxt, w, l);
       pv_tile(cur);
     }
     if (!renorm) break;
@@ -392,7 +406,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(
       const float val = lt > 0.f ? oacc[nb][i] * __builtin_amdgcn_rcpf(lt) : 0.f;
       const int64_t o = ((int64_t)row * num_heads + h0 + h) * kDV + dim;
       if constexpr (kSplit) {
-        ws_o[(int64_t)split * num_rows * num_heads * kDV + o] = val;
+        ws_o[(int64_t)split * num_rows * num_heads * kDV + o] = (__bf16)val;
       } else {
         out[o] = (__bf16)val;
       }
@@ -411,7 +425,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(
 }
 
 // Merge key-split partials: o = sum_s w_s o_s / sum_s w_s, w_s = l_s * 2^(m_s - max m).
-__global__ __launch_bounds__(64) void attn_combine_kernel(const float *__restrict__ ws_o,
+// Partials o_s are normalised per split and stored in bf16; weights and sums stay fp32.
+__global__ __launch_bounds__(64) void attn_combine_kernel(const __bf16 *__restrict__ ws_o,
                                                           const float *__restrict__ ws_ml,
                                                           int32_t splits, int32_t num_rows,
                                                           int32_t num_heads,
@@ -429,11 +444,9 @@ __global__ __launch_bounds__(64) void attn_combine_kernel(const float *__restric
     const float lt = ws_ml[(s * plane + hi) * 2 + 1];
     const float wgt = lt > 0.f ? lt * __builtin_amdgcn_exp2f(m - M) : 0.f;
     wsum += wgt;
-    const float *src = ws_o + (s * plane + hi) * kDV + 8 * l;
-    const f32x4 a = *reinterpret_cast<const f32x4 *>(src);
-    const f32x4 b = *reinterpret_cast<const f32x4 *>(src + 4);
+    const bf16x8 v = *reinterpret_cast<const bf16x8 *>(ws_o + (s * plane + hi) * kDV + 8 * l);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) { acc[e] += wgt * a[e]; acc[4 + e] += wgt * b[e]; }
+    for (int e = 0; e < 8; ++e) acc[e] += wgt * (float)v[e];
   }
   const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
   bf16x8 o;
@@ -507,6 +520,12 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(const float *__restrict__ 
 
 }  // namespace
 
+void launch_attn_combine(const __bf16 *ws_o, const float *ws_ml, int32_t splits, int32_t num_rows,
+                         int32_t num_heads, __bf16 *out, float *lse, hipStream_t stream) {
+  hipLaunchKernelGGL(attn_combine_kernel, dim3(num_rows * num_heads), dim3(64), 0, stream, ws_o,
+                     ws_ml, splits, num_rows, num_heads, out, lse);
+}
+
 AttnPlan plan_attn_bf16(int32_t num_rows, int32_t num_heads, int32_t topk) {
   AttnPlan p;
   const int groups = num_rows * (num_heads / kHG);
@@ -518,7 +537,8 @@ AttnPlan plan_attn_bf16(int32_t num_rows, int32_t num_heads, int32_t topk) {
   splits = (topk + kps - 1) / kps;
   p.splits = splits;
   p.keys_per_split = kps;
-  p.workspace = splits > 1 ? (size_t)splits * num_rows * num_heads * (kDV + 2) * sizeof(float) : 0;
+  // bf16 partial outputs, then fp32 (max, sum) pairs
+  p.workspace = splits > 1 ? (size_t)splits * num_rows * num_heads * (kDV * 2 + 2 * sizeof(float)) : 0;
   return p;
 }
 
@@ -539,15 +559,14 @@ hipError_t launch_attn_bf16(const void *q, const void *kv, int64_t kv_rows, cons
                        scale_log2, ob, lse, nullptr, nullptr);
     return hipGetLastError();
   }
-  float *ws_o = static_cast<float *>(workspace);
-  float *ws_ml = ws_o + (size_t)plan.splits * num_rows * num_heads * kDV;
+  __bf16 *ws_o = static_cast<__bf16 *>(workspace);
+  float *ws_ml = reinterpret_cast<float *>(ws_o + (size_t)plan.splits * num_rows * num_heads * kDV);
   hipLaunchKernelGGL(attn_bf16_kernel<true>, dim3(grid), dim3(kThreads), 0, stream, qb, kvb,
                      kv_rows, indices, num_rows, num_heads, topk, plan.keys_per_split, plan.splits,
                      scale_log2, ob, lse, ws_o, ws_ml);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(attn_combine_kernel, dim3(num_rows * num_heads), dim3(64), 0, stream, ws_o,
-                     ws_ml, plan.splits, num_rows, num_heads, ob, lse);
+  launch_attn_combine(ws_o, ws_ml, plan.splits, num_rows, num_heads, ob, lse, stream);
   return hipGetLastError();
 }
 

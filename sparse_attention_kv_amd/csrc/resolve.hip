@@ -5,8 +5,10 @@
 // the request's block table (block size, physical block stride) and can also return
 // per-row valid counts.  P3 "数据 back up": block p spans rows p*block_size + offset.
 //
-// One workgroup per query row.  Consecutive lanes read consecutive int32 positions
-// (coalesced); the block-table row of the request is small (<= 8 KB) and stays in L2.
+// One 1024-thread workgroup per query row.  Consecutive lanes read consecutive int32
+// positions (coalesced); a thread's position loads, then its block-table loads, are all
+// issued before any result is used, so a row costs about two memory round trips.  The
+// block-table row of a request is small (<= 8 KB) and stays in L2.
 // Output keeps -1 in place (no compaction); the valid count is a block reduction.
 
 #include "common.h"
@@ -14,7 +16,8 @@
 namespace hs {
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 1024;
+constexpr int kPer = 4;  // entries per thread per pass; all loads of a pass are issued first
 
 __global__ __launch_bounds__(kThreads) void resolve_topk_kernel(
     const int32_t *__restrict__ topk_pos, int32_t topk, const int32_t *__restrict__ req_id,
@@ -32,21 +35,30 @@ __global__ __launch_bounds__(kThreads) void resolve_topk_kernel(
   const int32_t *bt = block_table + (int64_t)(req_ok ? b : 0) * bt_stride;
 
   int count = 0;
-  for (int j = threadIdx.x; j < topk; j += kThreads) {
-    const int t = in[j];
-    int slot = -1;
-    if (req_ok && t >= 0 && t < lim) {
-      const int page_idx = t / block_size;
-      if (page_idx < bt_stride) {
-        const int page = bt[page_idx];
-        if (page >= 0) {
-          const int64_t s = (int64_t)page * physical_block_stride + (t - page_idx * block_size);
-          slot = s < 0x7fffffffLL ? (int)s : -1;  // rows must fit int32; fail closed
-        }
-      }
+  for (int base = 0; base < topk; base += kThreads * kPer) {
+    int t[kPer], page_idx[kPer], page[kPer];
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      const int j = base + k * kThreads + threadIdx.x;
+      t[k] = j < topk ? in[j] : -1;
     }
-    out[j] = slot;
-    count += slot >= 0;
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      const bool ok = req_ok && t[k] >= 0 && t[k] < lim;
+      page_idx[k] = ok ? t[k] / block_size : bt_stride;
+      page[k] = page_idx[k] < bt_stride ? bt[page_idx[k]] : -1;
+    }
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      const int j = base + k * kThreads + threadIdx.x;
+      int slot = -1;
+      if (page[k] >= 0) {
+        const int64_t sl = (int64_t)page[k] * physical_block_stride + (t[k] - page_idx[k] * block_size);
+        slot = sl < 0x7fffffffLL ? (int)sl : -1;  // rows must fit int32; fail closed
+      }
+      if (j < topk) out[j] = slot;
+      count += slot >= 0;
+    }
   }
   if (out_valid == nullptr) return;
 #pragma unroll
