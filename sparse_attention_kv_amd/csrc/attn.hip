@@ -24,47 +24,21 @@
 // f32 path: straightforward vector-ALU kernel (one wave per (row, head)), used for the
 // small fp32 validation shapes.
 
-#include "common.h"
+#include "attn_tile.h"
 
 namespace hs {
 namespace {
 
-constexpr int kD = 576;                       // latent row width (q . k)
-constexpr int kDV = 512;                      // value width
 constexpr int kHG = 32;                       // heads per workgroup
-constexpr int kTK = 64;                       // keys per tile
-constexpr int kThreads = 256;
-constexpr int kRowBytes = kD * 2;             // 1152
-constexpr int kRowChunks = kRowBytes / 16;    // 72
-constexpr int kTileBytes = kTK * kRowBytes;   // 73728
-constexpr int kLoadsPerThread = kTK * kRowChunks / kThreads;  // 18
-constexpr int kPStride = kTK * 2 + 16;        // P tile row stride in bytes (padded)
-constexpr int kMaxKeysPerSplit = 2048;
-constexpr float kLn2 = 0.69314718055994530942f;
-// The next tile's 18 DMA issues per wave are split into three groups placed at the top of
-// the tile, after QK^T and before PV.
-#ifndef HS_GATHER_G0
-#define HS_GATHER_G0 9
-#endif
-#ifndef HS_GATHER_G1
-#define HS_GATHER_G1 9
-#endif
-constexpr int kG0 = HS_GATHER_G0, kG1 = HS_GATHER_G1, kG2 = kLoadsPerThread - kG0 - kG1;
-
-// LDS-only barrier: waits for this wave's LDS traffic, then s_barrier.  Outstanding
-// global loads (the next tile's direct-to-LDS gathers) are deliberately not waited for.
-__device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
-
-__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x3f70); }  // vmcnt(0)
-
-__device__ __forceinline__ float fmax3(float a, float b) { return a > b ? a : b; }
+constexpr int kMinGroups64 = 32;              // (row, 64-head) groups from which attn64 runs
+constexpr int kOStride = 128 * 2 + 16;        // epilogue staging: a wave's 128 dims of one head
+constexpr int kPStride = tile::kTK * 2 + 16;  // P tile row stride in bytes (padded)
+constexpr int kQSlots = kHG * tile::kRowBytes / 1024;  // 36 one-KiB DMA slots of Q per workgroup
+using namespace tile;
 
 // Gather tile t (selected rows t*64 .. t*64+63 of the compacted list) into LDS buffer dst.
-// Physical 16-byte chunk c of the tile holds (key c/72, logical part (c%72) ^ ((key>>1)&7)).
+// Layout: physical 16-byte chunk c holds (key c/72, logical part (c%72) ^ ((key>>1)&7)); the
+// XOR keeps the row-wise 16-byte reads (QK^T) and transposed 8-byte reads (PV) conflict free.
 // Keys past n_valid re-load the last valid row; their scores are masked to -inf.
 // Wave w issues the 18 consecutive 1 KiB slots n = 18w .. 18w+17 (lane l's chunk in slot
 // n is c = 64n + l).  Inside the tile loop the 18 issues are spread over three points of
@@ -87,8 +61,7 @@ __device__ __forceinline__ void gather_part(const uint8_t *__restrict__ kv, cons
 #pragma unroll
   for (int i = 0; i < kCount; ++i) {
     const uint8_t *src = kv + (int64_t)rows[i] * kRowBytes + parts[i] * 16;
-    __builtin_amdgcn_global_load_lds(
-        src, (HS_LDS void *)(dst + (w * kLoadsPerThread + kFirst + i) * 1024), 16, 0, 0);
+    dma16(src, dst + (w * kLoadsPerThread + kFirst + i) * 1024);
   }
 }
 
@@ -98,12 +71,6 @@ __device__ __forceinline__ void gather_tile(const uint8_t *__restrict__ kv, cons
   gather_part<0, kLoadsPerThread>(kv, sidx, n_valid, t, dst, w, l);
 }
 
-// Scores are kept relative to a reference max m_ref per head (log2 domain).  P is formed
-// as 2^(s - m_ref) without re-normalising O every tile; only when a score exceeds m_ref
-// by more than kRescaleSlack (P would exceed 2^kRescaleSlack) do all waves agree on a
-// new reference and rescale O and the running sum.  The arithmetic is exact for any
-// reference; the slack only bounds P (bf16) and the fp32 accumulators.
-constexpr float kRescaleSlack = 64.f;
 
 template <bool kSplit>
 __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(
@@ -147,16 +114,19 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(
     vals[k] = (k < per && j < kcnt) ? irow[j] : -1;
   }
 
-  // ---- Q (32 heads x 576) into registers as the B operand of S^T = K Q^T ----
-  bf16x8 qreg[2][kD / 32];
+  // ---- Q (32 heads x 576), one copy per workgroup, staged through the second tile buffer.
+  // Slot 18hb + ks (1 KiB) holds, at 16l, lane l's chunk of qreg[hb][ks]: head 16hb + (l&15),
+  // elements 32ks + 8(l>>4) .. +7.  The DMA overlaps the index round trip and the first
+  // gather; each wave then reads its copy with contiguous (conflict-free) 16-byte reads.
   {
-    const __bf16 *qrow = q + ((int64_t)row * num_heads + h0) * kD;
+    const uint8_t *qrow = reinterpret_cast<const uint8_t *>(q + ((int64_t)row * num_heads + h0) * kD);
 #pragma unroll
-    for (int hb = 0; hb < 2; ++hb)
-#pragma unroll
-      for (int ks = 0; ks < kD / 32; ++ks)
-        qreg[hb][ks] = *reinterpret_cast<const bf16x8 *>(qrow + (16 * hb + (l & 15)) * kD +
-                                                         32 * ks + 8 * (l >> 4));
+    for (int i = 0; i < kQSlots / kWaves; ++i) {
+      const int slot = w * (kQSlots / kWaves) + i;
+      const int hb = slot / (kD / 32), ks = slot - hb * (kD / 32);
+      const uint8_t *src = qrow + (16 * hb + (l & 15)) * kRowBytes + 64 * ks + 16 * (l >> 4);
+      dma16(src, s_kv1 + slot * 1024);
+    }
   }
 
   // ---- compact the valid indices into LDS (order preserved) ----
@@ -172,7 +142,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(
     int wave_total;
     const int ex = wave_exclusive_scan(cnt, wave_total);
     if (l == 0) s_scan[w] = wave_total;
-    __syncthreads();
+    lds_barrier();
     int base = 0, total = 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -189,6 +159,17 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(
   }
 
   const int ntiles = (n_valid + kTK - 1) / kTK;
+  if (ntiles > 0) gather_tile(kv, s_sidx, n_valid, 0, s_kv0, w, l);
+  // This thread's Q slots were issued before the tile-0 gather: wait for all but those 18.
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(kLoadsPerThread));
+  lds_barrier();
+  bf16x8 qreg[2][kD / 32];
+#pragma unroll
+  for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+    for (int ks = 0; ks < kD / 32; ++ks)
+      qreg[hb][ks] = *reinterpret_cast<const bf16x8 *>(s_kv1 + (hb * (kD / 32) + ks) * 1024 + 16 * l);
+
   float m_ref[2] = {-INFINITY, -INFINITY};
   float l_run[2] = {0.f, 0.f};
   f32x16 oacc[4];
@@ -197,10 +178,13 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(
 #pragma unroll
     for (int i = 0; i < 16; ++i) oacc[nb][i] = 0.f;
 
-  // O (32 heads x this wave's 128 dims) += P V for the tile in `cur`.  Operands of the
-  // next 16-key step (one P fragment, eight transposed V reads) are issued before the
-  // four MFMAs of the current step.
-  auto pv_tile = [&](const uint8_t *cur) {
+  // O^T (this wave's 128 dims x 32 heads) += V^T P^T for the tile in `cur`: the MFMA A
+  // operand is V^T (a lane's 8 keys at one value dim, two transposed LDS reads) and B is
+  // P^T, so a lane ends with one head (l & 31) and, per 32-dim block nb, the dims
+  // 8(i>>2) + 4(l>>5) + (i&3).  Operands of the next 16-key step are issued before the
+  // four MFMAs of the current one; dma(ks) issues this step's share of the next tile's
+  // gather so the texture path drains while the MFMAs run.
+  auto pv_tile = [&](const uint8_t *cur, auto &&dma) {
     typedef short s16x4 __attribute__((ext_vector_type(4)));
     const int g = l >> 4, j = l & 15, r = j >> 2, c = j & 3;
     const uint8_t *prow = s_p + (l & 31) * kPStride + 16 * (l >> 5);
@@ -233,14 +217,13 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(
         typedef short s16x8 __attribute__((ext_vector_type(8)));
         const s16x8 vv = {vlo[b][nb][0], vlo[b][nb][1], vlo[b][nb][2], vlo[b][nb][3],
                           vhi[b][nb][0], vhi[b][nb][1], vhi[b][nb][2], vhi[b][nb][3]};
-        oacc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa[b], __builtin_bit_cast(bf16x8, vv),
+        oacc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vv), pa[b],
                                                            oacc[nb], 0, 0, 0);
       }
+      dma(ks);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
-
-  if (ntiles > 0) gather_tile(kv, s_sidx, n_valid, 0, s_kv0, w, l);
 
   // The inner loop touches O only through MFMA; a tile whose scores need a new reference
   // (always the first one) leaves it, O is rescaled once outside, and the loop resumes.
@@ -253,7 +236,20 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(
       wait_vmem();
       lds_barrier();
       const bool more = t + 1 < ntiles;
-      if constexpr (kG0 > 0) if (more) gather_part<0, kG0>(kv, s_sidx, n_valid, t + 1, nxt, w, l);
+      // next tile's 18 DMA slots: 3 after each of the three QK batches, 2/2/2/3 in PV
+      auto qk_dma = [&](int bt) {
+        if (!more) return;
+        if (bt == 0) gather_part<0, 3>(kv, s_sidx, n_valid, t + 1, nxt, w, l);
+        if (bt == 1) gather_part<3, 3>(kv, s_sidx, n_valid, t + 1, nxt, w, l);
+        if (bt == 2) gather_part<6, 3>(kv, s_sidx, n_valid, t + 1, nxt, w, l);
+      };
+      auto pv_dma = [&](int ks) {
+        if (!more) return;
+        if (ks == 0) gather_part<9, 2>(kv, s_sidx, n_valid, t + 1, nxt, w, l);
+        if (ks == 1) gather_part<11, 2>(kv, s_sidx, n_valid, t + 1, nxt, w, l);
+        if (ks == 2) gather_part<13, 2>(kv, s_sidx, n_valid, t + 1, nxt, w, l);
+        if (ks == 3) gather_part<15, 3>(kv, s_sidx, n_valid, t + 1, nxt, w, l);
+      };
 
       // ---- S^T (16 keys of this wave x 32 heads), K fragments read 6 at a time ahead ----
       f32x4 sacc[2];
@@ -287,10 +283,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(
             sacc[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[bt & 1][j], qreg[0][ks], sacc[0], 0, 0, 0);
             sacc[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[bt & 1][j], qreg[1][ks], sacc[1], 0, 0, 0);
           }
+          qk_dma(bt);
+          __builtin_amdgcn_sched_barrier(0);
         }
       }
-
-      if constexpr (kG1 > 0) if (more) gather_part<kG0, kG1>(kv, s_sidx, n_valid, t + 1, nxt, w, l);
 
       // ---- softmax numerators against the reference max ----
       const int kfirst = t * kTK + 16 * w + 4 * (l >> 4);
@@ -303,7 +299,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           s[hb][i] = (kfirst + i < n_valid) ? sacc[hb][i] * scale_log2 : -INFINITY;
-          mw[hb] = fmax3(mw[hb], s[hb][i]);
+          mw[hb] = vmax(mw[hb], s[hb][i]);
         }
         over |= mw[hb] > m_ref[hb] + kRescaleSlack;
       }
@@ -326,8 +322,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(
       // publish this wave's per-head maxima and whether it needs a new reference
 #pragma unroll
       for (int hb = 0; hb < 2; ++hb) {
-        mw[hb] = fmax3(mw[hb], __shfl_xor(mw[hb], 16, 64));
-        mw[hb] = fmax3(mw[hb], __shfl_xor(mw[hb], 32, 64));
+        mw[hb] = vmax(mw[hb], __shfl_xor(mw[hb], 16, 64));
+        mw[hb] = vmax(mw[hb], __shfl_xor(mw[hb], 32, 64));
         if (l < 16) s_red[w][16 * hb + l] = mw[hb];
       }
       if (l == 0) s_flag[w] = any_over;
@@ -337,8 +333,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(
 #pragma unroll
         for (int hb = 0; hb < 2; ++hb) {
           const int h = 16 * hb + (l & 15);
-          const float tm = fmax3(fmax3(s_red[0][h], s_red[1][h]), fmax3(s_red[2][h], s_red[3][h]));
-          const float m_new = fmax3(m_ref[hb], tm);
+          const float tm = vmax(vmax(s_red[0][h], s_red[1][h]), vmax(s_red[2][h], s_red[3][h]));
+          const float m_new = vmax(m_ref[hb], tm);
           const bool none = m_new == -INFINITY;
           const float alpha = none ? 1.f : __builtin_amdgcn_exp2f(m_ref[hb] - m_new);
           float ps = 0.f;
@@ -354,29 +350,34 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(
           *reinterpret_cast<bf16x4 *>(s_p + h * kPStride + (16 * w + 4 * (l >> 4)) * 2) = pk;
           if (w == 0 && l < 16) s_alpha[h] = alpha;
         }
-        if constexpr (kG2 > 0) if (more) gather_part<kG0 + kG1, kG2>(kv, s_sidx, n_valid, t + 1, nxt, w, l);
         renorm = true;
         break;
       }
       l_run[0] += psum[0];
       l_run[1] += psum[1];
-      if constexpr (kG2 > 0) if (more) gather_part<kG0 + kG1, kG2>(kv, s_sidx, n_valid, t + 1, nxt, w, l);
-      pv_tile(cur);
+      pv_tile(cur, pv_dma);
     }
     if (!renorm) break;
     // ---- rare path: rescale O by alpha (O is still zero on the first tile), then PV ----
     lds_barrier();
     if (t > 0) {
-      f32x4 a4[4];
-#pragma unroll
-      for (int qd = 0; qd < 4; ++qd)
-        a4[qd] = *reinterpret_cast<const f32x4 *>(s_alpha + 8 * qd + 4 * (l >> 5));
+      const float a = s_alpha[l & 31];
 #pragma unroll
       for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) oacc[nb][i] *= a4[i >> 2][i & 3];
+        for (int i = 0; i < 16; ++i) oacc[nb][i] *= a;
     }
-    pv_tile((t & 1) ? s_kv1 : s_kv0);
+    {
+      const bool more = t + 1 < ntiles;
+      uint8_t *nxt = (t & 1) ? s_kv0 : s_kv1;
+      pv_tile((t & 1) ? s_kv1 : s_kv0, [&](int ks) {
+        if (!more) return;
+        if (ks == 0) gather_part<9, 2>(kv, s_sidx, n_valid, t + 1, nxt, w, l);
+        if (ks == 1) gather_part<11, 2>(kv, s_sidx, n_valid, t + 1, nxt, w, l);
+        if (ks == 2) gather_part<13, 2>(kv, s_sidx, n_valid, t + 1, nxt, w, l);
+        if (ks == 3) gather_part<15, 3>(kv, s_sidx, n_valid, t + 1, nxt, w, l);
+      });
+    }
     ++t;
   }
 
@@ -393,24 +394,28 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(
   if (tid < kHG) s_fl[tid] = s_red[0][tid] + s_red[1][tid] + s_red[2][tid] + s_red[3][tid];
   lds_barrier();
 
-  f32x4 fl4[4];
+  {
+    // lane: head l & 31; per block nb and group q, dims 32nb + 8q + 4(l>>5) .. +3 of this
+    // wave's 128.  Staged through LDS (tile buffer 0 is free: the barrier above follows the
+    // last tile) so each store instruction writes four whole 256-byte head slices.
+    const float lt = s_fl[l & 31];
+    const float inv = lt > 0.f ? __builtin_amdgcn_rcpf(lt) : 0.f;
+    uint8_t *stg = s_kv0 + w * kHG * kOStride;
 #pragma unroll
-  for (int qd = 0; qd < 4; ++qd) fl4[qd] = *reinterpret_cast<const f32x4 *>(s_fl + 8 * qd + 4 * (l >> 5));
+    for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
-  for (int nb = 0; nb < 4; ++nb) {
-    const int dim = 128 * w + 32 * nb + (l & 31);
+      for (int qd = 0; qd < 4; ++qd) {
+        bf16x4 v;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int h = 8 * (i >> 2) + 4 * (l >> 5) + (i & 3);
-      const float lt = fl4[i >> 2][i & 3];
-      const float val = lt > 0.f ? oacc[nb][i] * __builtin_amdgcn_rcpf(lt) : 0.f;
-      const int64_t o = ((int64_t)row * num_heads + h0 + h) * kDV + dim;
-      if constexpr (kSplit) {
-        ws_o[(int64_t)split * num_rows * num_heads * kDV + o] = (__bf16)val;
-      } else {
-        out[o] = (__bf16)val;
+        for (int e = 0; e < 4; ++e) v[e] = (__bf16)(oacc[nb][4 * qd + e] * inv);
+        *reinterpret_cast<bf16x4 *>(stg + (l & 31) * kOStride + 2 * (32 * nb + 8 * qd + 4 * (l >> 5))) = v;
       }
-    }
+    __bf16 *dst = kSplit ? ws_o + (int64_t)split * num_rows * num_heads * kDV : out;
+    dst += ((int64_t)row * num_heads + h0 + (l >> 4)) * kDV + 128 * w + 8 * (l & 15);
+#pragma unroll
+    for (int i = 0; i < kHG / 4; ++i)
+      *reinterpret_cast<i32x4 *>(dst + 4 * i * kDV) =
+          *reinterpret_cast<const i32x4 *>(stg + (4 * i + (l >> 4)) * kOStride + 16 * (l & 15));
   }
   if (tid < kHG) {
     const float m = s_fm[tid], lt = s_fl[tid];
@@ -426,27 +431,49 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(
 
 // Merge key-split partials: o = sum_s w_s o_s / sum_s w_s, w_s = l_s * 2^(m_s - max m).
 // Partials o_s are normalised per split and stored in bf16; weights and sums stay fp32.
+// Split-KV combine: one wave per (row, head); lane l owns value dims 8l..8l+7.  Splits are
+// taken eight at a time with every load of a chunk issued before any is used; the running
+// maximum moves up per chunk (weights are l_s * 2^(m_s - M)).
+constexpr int kCombineChunk = 8;
+
 __global__ __launch_bounds__(64) void attn_combine_kernel(const __bf16 *__restrict__ ws_o,
-                                                          const float *__restrict__ ws_ml,
-                                                          int32_t splits, int32_t num_rows,
-                                                          int32_t num_heads,
-                                                          __bf16 *__restrict__ out,
-                                                          float *__restrict__ lse) {
+                                                         const float *__restrict__ ws_ml,
+                                                         int32_t splits, int32_t num_rows,
+                                                         int32_t num_heads,
+                                                         __bf16 *__restrict__ out,
+                                                         float *__restrict__ lse) {
   const int64_t hi = blockIdx.x;  // row * num_heads + head
   const int l = threadIdx.x;
   const int64_t plane = (int64_t)num_rows * num_heads;
-  float M = -INFINITY;
-  for (int s = 0; s < splits; ++s) M = fmax3(M, ws_ml[(s * plane + hi) * 2]);
-  float wsum = 0.f;
+  float M = -INFINITY, wsum = 0.f;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  for (int s = 0; s < splits; ++s) {
-    const float m = ws_ml[(s * plane + hi) * 2];
-    const float lt = ws_ml[(s * plane + hi) * 2 + 1];
-    const float wgt = lt > 0.f ? lt * __builtin_amdgcn_exp2f(m - M) : 0.f;
-    wsum += wgt;
-    const bf16x8 v = *reinterpret_cast<const bf16x8 *>(ws_o + (s * plane + hi) * kDV + 8 * l);
+  for (int s0 = 0; s0 < splits; s0 += kCombineChunk) {
+    float m[kCombineChunk], lt[kCombineChunk];
+    bf16x8 v[kCombineChunk];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc[e] += wgt * (float)v[e];
+    for (int k = 0; k < kCombineChunk; ++k) {
+      const int sk = s0 + k < splits ? s0 + k : splits - 1;
+      const float2 ml = *reinterpret_cast<const float2 *>(ws_ml + (sk * plane + hi) * 2);
+      m[k] = s0 + k < splits ? ml.x : -INFINITY;
+      lt[k] = s0 + k < splits ? ml.y : 0.f;
+      v[k] = *reinterpret_cast<const bf16x8 *>(ws_o + (sk * plane + hi) * kDV + 8 * l);
+    }
+    float Mc = M;
+#pragma unroll
+    for (int k = 0; k < kCombineChunk; ++k) Mc = vmax(Mc, m[k]);
+    if (Mc == -INFINITY) continue;
+    const float r = __builtin_amdgcn_exp2f(M - Mc);  // 0 when M was -inf
+    wsum *= r;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] *= r;
+    M = Mc;
+#pragma unroll
+    for (int k = 0; k < kCombineChunk; ++k) {
+      const float wgt = lt[k] > 0.f ? lt[k] * __builtin_amdgcn_exp2f(m[k] - M) : 0.f;
+      wsum += wgt;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] += wgt * (float)v[k][e];
+    }
   }
   const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
   bf16x8 o;
@@ -492,7 +519,7 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(const float *__restrict__ 
       sc = part * scale;
     }
     if (l == 0) s_score[j] = sc;
-    m = fmax3(m, sc);
+    m = vmax(m, sc);
   }
   __syncthreads();
   float lsum = 0.f;
@@ -528,10 +555,15 @@ void launch_attn_combine(const __bf16 *ws_o, const float *ws_ml, int32_t splits,
 
 AttnPlan plan_attn_bf16(int32_t num_rows, int32_t num_heads, int32_t topk) {
   AttnPlan p;
-  const int groups = num_rows * (num_heads / kHG);
+  // 64 heads per workgroup (each gathered tile serves twice as many heads; ~1.4-1.7x the
+  // throughput from 32 rows of 128 heads up) once there are enough (row, 64-head) groups
+  // to fill the chip; the 32-head kernel has the shorter critical path for small batches.
+  p.heads_per_wg = (num_heads % 64 == 0 && num_rows * (num_heads / 64) >= kMinGroups64) ? 64 : kHG;
+  const int groups = num_rows * (num_heads / p.heads_per_wg);
+  // Enough workgroups to cover the 256 CUs once, but keep every split >= min_tiles tiles.
+  const int min_keys = (p.heads_per_wg == 64 ? 2 : 4) * kTK;
   int splits = (topk + kMaxKeysPerSplit - 1) / kMaxKeysPerSplit;
-  // Enough workgroups to cover the 256 CUs once, but keep every split >= 4 tiles.
-  while (groups * splits < 256 && (topk + 2 * splits - 1) / (2 * splits) >= 4 * kTK) splits *= 2;
+  while (groups * splits < 256 && (topk + 2 * splits - 1) / (2 * splits) >= min_keys) splits *= 2;
   int kps = (topk + splits - 1) / splits;
   kps = (kps + kTK - 1) / kTK * kTK;
   splits = (topk + kps - 1) / kps;
@@ -546,6 +578,9 @@ hipError_t launch_attn_bf16(const void *q, const void *kv, int64_t kv_rows, cons
                             int32_t num_rows, int32_t num_heads, int32_t topk, float scale,
                             void *out, float *lse, void *workspace, const AttnPlan &plan,
                             hipStream_t stream) {
+  if (plan.heads_per_wg == 64)
+    return launch_attn64(q, kv, kv_rows, indices, num_rows, num_heads, topk, scale, out, lse,
+                         workspace, plan, stream);
   const int n_hg = num_heads / kHG;
   const int units = num_rows * plan.splits;
   const int grid = (units + 7) / 8 * 8 * n_hg;

@@ -1,0 +1,73 @@
+// Shared pieces of the bf16 sparse-attention kernels (gfx950): tile geometry, the
+// direct-to-LDS gather of selected KV rows, and LDS-only synchronisation.
+//
+// A tile is 64 selected latent rows (64 x 1152 B = 72 KiB) gathered with direct-to-LDS
+// 16-byte loads; each kernel chooses the placement of the 16-byte chunks in LDS.
+#pragma once
+
+#include "common.h"
+
+namespace hs {
+namespace tile {
+
+constexpr int kD = 576;                       // latent row width (q . k)
+constexpr int kDV = 512;                      // value width
+constexpr int kTK = 64;                       // keys per tile
+constexpr int kThreads = 256;
+constexpr int kRowBytes = kD * 2;             // 1152
+constexpr int kRowChunks = kRowBytes / 16;    // 72
+constexpr int kTileBytes = kTK * kRowBytes;   // 73728
+constexpr int kLoadsPerThread = kTK * kRowChunks / kThreads;  // 18
+constexpr int kMaxKeysPerSplit = 2048;
+constexpr int kWaves = kThreads / 64;
+constexpr float kLn2 = 0.69314718055994530942f;
+
+// LDS-only barrier: waits for this wave's LDS traffic, then s_barrier.  Outstanding
+// global loads (the next tile's direct-to-LDS gathers) are deliberately not waited for:
+// an LDS release fence would make the compiler wait for them too (they write LDS), so the
+// wait and the barrier are one asm statement whose memory clobber keeps the compiler from
+// moving memory accesses across it.  Code that needs a gathered tile waits with
+// wait_vmem() first.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+// Direct-to-LDS 16-byte load: lane l's 16 bytes from src land at LDS byte lds_base + 16 l.
+// Written as inline asm so that the compiler's wait-count insertion does not treat every
+// later LDS read of either tile buffer as dependent on it (it cannot tell the buffers
+// apart and would wait for the whole in-flight prefetch).  Readers of a DMA'd buffer wait
+// explicitly (wait_vmem / vmcnt_imm) before the barrier that publishes it.  The s_nop is
+// the wait state required between an M0 write and an LDS DMA.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"  // m0 is reserved; nothing else here uses it
+__device__ __forceinline__ void dma16(const void *src, const void *lds_dst) {
+  const uint32_t base = __builtin_amdgcn_readfirstlane(
+      static_cast<uint32_t>((uintptr_t)(HS_LDS const void *)lds_dst));
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(src), "s"(base)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x3f70); }  // vmcnt(0)
+// s_waitcnt immediate for vmcnt(n), expcnt and lgkmcnt left at their maxima (gfx9 encoding:
+// vmcnt bits [3:0] and [15:14]).
+constexpr int vmcnt_imm(int n) { return ((n >> 4) & 3) << 14 | 0x3f70 | (n & 15); }
+
+// v_max_f32 (inputs here are finite or -inf)
+__device__ __forceinline__ float vmax(float a, float b) { return __builtin_fmaxf(a, b); }
+
+// Scores are kept relative to a reference max m_ref per head (log2 domain).  P is formed
+// as 2^(s - m_ref) without re-normalising O every tile; only when a score exceeds m_ref
+// by more than kRescaleSlack (P would exceed 2^kRescaleSlack) is a new reference taken
+// and O and the running sum rescaled.  The arithmetic is exact for any reference; the
+// slack only bounds P (bf16) and the fp32 accumulators.
+constexpr float kRescaleSlack = 64.f;
+
+}  // namespace tile
+
+// Split-KV combine (attn.hip): merges normalised bf16 partials with fp32 (max, sum).
+void launch_attn_combine(const __bf16 *ws_o, const float *ws_ml, int32_t splits, int32_t num_rows,
+                         int32_t num_heads, __bf16 *out, float *lse, hipStream_t stream);
+
+}  // namespace hs

@@ -35,6 +35,7 @@ hipError_t launch_swap_in(const hs_hot_state &st, const void *host_pool_dev,
                           hipStream_t stream);
 
 struct AttnPlan {
+  int heads_per_wg;    // 64 (attn64_kernel) or 32 (attn_bf16_kernel)
   int splits;          // key splits per (row, head group); 1 = no combine pass
   int keys_per_split;  // multiple of the key tile
   size_t workspace;    // bytes
@@ -45,6 +46,10 @@ hipError_t launch_attn_bf16(const void *q, const void *kv, int64_t kv_rows, cons
                             int32_t num_rows, int32_t num_heads, int32_t topk, float scale,
                             void *out, float *lse, void *workspace, const AttnPlan &plan,
                             hipStream_t stream);
+
+hipError_t launch_attn64(const void *q, const void *kv, int64_t kv_rows, const int32_t *indices,
+                         int32_t num_rows, int32_t num_heads, int32_t topk, float scale, void *out,
+                         float *lse, void *workspace, const AttnPlan &plan, hipStream_t stream);
 
 hipError_t launch_attn_f32(const float *q, const float *kv, int64_t kv_rows, const int32_t *indices,
                            int32_t num_rows, int32_t num_heads, int32_t d_qk, int32_t d_v,

@@ -97,19 +97,63 @@ def test_attn_bf16_empty_single_duplicate_and_zero_query():
 def test_attn_split_and_unsplit_agree():
     """One row alone (key-split + combine) vs the same row in a large batch (no split)."""
     import sparse_attention_kv_amd as hs
-    H, kv_rows, topk = 128, 20000, 2048
+    H, kv_rows, topk, big_rows = 128, 20000, 2048, 128
     assert hs.hs_attn_workspace_bytes(1, H, 576, 512, topk, torch.bfloat16) > 0
-    assert hs.hs_attn_workspace_bytes(64, H, 576, 512, topk, torch.bfloat16) == 0
-    q = _rand_bf16((64, H, 576), 21)
+    assert hs.hs_attn_workspace_bytes(big_rows, H, 576, 512, topk, torch.bfloat16) == 0
+    q = _rand_bf16((big_rows, H, 576), 21)
     kv = _rand_bf16((kv_rows, 576), 22)
     rng = np.random.default_rng(5)
-    idx = to_dev(np.stack([rng.choice(kv_rows, topk, replace=False) for _ in range(64)]).astype(np.int32))
+    idx = to_dev(np.stack([rng.choice(kv_rows, topk, replace=False) for _ in range(big_rows)]).astype(np.int32))
     log("attn split vs unsplit")
     big, big_lse = _attn(q, kv, idx, 1 / 24, 512)
-    for r in (0, 33, 63):
+    for r in (0, 33, 127):
         one, one_lse = _attn(q[r:r + 1].contiguous(), kv, idx[r:r + 1].contiguous(), 1 / 24, 512)
         assert_close(out_f64(one[0]), out_f64(big[r]), (1e-2, 1e-2), "split vs unsplit")
         assert_close(one_lse[0].cpu().double().numpy(), big_lse[r].cpu().double().numpy(), LSE_TOL, "lse")
+
+
+def test_attn_many_splits_with_empty_leading_splits():
+    """Long top-k on few rows: many key splits, combined in several chunks; row 0 has
+    only padding in its first 6000 entries (empty splits), row 1 keeps one valid key."""
+    import sparse_attention_kv_amd as hs
+    rows, H, kv_rows, topk = 2, 128, 30000, 8192
+    assert hs.hs_attn_workspace_bytes(rows, H, 576, 512, topk, torch.bfloat16) > 0
+    q = _rand_bf16((rows, H, 576), 31)
+    kv = _rand_bf16((kv_rows, 576), 32)
+    rng = np.random.default_rng(9)
+    idx = np.stack([rng.choice(kv_rows, topk, replace=False) for _ in range(rows)]).astype(np.int32)
+    idx[0, :6000] = -1
+    idx[1, :] = -1
+    idx[1, 5000] = 17
+    _check(q, kv, to_dev(idx), 1 / 24, 512, BF16_TOL, "many splits")
+
+
+# Shapes with >= 32 (row, 64-head) groups take the 64-head kernel; the cases above take the
+# 32-head one.  These repeat the ragged / padded / empty cases on the 64-head path.
+@pytest.mark.parametrize("topk", [1, 65, 2047, 4500])
+def test_attn_bf16_64head_path_ragged_topk(topk):
+    rows, H, kv_rows = 16, 128, 6000
+    rng = np.random.default_rng(100 + topk)
+    q = _rand_bf16((rows, H, 576), 200 + topk)
+    kv = _rand_bf16((kv_rows, 576), 300 + topk)
+    idx = np.stack([rng.choice(kv_rows, topk, replace=False) for _ in range(rows)]).astype(np.int32)
+    idx[1, rng.random(topk) < 0.3] = -1
+    idx[2, rng.random(topk) < 0.2] = kv_rows + 7
+    idx[3, :] = -1
+    if topk > 1:
+        idx[4, :] = idx[4, 0]  # one key repeated
+    _check(q, kv, to_dev(idx), 1 / 24, 512, BF16_TOL, f"64-head ragged topk={topk}")
+
+
+def test_attn_bf16_64head_path_zero_query_and_large_scores():
+    rows, H, kv_rows, topk = 32, 64, 3000, 300
+    rng = np.random.default_rng(77)
+    q = _rand_bf16((rows, H, 576), 78)
+    q[0] = 0  # uniform softmax
+    q[1] *= 8  # large scores: the reference maximum moves several times
+    kv = _rand_bf16((kv_rows, 576), 79)
+    idx = np.stack([rng.choice(kv_rows, topk, replace=False) for _ in range(rows)]).astype(np.int32)
+    _check(q, kv, to_dev(idx), 1 / 24, 512, BF16_TOL, "64-head zero query / large scores")
 
 
 def test_attn_deterministic_and_index_order_invariant():
