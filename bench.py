@@ -15,7 +15,11 @@ replayed K times is reported alongside).
 8 TB/s HBM peak, with its algorithmic bytes per launch; `cpu_baseline` = the CPU oracle
 on the host cores over the same workload.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu]
+A second object, `swap_in`, measures the swap path on the 32-request MTP workload: the
+host-link reference rate (1 GiB pinned->device copy, and a cold swap-in wave that misses
+on every row), the swap-in kernel's rate over its miss bytes, and the whole step.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-swap]
 """
 
 from __future__ import annotations
@@ -95,6 +99,117 @@ def cpu_baseline(w, s, budget_s=12.0):
                       f"x {reps} repetitions, {dt:.1f} s on {os.cpu_count()} visible host CPUs"}
 
 
+def measure_swap(dev, reps=5):
+    """Swap path on the 32-request MTP workload (4 rows per request, top-k 2048, 4096 hot
+    slots per request, 1.21 GB pinned host pool): host-link reference rate, swap-in
+    kernel rates and the whole step.  Hot state is restored from a device snapshot before
+    every repetition (not timed)."""
+    import numpy as np
+    import torch
+
+    import sparse_attention_kv_amd as hs
+    from sparse_attention_kv_amd.pipeline import DecodeStep, build_hot_state
+    from workloads import generate, spec
+
+    s = spec("mtp_swap")
+    log(f"generate {s.name} (pinned host pool)")
+    w = generate(s, pin_host_pool=True)
+
+    def d(a):
+        return torch.as_tensor(np.ascontiguousarray(a)).to(device=dev, dtype=torch.int32)
+
+    topk_pos, req_id, lim, bt, seq = (d(w.topk_pos), d(w.req_id), d(w.causal_limit),
+                                      d(w.block_table), d(w.seq_len))
+    st = build_hot_state(torch.from_numpy(w.init_pos), torch.from_numpy(w.init_stamp), seq, bt,
+                         s.block_size, w.kv_pool, dev)
+    snap = [t.clone() for t in (st.slot_loc, st.slot_stamp, st.loc_to_hot)]
+
+    def restore():
+        for t, c in zip((st.slot_loc, st.slot_stamp, st.loc_to_hot), snap):
+            t.copy_(c)
+
+    step = DecodeStep(num_reqs=s.num_reqs, rows_per_req=s.rows_per_req, topk=s.topk,
+                      num_heads=s.num_heads, d_qk=s.d_qk, d_v=s.d_v, dtype=torch.bfloat16,
+                      capacity=s.capacity, device=dev)
+    b = step.buf
+    q = w.q.to(dev)
+    row_bytes = s.d_qk * 2
+    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    main = torch.cuda.current_stream()
+    copy = step.copy_stream
+
+    # host-link reference: 1 GiB pinned -> device copy
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, pin_memory=True)
+    dst = torch.empty(n, dtype=torch.uint8, device=dev)
+    dst.copy_(src, non_blocking=True)
+    torch.cuda.synchronize()
+    e0, e1 = ev(), ev()
+    e0.record(main)
+    for _ in range(3):
+        dst.copy_(src, non_blocking=True)
+    e1.record(main)
+    torch.cuda.synchronize()
+    memcpy_gbs = 3 * n / (e0.elapsed_time(e1) / 1e3) / 1e9
+    del src, dst
+
+    # whole step: resolve + 4 waves of (swap-in on the copy stream, attention)
+    def run():
+        step.run_swap(st, topk_pos, req_id, lim, bt, s.block_size, q, s.scale, s.tick0)
+
+    times = []
+    for rep in range(reps + 2):
+        restore()
+        torch.cuda.synchronize()
+        e0.record(main)
+        run()
+        main.wait_stream(copy)
+        e1.record(main)
+        torch.cuda.synchronize()
+        if rep >= 2:
+            times.append(e0.elapsed_time(e1))
+    step_ms = float(np.median(times))
+
+    # swap-in alone, wave by wave, from the same starting state
+    restore()
+    hs.hs_resolve_topk(topk_pos, req_id, lim, bt, s.block_size, s.block_size, b.slots, b.valid)
+    torch.cuda.synchronize()
+    wave_us, wave_bytes = [], []
+    for r in range(s.rows_per_req):
+        lo, hi = r * s.num_reqs, (r + 1) * s.num_reqs
+        a, z = ev(), ev()
+        a.record(main)
+        hs.hs_swap_in(st, b.slots[lo:hi], s.tick0 + r, b.hot_idx[lo:hi], b.miss_count[r])
+        z.record(main)
+        torch.cuda.synchronize()
+        wave_us.append(a.elapsed_time(z) * 1e3)
+        wave_bytes.append(int(b.miss_count[r].sum().item()) * row_bytes)
+    warm_gbs = sum(wave_bytes) / (sum(wave_us) / 1e6) / 1e9
+
+    # cold wave: empty hot buffer, every selected row is a miss (streaming zero-copy read)
+    st.slot_loc.fill_(-1)
+    st.slot_stamp.fill_(-1)
+    st.loc_to_hot.fill_(-1)
+    a, z = ev(), ev()
+    a.record(main)
+    hs.hs_swap_in(st, b.slots[0:s.num_reqs], s.tick0, b.hot_idx[0:s.num_reqs], b.miss_count[0])
+    z.record(main)
+    torch.cuda.synchronize()
+    cold_us = a.elapsed_time(z) * 1e3
+    cold_bytes = int(b.miss_count[0].sum().item()) * row_bytes
+    cold_gbs = cold_bytes / (cold_us / 1e6) / 1e9
+    b_host = max(memcpy_gbs, cold_gbs)
+    return {
+        "workload": "MTP swap decode: 32 requests x 4 rows, seq_len 32768, top-k 2048, 4096 hot "
+                    "slots per request, reuse 0.7, 1.21 GB pinned host pool",
+        "rows_per_step": s.rows, "step_ms": step_ms, "rows_per_s": s.rows / (step_ms / 1e3),
+        "B_host_GBps": b_host, "memcpy_pinned_to_device_GBps": memcpy_gbs,
+        "swap_waves_us": wave_us, "swap_miss_bytes": wave_bytes,
+        "swap_GBps": warm_gbs, "swap_frac_of_B_host": warm_gbs / b_host,
+        "cold_wave_us": cold_us, "cold_wave_bytes": cold_bytes, "cold_wave_GBps": cold_gbs,
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -103,6 +218,7 @@ def main():
     ap.add_argument("--workload", default="resident")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--no-swap", action="store_true", help="skip the swap-path measurement")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
@@ -237,6 +353,9 @@ def main():
                      "launch_us": attn_t * 1e3,
                      "launch_us_in_graph": attn_graph_ms * 1e3 if attn_graph_ms else None},
     }
+    if not args.no_swap:
+        log("swap path")
+        res["swap_in"] = measure_swap(dev)
     if not args.no_cpu:
         log("cpu baseline (oracle)")
         res["cpu_baseline"] = cpu_baseline(w, s)
