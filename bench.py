@@ -50,24 +50,35 @@ def attn_alg_bytes(valid_per_row, heads, d_qk, d_v, topk, elem=2):
     return kv + rows * (heads * d_qk * elem + heads * d_v * elem + topk * 4)
 
 
+ATTN_SOURCES = ("attn.hip", "attn64.hip", "attn_tile.h", "common.h")
+
+
 def kernel_source_hash():
+    """Hash of the attention kernels' sources (ties stored counter figures to them)."""
     h = hashlib.sha256()
-    for f in ("attn.hip", "resolve.hip", "common.h"):
+    for f in ATTN_SOURCES:
         with open(os.path.join(ROOT, "sparse_attention_kv_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
 def stored_traffic(workload):
-    """HBM traffic per attention launch from the committed rocprofv3 counter summary,
-    if it was taken on the current kernel source; else None."""
-    path = os.path.join(ROOT, "profiles", f"attn_{workload}_counters.json")
+    """HBM bytes per attention launch from the committed rocprofv3 counter summary
+    (lines `key: value`), if it was taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", f"attn_{workload}_counters.txt")
     if not os.path.exists(path):
         return None
-    d = json.load(open(path))
-    if d.get("source_hash") != kernel_source_hash():
+    kv = {}
+    for line in open(path):
+        if ":" in line and not line.startswith((" ", "#", "|")):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("source_hash") != kernel_source_hash():
         return None
-    return d.get("traffic_bytes_per_launch")
+    try:
+        return int(kv["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def cpu_baseline(w, s, budget_s=12.0):
@@ -257,12 +268,16 @@ def main():
     def run_attn():
         hs.hs_sparse_decode_attn(q, kv, b.slots, s.scale, s.d_v, b.out, b.lse, b.workspace)
 
-    # plain device copy of known size (counter calibration for rocprofv3 --pmc runs)
+    # plain streaming kernel of known size (counter calibration for rocprofv3 --pmc runs):
+    # the 64 MiB source is written first, then a 512 MiB buffer evicts it from the L2s, so
+    # the elementwise bitwise_not reads 64 MiB from HBM and writes 64 MiB.
     calib_n = 64 << 20
     src = torch.empty(calib_n, dtype=torch.uint8, device=dev).fill_(1)
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev).fill_(2)
     dst = torch.empty_like(src)
-    dst.copy_(src)
+    torch.bitwise_not(src, out=dst)
     torch.cuda.synchronize()
+    del flush, src, dst
 
     log(f"warmup {args.warmup}")
     for _ in range(args.warmup):

@@ -91,15 +91,16 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(
 
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
   const int n_hg = num_heads / kHG;
-  // XCD-aware decode: dispatch i lands on XCD i % 8; the n_hg head groups of one
-  // (row, split) unit are consecutive dispatches on the same XCD.
-  const int xcd = blockIdx.x & 7;
-  const int k_on_xcd = blockIdx.x >> 3;
-  const int unit = (k_on_xcd / n_hg) * 8 + xcd;
-  const int hg = k_on_xcd % n_hg;
-  if (unit >= num_rows * splits) return;
-  const int row = unit / splits;
-  const int split = unit - row * splits;
+  // Dispatch i runs on XCD i % 8; XCD x takes units [x * per, (x + 1) * per).  Units are
+  // ordered (row, split, head group): the head groups of a (row, split) read the same KV
+  // rows and the splits of a row the same Q, so each is fetched from HBM once per row.
+  const int units = num_rows * splits * n_hg;
+  const int per_xcd = (units + 7) / 8;
+  const int u = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+  if (u >= units) return;
+  const int hg = u % n_hg;
+  const int split = (u / n_hg) % splits;
+  const int row = u / (n_hg * splits);
   const int h0 = hg * kHG;
   const int kbeg = split * keys_per_split;
   const int kcnt = max(0, min(keys_per_split, topk - kbeg));
@@ -582,8 +583,8 @@ hipError_t launch_attn_bf16(const void *q, const void *kv, int64_t kv_rows, cons
     return launch_attn64(q, kv, kv_rows, indices, num_rows, num_heads, topk, scale, out, lse,
                          workspace, plan, stream);
   const int n_hg = num_heads / kHG;
-  const int units = num_rows * plan.splits;
-  const int grid = (units + 7) / 8 * 8 * n_hg;
+  const int units = num_rows * plan.splits * n_hg;
+  const int grid = (units + 7) / 8 * 8;
   const float scale_log2 = scale * 1.44269504088896340736f;
   const __bf16 *qb = static_cast<const __bf16 *>(q);
   const uint8_t *kvb = static_cast<const uint8_t *>(kv);
