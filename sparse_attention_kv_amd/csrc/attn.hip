@@ -31,7 +31,10 @@ namespace {
 
 constexpr int kHG = 32;                       // heads per workgroup
 constexpr int kMinGroups64 = 32;              // (row, 64-head) groups from which attn64 runs
-constexpr int kOStride = 128 * 2 + 16;        // epilogue staging: a wave's 128 dims of one head
+constexpr int kThreads8 = 512;                // 8 waves: two per SIMD
+constexpr int kWaves8 = kThreads8 / 64;
+constexpr int kSlots8 = tile::kTK * tile::kRowChunks / kThreads8;  // 9 gather slots per wave
+constexpr int kOStride = 64 * 2 + 16;         // epilogue staging: a wave's 64 dims of one head
 constexpr int kPStride = tile::kTK * 2 + 16;  // P tile row stride in bytes (padded)
 constexpr int kQSlots = kHG * tile::kRowBytes / 1024;  // 36 one-KiB DMA slots of Q per workgroup
 using namespace tile;
@@ -39,20 +42,17 @@ using namespace tile;
 // Gather tile t (selected rows t*64 .. t*64+63 of the compacted list) into LDS buffer dst.
 // Layout: physical 16-byte chunk c holds (key c/72, logical part (c%72) ^ ((key>>1)&7)); the
 // XOR keeps the row-wise 16-byte reads (QK^T) and transposed 8-byte reads (PV) conflict free.
-// Keys past n_valid re-load the last valid row; their scores are masked to -inf.
-// Wave w issues the 18 consecutive 1 KiB slots n = 18w .. 18w+17 (lane l's chunk in slot
-// n is c = 64n + l).  Inside the tile loop the 18 issues are spread over three points of
-// the tile's computation so the texture-address path drains while MFMAs run.
+// Keys past n_valid re-load the last valid row; their scores are masked to -inf.  Wave w
+// issues the 9 one-KiB slots n = 9w .. 9w+8 (lane l's chunk in slot n is c = 64n + l).
 template <int kFirst, int kCount>
 __device__ __forceinline__ void gather_part(const uint8_t *__restrict__ kv, const int32_t *sidx,
                                             int n_valid, int t, uint8_t *dst, int w, int l) {
-  // All row-index reads first: the DMA writes LDS, so the compiler will not hoist a
-  // later LDS read above an earlier DMA issue.
+  // All row-index reads first, then the DMA issues.
   const int last = n_valid - 1;
   int rows[kCount], parts[kCount];
 #pragma unroll
   for (int i = 0; i < kCount; ++i) {
-    const int c = (w * kLoadsPerThread + kFirst + i) * 64 + l;
+    const int c = (w * kSlots8 + kFirst + i) * 64 + l;
     const int key = c / kRowChunks;
     const int kk = t * kTK + key;
     rows[i] = sidx[kk < last ? kk : last];
@@ -61,19 +61,12 @@ __device__ __forceinline__ void gather_part(const uint8_t *__restrict__ kv, cons
 #pragma unroll
   for (int i = 0; i < kCount; ++i) {
     const uint8_t *src = kv + (int64_t)rows[i] * kRowBytes + parts[i] * 16;
-    dma16(src, dst + (w * kLoadsPerThread + kFirst + i) * 1024);
+    dma16(src, dst + (w * kSlots8 + kFirst + i) * 1024);
   }
 }
 
-// Whole tile at once (prologue).
-__device__ __forceinline__ void gather_tile(const uint8_t *__restrict__ kv, const int32_t *sidx,
-                                            int n_valid, int t, uint8_t *dst, int w, int l) {
-  gather_part<0, kLoadsPerThread>(kv, sidx, n_valid, t, dst, w, l);
-}
-
-
 template <bool kSplit>
-__global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(
+__global__ __launch_bounds__(kThreads8, 1) void attn_bf16_kernel(
     const __bf16 *__restrict__ q, const uint8_t *__restrict__ kv, int64_t kv_rows,
     const int32_t *__restrict__ indices, int32_t num_rows, int32_t num_heads, int32_t topk,
     int32_t keys_per_split, int32_t splits, float scale_log2, __bf16 *__restrict__ out,
@@ -86,10 +79,12 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(
   __shared__ __attribute__((aligned(16))) float s_alpha[kHG];
   __shared__ __attribute__((aligned(16))) float s_fm[kHG];
   __shared__ __attribute__((aligned(16))) float s_fl[kHG];
-  __shared__ int s_scan[8];
-  __shared__ int s_flag[4];
+  __shared__ int s_scan[kWaves8];
+  __shared__ int s_flag[kWaves8];
 
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+  const int kq = w & 3;   // QK^T: this wave's 16 keys of the tile
+  const int hh = w >> 2;  // QK^T: this wave's 16 heads of the 32
   const int n_hg = num_heads / kHG;
   // Dispatch i runs on XCD i % 8; XCD x takes units [x * per, (x + 1) * per).  Units are
   // ordered (row, split, head group): the head groups of a (row, split) read the same KV
@@ -107,26 +102,27 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(
 
   // ---- indices of this split (issued first: they gate the first KV gather) ----
   const int32_t *irow = indices + (int64_t)row * topk + kbeg;
-  const int per = (kcnt + kThreads - 1) / kThreads;  // <= 8
-  int vals[kMaxKeysPerSplit / kThreads];
+  const int per = (kcnt + kThreads8 - 1) / kThreads8;  // <= 4
+  int vals[kMaxKeysPerSplit / kThreads8];
 #pragma unroll
-  for (int k = 0; k < kMaxKeysPerSplit / kThreads; ++k) {
+  for (int k = 0; k < kMaxKeysPerSplit / kThreads8; ++k) {
     const int j = tid * per + k;
     vals[k] = (k < per && j < kcnt) ? irow[j] : -1;
   }
 
   // ---- Q (32 heads x 576), one copy per workgroup, staged through the second tile buffer.
-  // Slot 18hb + ks (1 KiB) holds, at 16l, lane l's chunk of qreg[hb][ks]: head 16hb + (l&15),
-  // elements 32ks + 8(l>>4) .. +7.  The DMA overlaps the index round trip and the first
-  // gather; each wave then reads its copy with contiguous (conflict-free) 16-byte reads.
+  // Slot 18hb + ks (1 KiB) holds, at 16l, lane l's chunk of the B operand for head block hb:
+  // head 16hb + (l&15), elements 32ks + 8(l>>4) .. +7.  Wave w issues slots w, w+8, ...
   {
     const uint8_t *qrow = reinterpret_cast<const uint8_t *>(q + ((int64_t)row * num_heads + h0) * kD);
 #pragma unroll
-    for (int i = 0; i < kQSlots / kWaves; ++i) {
-      const int slot = w * (kQSlots / kWaves) + i;
-      const int hb = slot / (kD / 32), ks = slot - hb * (kD / 32);
-      const uint8_t *src = qrow + (16 * hb + (l & 15)) * kRowBytes + 64 * ks + 16 * (l >> 4);
-      dma16(src, s_kv1 + slot * 1024);
+    for (int i = 0; i < (kQSlots + kWaves8 - 1) / kWaves8; ++i) {
+      const int slot = w + kWaves8 * i;
+      if (slot < kQSlots) {
+        const int hb = slot / (kD / 32), ks = slot - hb * (kD / 32);
+        const uint8_t *src = qrow + (16 * hb + (l & 15)) * kRowBytes + 64 * ks + 16 * (l >> 4);
+        dma16(src, s_kv1 + slot * 1024);
+      }
     }
   }
 
@@ -135,7 +131,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(
   {
     int cnt = 0;
 #pragma unroll
-    for (int k = 0; k < kMaxKeysPerSplit / kThreads; ++k) {
+    for (int k = 0; k < kMaxKeysPerSplit / kThreads8; ++k) {
       const bool ok = vals[k] >= 0 && vals[k] < kv_rows;
       vals[k] = ok ? vals[k] : -1;
       cnt += ok;
@@ -146,60 +142,57 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(
     lds_barrier();
     int base = 0, total = 0;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < kWaves8; ++i) {
       const int c = s_scan[i];
       base += i < w ? c : 0;
       total += c;
     }
     int pos = base + ex;
 #pragma unroll
-    for (int k = 0; k < kMaxKeysPerSplit / kThreads; ++k)
+    for (int k = 0; k < kMaxKeysPerSplit / kThreads8; ++k)
       if (vals[k] >= 0) s_sidx[pos++] = vals[k];
     n_valid = total;
     lds_barrier();
   }
 
   const int ntiles = (n_valid + kTK - 1) / kTK;
-  if (ntiles > 0) gather_tile(kv, s_sidx, n_valid, 0, s_kv0, w, l);
-  // This thread's Q slots were issued before the tile-0 gather: wait for all but those 18.
-  __builtin_amdgcn_s_waitcnt(vmcnt_imm(kLoadsPerThread));
+  if (ntiles > 0) gather_part<0, kSlots8>(kv, s_sidx, n_valid, 0, s_kv0, w, l);
+  // This thread's Q slots were issued before the tile-0 gather: wait for all but those 9.
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(kSlots8));
   lds_barrier();
-  bf16x8 qreg[2][kD / 32];
+  bf16x8 qreg[kD / 32];  // B operand of this wave's head block
 #pragma unroll
-  for (int hb = 0; hb < 2; ++hb)
-#pragma unroll
-    for (int ks = 0; ks < kD / 32; ++ks)
-      qreg[hb][ks] = *reinterpret_cast<const bf16x8 *>(s_kv1 + (hb * (kD / 32) + ks) * 1024 + 16 * l);
+  for (int ks = 0; ks < kD / 32; ++ks)
+    qreg[ks] = *reinterpret_cast<const bf16x8 *>(s_kv1 + (hh * (kD / 32) + ks) * 1024 + 16 * l);
 
-  float m_ref[2] = {-INFINITY, -INFINITY};
-  float l_run[2] = {0.f, 0.f};
-  f32x16 oacc[4];
+  float m_ref = -INFINITY;  // reference max of head 16hh + (l & 15) (log2 domain)
+  float l_run = 0.f;        // this lane's share of that head's softmax sum
+  f32x16 oacc[2];           // O^T: this wave's 64 value dims (2 blocks of 32) x 32 heads
 #pragma unroll
-  for (int nb = 0; nb < 4; ++nb)
+  for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
     for (int i = 0; i < 16; ++i) oacc[nb][i] = 0.f;
 
-  // O^T (this wave's 128 dims x 32 heads) += V^T P^T for the tile in `cur`: the MFMA A
+  // O^T (this wave's 64 dims x 32 heads) += V^T P^T for the tile in `cur`: the MFMA A
   // operand is V^T (a lane's 8 keys at one value dim, two transposed LDS reads) and B is
   // P^T, so a lane ends with one head (l & 31) and, per 32-dim block nb, the dims
   // 8(i>>2) + 4(l>>5) + (i&3).  Operands of the next 16-key step are issued before the
-  // four MFMAs of the current one; dma(ks) issues this step's share of the next tile's
-  // gather so the texture path drains while the MFMAs run.
-  auto pv_tile = [&](const uint8_t *cur, auto &&dma) {
+  // MFMAs of the current one.
+  auto pv_tile = [&](const uint8_t *cur) {
     typedef short s16x4 __attribute__((ext_vector_type(4)));
     const int g = l >> 4, j = l & 15, r = j >> 2, c = j & 3;
     const uint8_t *prow = s_p + (l & 31) * kPStride + 16 * (l >> 5);
-    int voff[4];
+    int voff[2];
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb) voff[nb] = 128 * w + 32 * nb + 16 * (g & 1) + 4 * c;
+    for (int nb = 0; nb < 2; ++nb) voff[nb] = 64 * w + 32 * nb + 16 * (g & 1) + 4 * c;
     bf16x8 pa[2];
-    s16x4 vlo[2][4], vhi[2][4];
+    s16x4 vlo[2][2], vhi[2][2];
     auto load_step = [&](int ks, int buf) {
       pa[buf] = *reinterpret_cast<const bf16x8 *>(prow + 32 * ks);
       const int key0 = 16 * ks + 8 * (g >> 1) + r;
       const int key1 = key0 + 4;
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb) {
+      for (int nb = 0; nb < 2; ++nb) {
         const int part = voff[nb] >> 3, off = (voff[nb] & 7) * 2;
         vlo[buf][nb] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
             (HS_LDS s16x4 *)(cur + key0 * kRowBytes + ((part ^ ((key0 >> 1) & 7)) << 4) + off));
@@ -214,14 +207,13 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(
       __builtin_amdgcn_sched_barrier(0);
       const int b = ks & 1;
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb) {
+      for (int nb = 0; nb < 2; ++nb) {
         typedef short s16x8 __attribute__((ext_vector_type(8)));
         const s16x8 vv = {vlo[b][nb][0], vlo[b][nb][1], vlo[b][nb][2], vlo[b][nb][3],
                           vhi[b][nb][0], vhi[b][nb][1], vhi[b][nb][2], vhi[b][nb][3]};
         oacc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vv), pa[b],
                                                            oacc[nb], 0, 0, 0);
       }
-      dma(ks);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
@@ -237,29 +229,14 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(
       wait_vmem();
       lds_barrier();
       const bool more = t + 1 < ntiles;
-      // next tile's 18 DMA slots: 3 after each of the three QK batches, 2/2/2/3 in PV
-      auto qk_dma = [&](int bt) {
-        if (!more) return;
-        if (bt == 0) gather_part<0, 3>(kv, s_sidx, n_valid, t + 1, nxt, w, l);
-        if (bt == 1) gather_part<3, 3>(kv, s_sidx, n_valid, t + 1, nxt, w, l);
-        if (bt == 2) gather_part<6, 3>(kv, s_sidx, n_valid, t + 1, nxt, w, l);
-      };
-      auto pv_dma = [&](int ks) {
-        if (!more) return;
-        if (ks == 0) gather_part<9, 2>(kv, s_sidx, n_valid, t + 1, nxt, w, l);
-        if (ks == 1) gather_part<11, 2>(kv, s_sidx, n_valid, t + 1, nxt, w, l);
-        if (ks == 2) gather_part<13, 2>(kv, s_sidx, n_valid, t + 1, nxt, w, l);
-        if (ks == 3) gather_part<15, 3>(kv, s_sidx, n_valid, t + 1, nxt, w, l);
-      };
 
-      // ---- S^T (16 keys of this wave x 32 heads), K fragments read 6 at a time ahead ----
-      f32x4 sacc[2];
+      // ---- S^T (this wave's 16 keys x 16 heads), K fragments read 6 at a time ahead; the
+      // next tile's 9 DMA slots go out 3 after each batch of 6 MFMAs ----
+      f32x4 sacc;
 #pragma unroll
-      for (int hb = 0; hb < 2; ++hb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) sacc[hb][i] = 0.f;
+      for (int i = 0; i < 4; ++i) sacc[i] = 0.f;
       {
-        const int key = 16 * w + (l & 15);
+        const int key = 16 * kq + (l & 15);
         const uint8_t *krow = cur + key * kRowBytes;
         const int sw = (key >> 1) & 7;
         constexpr int kB = 6;
@@ -279,84 +256,72 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(
           }
           __builtin_amdgcn_sched_barrier(0);  // keep the next batch's reads ahead of these MFMAs
 #pragma unroll
-          for (int j = 0; j < kB; ++j) {
-            const int ks = bt * kB + j;
-            sacc[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[bt & 1][j], qreg[0][ks], sacc[0], 0, 0, 0);
-            sacc[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[bt & 1][j], qreg[1][ks], sacc[1], 0, 0, 0);
+          for (int j = 0; j < kB; ++j)
+            sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[bt & 1][j], qreg[bt * kB + j], sacc, 0, 0, 0);
+          if (more) {
+            if (bt == 0) gather_part<0, 3>(kv, s_sidx, n_valid, t + 1, nxt, w, l);
+            if (bt == 1) gather_part<3, 3>(kv, s_sidx, n_valid, t + 1, nxt, w, l);
+            if (bt == 2) gather_part<6, 3>(kv, s_sidx, n_valid, t + 1, nxt, w, l);
           }
-          qk_dma(bt);
           __builtin_amdgcn_sched_barrier(0);
         }
       }
 
-      // ---- softmax numerators against the reference max ----
-      const int kfirst = t * kTK + 16 * w + 4 * (l >> 4);
-      float s[2][4];
-      float mw[2];
-      bool over = false;
+      // ---- softmax numerators against the reference max (head 16hh + (l&15), keys
+      // 16kq + 4(l>>4) + i of the tile) ----
+      const int h = 16 * hh + (l & 15);
+      const int kfirst = t * kTK + 16 * kq + 4 * (l >> 4);
+      float s[4];
+      float mw = -INFINITY;
 #pragma unroll
-      for (int hb = 0; hb < 2; ++hb) {
-        mw[hb] = -INFINITY;
+      for (int i = 0; i < 4; ++i) {
+        s[i] = (kfirst + i < n_valid) ? sacc[i] * scale_log2 : -INFINITY;
+        mw = vmax(mw, s[i]);
+      }
+      const bool any_over = __builtin_amdgcn_ballot_w64(mw > m_ref + kRescaleSlack) != 0;
+      float psum = 0.f;
+      if (!any_over) {
+        bf16x4 pk;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          s[hb][i] = (kfirst + i < n_valid) ? sacc[hb][i] * scale_log2 : -INFINITY;
-          mw[hb] = vmax(mw[hb], s[hb][i]);
+          const float p = __builtin_amdgcn_exp2f(s[i] - m_ref);
+          psum += p;
+          pk[i] = (__bf16)p;
         }
-        over |= mw[hb] > m_ref[hb] + kRescaleSlack;
-      }
-      const bool any_over = __builtin_amdgcn_ballot_w64(over) != 0;
-      float psum[2] = {0.f, 0.f};
-      if (!any_over) {
-#pragma unroll
-        for (int hb = 0; hb < 2; ++hb) {
-          const int h = 16 * hb + (l & 15);
-          bf16x4 pk;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float p = __builtin_amdgcn_exp2f(s[hb][i] - m_ref[hb]);
-            psum[hb] += p;
-            pk[i] = (__bf16)p;
-          }
-          *reinterpret_cast<bf16x4 *>(s_p + h * kPStride + (16 * w + 4 * (l >> 4)) * 2) = pk;
-        }
+        *reinterpret_cast<bf16x4 *>(s_p + h * kPStride + (16 * kq + 4 * (l >> 4)) * 2) = pk;
       }
       // publish this wave's per-head maxima and whether it needs a new reference
-#pragma unroll
-      for (int hb = 0; hb < 2; ++hb) {
-        mw[hb] = vmax(mw[hb], __shfl_xor(mw[hb], 16, 64));
-        mw[hb] = vmax(mw[hb], __shfl_xor(mw[hb], 32, 64));
-        if (l < 16) s_red[w][16 * hb + l] = mw[hb];
-      }
+      mw = vmax(mw, __shfl_xor(mw, 16, 64));
+      mw = vmax(mw, __shfl_xor(mw, 32, 64));
+      if (l < 16) s_red[kq][h] = mw;
       if (l == 0) s_flag[w] = any_over;
       lds_barrier();
-      if (s_flag[0] | s_flag[1] | s_flag[2] | s_flag[3]) {
-        // new reference from all waves' maxima; running sums rescaled, P redone
+      int flags = 0;
 #pragma unroll
-        for (int hb = 0; hb < 2; ++hb) {
-          const int h = 16 * hb + (l & 15);
-          const float tm = vmax(vmax(s_red[0][h], s_red[1][h]), vmax(s_red[2][h], s_red[3][h]));
-          const float m_new = vmax(m_ref[hb], tm);
-          const bool none = m_new == -INFINITY;
-          const float alpha = none ? 1.f : __builtin_amdgcn_exp2f(m_ref[hb] - m_new);
-          float ps = 0.f;
-          bf16x4 pk;
+      for (int i = 0; i < kWaves8; ++i) flags |= s_flag[i];
+      if (flags) {
+        // new reference from all key quarters' maxima; running sum rescaled, P redone
+        const float tm = vmax(vmax(s_red[0][h], s_red[1][h]), vmax(s_red[2][h], s_red[3][h]));
+        const float m_new = vmax(m_ref, tm);
+        const bool none = m_new == -INFINITY;
+        const float alpha = none ? 1.f : __builtin_amdgcn_exp2f(m_ref - m_new);
+        float ps = 0.f;
+        bf16x4 pk;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float p = none ? 0.f : __builtin_amdgcn_exp2f(s[hb][i] - m_new);
-            ps += p;
-            pk[i] = (__bf16)p;
-          }
-          l_run[hb] = l_run[hb] * alpha + ps;
-          m_ref[hb] = m_new;
-          *reinterpret_cast<bf16x4 *>(s_p + h * kPStride + (16 * w + 4 * (l >> 4)) * 2) = pk;
-          if (w == 0 && l < 16) s_alpha[h] = alpha;
+        for (int i = 0; i < 4; ++i) {
+          const float p = none ? 0.f : __builtin_amdgcn_exp2f(s[i] - m_new);
+          ps += p;
+          pk[i] = (__bf16)p;
         }
+        l_run = l_run * alpha + ps;
+        m_ref = m_new;
+        *reinterpret_cast<bf16x4 *>(s_p + h * kPStride + (16 * kq + 4 * (l >> 4)) * 2) = pk;
+        if (kq == 0 && l < 16) s_alpha[h] = alpha;
         renorm = true;
         break;
       }
-      l_run[0] += psum[0];
-      l_run[1] += psum[1];
-      pv_tile(cur, pv_dma);
+      l_run += psum;
+      pv_tile(cur);
     }
     if (!renorm) break;
     // ---- rare path: rescale O by alpha (O is still zero on the first tile), then PV ----
@@ -364,32 +329,22 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(
     if (t > 0) {
       const float a = s_alpha[l & 31];
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb)
+      for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) oacc[nb][i] *= a;
     }
-    {
-      const bool more = t + 1 < ntiles;
-      uint8_t *nxt = (t & 1) ? s_kv0 : s_kv1;
-      pv_tile((t & 1) ? s_kv1 : s_kv0, [&](int ks) {
-        if (!more) return;
-        if (ks == 0) gather_part<9, 2>(kv, s_sidx, n_valid, t + 1, nxt, w, l);
-        if (ks == 1) gather_part<11, 2>(kv, s_sidx, n_valid, t + 1, nxt, w, l);
-        if (ks == 2) gather_part<13, 2>(kv, s_sidx, n_valid, t + 1, nxt, w, l);
-        if (ks == 3) gather_part<15, 3>(kv, s_sidx, n_valid, t + 1, nxt, w, l);
-      });
-    }
+    pv_tile((t & 1) ? s_kv1 : s_kv0);
     ++t;
   }
 
   // ---- epilogue: total softmax sums, normalise, write ----
-#pragma unroll
-  for (int hb = 0; hb < 2; ++hb) {
-    float lr = l_run[hb];
+  {
+    float lr = l_run;
     lr += __shfl_xor(lr, 16, 64);
     lr += __shfl_xor(lr, 32, 64);
-    if (l < 16) s_red[w][16 * hb + l] = lr;
-    if (w == 0 && l < 16) s_fm[16 * hb + l] = m_ref[hb];
+    const int h = 16 * hh + (l & 15);
+    if (l < 16) s_red[kq][h] = lr;
+    if (kq == 0 && l < 16) s_fm[h] = m_ref;
   }
   lds_barrier();
   if (tid < kHG) s_fl[tid] = s_red[0][tid] + s_red[1][tid] + s_red[2][tid] + s_red[3][tid];
@@ -397,13 +352,13 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(
 
   {
     // lane: head l & 31; per block nb and group q, dims 32nb + 8q + 4(l>>5) .. +3 of this
-    // wave's 128.  Staged through LDS (tile buffer 0 is free: the barrier above follows the
-    // last tile) so each store instruction writes four whole 256-byte head slices.
+    // wave's 64.  Staged through LDS (tile buffer 0 is free: the barriers above follow the
+    // last tile) so each store instruction writes eight whole 128-byte head slices.
     const float lt = s_fl[l & 31];
     const float inv = lt > 0.f ? __builtin_amdgcn_rcpf(lt) : 0.f;
     uint8_t *stg = s_kv0 + w * kHG * kOStride;
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb)
+    for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
       for (int qd = 0; qd < 4; ++qd) {
         bf16x4 v;
@@ -412,11 +367,11 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(
         *reinterpret_cast<bf16x4 *>(stg + (l & 31) * kOStride + 2 * (32 * nb + 8 * qd + 4 * (l >> 5))) = v;
       }
     __bf16 *dst = kSplit ? ws_o + (int64_t)split * num_rows * num_heads * kDV : out;
-    dst += ((int64_t)row * num_heads + h0 + (l >> 4)) * kDV + 128 * w + 8 * (l & 15);
+    dst += ((int64_t)row * num_heads + h0 + (l >> 3)) * kDV + 64 * w + 8 * (l & 7);
 #pragma unroll
-    for (int i = 0; i < kHG / 4; ++i)
-      *reinterpret_cast<i32x4 *>(dst + 4 * i * kDV) =
-          *reinterpret_cast<const i32x4 *>(stg + (4 * i + (l >> 4)) * kOStride + 16 * (l & 15));
+    for (int i = 0; i < kHG / 8; ++i)
+      *reinterpret_cast<i32x4 *>(dst + 8 * i * kDV) =
+          *reinterpret_cast<const i32x4 *>(stg + (8 * i + (l >> 3)) * kOStride + 16 * (l & 7));
   }
   if (tid < kHG) {
     const float m = s_fm[tid], lt = s_fl[tid];
@@ -590,14 +545,14 @@ hipError_t launch_attn_bf16(const void *q, const void *kv, int64_t kv_rows, cons
   const uint8_t *kvb = static_cast<const uint8_t *>(kv);
   __bf16 *ob = static_cast<__bf16 *>(out);
   if (plan.splits == 1) {
-    hipLaunchKernelGGL(attn_bf16_kernel<false>, dim3(grid), dim3(kThreads), 0, stream, qb, kvb,
+    hipLaunchKernelGGL(attn_bf16_kernel<false>, dim3(grid), dim3(kThreads8), 0, stream, qb, kvb,
                        kv_rows, indices, num_rows, num_heads, topk, plan.keys_per_split, 1,
                        scale_log2, ob, lse, nullptr, nullptr);
     return hipGetLastError();
   }
   __bf16 *ws_o = static_cast<__bf16 *>(workspace);
   float *ws_ml = reinterpret_cast<float *>(ws_o + (size_t)plan.splits * num_rows * num_heads * kDV);
-  hipLaunchKernelGGL(attn_bf16_kernel<true>, dim3(grid), dim3(kThreads), 0, stream, qb, kvb,
+  hipLaunchKernelGGL(attn_bf16_kernel<true>, dim3(grid), dim3(kThreads8), 0, stream, qb, kvb,
                      kv_rows, indices, num_rows, num_heads, topk, plan.keys_per_split, plan.splits,
                      scale_log2, ob, lse, ws_o, ws_ml);
   hipError_t e = hipGetLastError();
