@@ -11,8 +11,8 @@ timed region.
 Prints ONE JSON line.  `value` = query rows/s of the whole step: K steps launched back to
 back on one stream, bracketed by device synchronisation (a captured HIP graph of the step
 replayed K times is reported alongside).
-`roofline` = the attention op (every dispatch of hs_sparse_decode_attn) against the
-8 TB/s HBM peak, with its algorithmic bytes per launch; `cpu_baseline` = the CPU oracle
+`roofline` = that attention op (its dispatches) against the 8 TB/s HBM peak, with its
+algorithmic bytes per launch; `cpu_baseline` = the CPU oracle
 on the host cores over the same workload.
 
 A second object, `swap_in`, measures the swap path on the 32-request MTP workload: the
@@ -263,10 +263,11 @@ def main():
     b = step.buf
 
     def run_step():
-        step.run_resident(topk_pos, req_id, lim, bt, s.block_size, q, kv, s.scale)
+        # resolve + attention in one call: positions are resolved in the attention prologue
+        step.run_resident_fused(topk_pos, req_id, lim, bt, s.block_size, q, kv, s.scale)
 
-    def run_attn():
-        hs.hs_sparse_decode_attn(q, kv, b.slots, s.scale, s.d_v, b.out, b.lse, b.workspace)
+    def run_step_two_calls():
+        step.run_resident(topk_pos, req_id, lim, bt, s.block_size, q, kv, s.scale)
 
     # plain streaming kernel of known size (counter calibration for rocprofv3 --pmc runs):
     # the 64 MiB source is written first, then a 512 MiB buffer evicts it from the L2s, so
@@ -280,6 +281,7 @@ def main():
     del flush, src, dst
 
     log(f"warmup {args.warmup}")
+    run_step_two_calls()  # fills b.valid (per-row valid counts) for the algorithmic bytes
     for _ in range(args.warmup):
         run_step()
     torch.cuda.synchronize()
@@ -297,16 +299,17 @@ def main():
     torch.cuda.synchronize()
     eager_ms = e0.elapsed_time(e1) / args.steps
 
-    # attention op alone: K launches back to back on the stream, bracketed by events
+    # the same step as two calls (hs_resolve_topk, then hs_sparse_decode_attn), for reference
+    for _ in range(args.warmup):
+        run_step_two_calls()
     e0.record(stream)
     for _ in range(args.steps):
-        run_attn()
+        run_step_two_calls()
     e1.record(stream)
     torch.cuda.synchronize()
-    attn_ms = e0.elapsed_time(e1) / args.steps
+    two_call_ms = e0.elapsed_time(e1) / args.steps
 
     graph_ms = None
-    attn_graph_ms = None
     if not args.no_graph:
         g = torch.cuda.CUDAGraph()
         cap = torch.cuda.Stream()
@@ -328,24 +331,10 @@ def main():
         torch.cuda.synchronize()
         graph_ms = e0.elapsed_time(e1) / args.steps
         assert torch.equal(b.out, ref_out), "graph replay differs from eager result"
-        # attention op alone in a graph of 20 back-to-back launches
-        ga = torch.cuda.CUDAGraph()
-        with torch.cuda.stream(cap):
-            with torch.cuda.graph(ga, stream=cap):
-                for _ in range(20):
-                    run_attn()
-        torch.cuda.synchronize()
-        reps = max(1, args.steps // 20)
-        e0.record(stream)
-        for _ in range(reps):
-            ga.replay()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        attn_graph_ms = e0.elapsed_time(e1) / (reps * 20)
 
     ms = eager_ms
     value = s.rows / (ms / 1e3)
-    attn_t = attn_ms
+    attn_t = eager_ms  # the step is one attention op (its attention + combine dispatches)
     achieved = alg / (attn_t / 1e3) / 1e9
     traffic = stored_traffic(args.workload)
     plan_ws = hs.hs_attn_workspace_bytes(s.rows, s.num_heads, s.d_qk, s.d_v, s.topk, torch.bfloat16)
@@ -359,14 +348,15 @@ def main():
                    "rows_per_step": s.rows, "topk": s.topk, "heads": s.num_heads,
                    "timing": "K eager steps on one stream between synchronisations",
                    "eager_ms_per_step": eager_ms, "graph_ms_per_step": graph_ms,
+                   "two_call_ms_per_step": two_call_ms,
                    "attn_split_workspace_bytes": plan_ws},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS,
                      "traffic": traffic,
-                     "kernel": "hs_sparse_decode_attn (split-KV attention + combine dispatches)",
+                     "kernel": "hs_sparse_decode_attn_paged (attention with position "
+                               "resolution + split combine dispatches)",
                      "alg_bytes_per_launch": alg,
-                     "launch_us": attn_t * 1e3,
-                     "launch_us_in_graph": attn_graph_ms * 1e3 if attn_graph_ms else None},
+                     "launch_us": attn_t * 1e3},
     }
     if not args.no_swap:
         log("swap path")

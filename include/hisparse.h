@@ -174,7 +174,37 @@ hs_status hs_sparse_decode_attn(const void *q, const void *kv, int64_t kv_rows,
                                 int32_t dtype, void *out, float *lse, void *workspace,
                                 size_t workspace_bytes, void *stream);
 
-/* Device workspace hs_sparse_decode_attn needs for these sizes (0 when none). */
+/*
+ * hs_sparse_decode_attn_paged -- the fully resident batch in one call: P3 resolve_topk
+ * listing (when every request's KV is resident, the top-k positions are converted to
+ * cache rows through the block table and attention reads the paged cache directly).
+ * Computes exactly hs_resolve_topk(topk_pos, ..., out_slots) followed by
+ * hs_sparse_decode_attn(q, kv_pool, kv_rows, out_slots, ...), without writing the rows:
+ * position t of row i (request req_id[i]) selects pool row
+ * block_table[b, t / block_size] * physical_block_stride + t % block_size when
+ * 0 <= t < causal_limit[i] and that table entry is >= 0; other entries select nothing.
+ *
+ *   q, out, lse, workspace  as for hs_sparse_decode_attn (same workspace size)
+ *   kv_pool      [kv_rows, d_qk] of dtype, the paged device cache
+ *   topk_pos, req_id, causal_limit, block_table, bt_stride, block_size,
+ *   physical_block_stride, num_reqs   as for hs_resolve_topk
+ *
+ * Supported: dtype HS_BF16, d_qk = 576, d_v = 512, num_heads a multiple of 32 (other
+ * shapes: resolve, then hs_sparse_decode_attn).  Valid counts are not produced; use
+ * hs_resolve_topk where they are needed.
+ * Errors: as hs_resolve_topk and hs_sparse_decode_attn; HS_ERR_UNSUPPORTED for other shapes.
+ */
+hs_status hs_sparse_decode_attn_paged(const void *q, const void *kv_pool, int64_t kv_rows,
+                                      const int32_t *topk_pos, const int32_t *req_id,
+                                      const int32_t *causal_limit, int32_t num_reqs,
+                                      const int32_t *block_table, int32_t bt_stride,
+                                      int32_t block_size, int32_t physical_block_stride,
+                                      int32_t num_rows, int32_t num_heads, int32_t d_qk,
+                                      int32_t d_v, int32_t topk, float scale, int32_t dtype,
+                                      void *out, float *lse, void *workspace,
+                                      size_t workspace_bytes, void *stream);
+
+/* Device workspace hs_sparse_decode_attn(_paged) needs for these sizes (0 when none). */
 size_t hs_attn_workspace_bytes(int32_t num_rows, int32_t num_heads, int32_t d_qk, int32_t d_v,
                                int32_t topk, int32_t dtype);
 

@@ -21,8 +21,8 @@ LIB_PATH = os.path.join(_HERE, "libhisparse.so")
 HS_OK, HS_ERR_INVALID_ARG, HS_ERR_CAPACITY, HS_ERR_UNSUPPORTED, HS_ERR_HIP = 0, -1, -2, -3, -4
 HS_BF16, HS_F32 = 0, 1
 
-EXPORTED = ("hs_resolve_topk", "hs_swap_in", "hs_sparse_decode_attn", "hs_attn_workspace_bytes",
-            "hs_finalize_accepted", "hs_status_string", "hs_version")
+EXPORTED = ("hs_resolve_topk", "hs_swap_in", "hs_sparse_decode_attn", "hs_sparse_decode_attn_paged",
+            "hs_attn_workspace_bytes", "hs_finalize_accepted", "hs_status_string", "hs_version")
 
 
 class HsError(RuntimeError):
@@ -52,6 +52,10 @@ def _load() -> ctypes.CDLL:
     lib.hs_sparse_decode_attn.argtypes = [vp, vp, i64, vp, i32, i32, i32, i32, i32, f32, i32,
                                           vp, vp, vp, sz, vp]
     lib.hs_sparse_decode_attn.restype = i32
+    lib.hs_sparse_decode_attn_paged.argtypes = [vp, vp, i64, vp, vp, vp, i32, vp, i32, i32, i32,
+                                                i32, i32, i32, i32, i32, f32, i32, vp, vp, vp, sz,
+                                                vp]
+    lib.hs_sparse_decode_attn_paged.restype = i32
     lib.hs_attn_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32]
     lib.hs_attn_workspace_bytes.restype = sz
     lib.hs_finalize_accepted.argtypes = [ctypes.POINTER(HsHotState), vp, i32, vp, vp, i32, vp, vp,
@@ -185,6 +189,33 @@ def hs_sparse_decode_attn(q: torch.Tensor, kv: torch.Tensor, indices: torch.Tens
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check("hs_sparse_decode_attn", _lib.hs_sparse_decode_attn(
         _ptr(q), _ptr(kv), kv.shape[0], _ptr(indices), rows, heads, d_qk, d_v, indices.shape[1],
+        float(scale), _dtype_code(q.dtype), _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes,
+        _stream(stream)))
+
+
+def hs_sparse_decode_attn_paged(q: torch.Tensor, kv_pool: torch.Tensor, topk_pos: torch.Tensor,
+                                req_id: torch.Tensor, causal_limit: torch.Tensor,
+                                block_table: torch.Tensor, block_size: int,
+                                physical_block_stride: int, scale: float, d_v: int,
+                                out: torch.Tensor, lse: Optional[torch.Tensor] = None,
+                                workspace: Optional[torch.Tensor] = None, stream=None):
+    """Resolve + attention of a fully resident batch in one call (see include/hisparse.h)."""
+    i32 = torch.int32
+    _dev(q, "q"); _dev(kv_pool, "kv_pool"); _dev(out, "out", q.dtype)
+    _dev(topk_pos, "topk_pos", i32); _dev(req_id, "req_id", i32)
+    _dev(causal_limit, "causal_limit", i32); _dev(block_table, "block_table", i32)
+    if kv_pool.dtype != q.dtype:
+        raise ValueError("q and kv_pool dtypes differ")
+    if lse is not None:
+        _dev(lse, "lse", torch.float32)
+    if workspace is not None:
+        _dev(workspace, "workspace")
+    rows, heads, d_qk = q.shape
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("hs_sparse_decode_attn_paged", _lib.hs_sparse_decode_attn_paged(
+        _ptr(q), _ptr(kv_pool), kv_pool.shape[0], _ptr(topk_pos), _ptr(req_id),
+        _ptr(causal_limit), block_table.shape[0], _ptr(block_table), block_table.shape[1],
+        block_size, physical_block_stride, rows, heads, d_qk, d_v, topk_pos.shape[1],
         float(scale), _dtype_code(q.dtype), _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes,
         _stream(stream)))
 

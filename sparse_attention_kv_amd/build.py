@@ -2,7 +2,8 @@
 
 Each translation unit is compiled in parallel into _build/, then linked into
 sparse_attention_kv_amd/libhisparse.so (replaced atomically).
-Usage: python -m sparse_attention_kv_amd.build [--asm]
+Usage: python sparse_attention_kv_amd/build.py [--asm]   (run by path: importing the
+package loads the library, which may be missing or stale before this build)
 """
 
 from __future__ import annotations

@@ -117,13 +117,44 @@ hs_status hs_sparse_decode_attn(const void *q, const void *kv, int64_t kv_rows,
                                !aligned16(workspace)))
       return HS_ERR_INVALID_ARG;
     return from_hip(hs::launch_attn_bf16(q, kv, kv_rows, indices, num_rows, num_heads, topk, scale,
-                                         out, lse, workspace, plan, st));
+                                         out, lse, workspace, plan, nullptr, st));
   }
   if (d_qk > hs::attn_f32_max_d() || d_v > d_qk || topk > hs::attn_f32_max_topk())
     return HS_ERR_UNSUPPORTED;
   return from_hip(hs::launch_attn_f32(static_cast<const float *>(q), static_cast<const float *>(kv),
                                       kv_rows, indices, num_rows, num_heads, d_qk, d_v, topk, scale,
                                       static_cast<float *>(out), lse, st));
+}
+
+hs_status hs_sparse_decode_attn_paged(const void *q, const void *kv_pool, int64_t kv_rows,
+                                      const int32_t *topk_pos, const int32_t *req_id,
+                                      const int32_t *causal_limit, int32_t num_reqs,
+                                      const int32_t *block_table, int32_t bt_stride,
+                                      int32_t block_size, int32_t physical_block_stride,
+                                      int32_t num_rows, int32_t num_heads, int32_t d_qk,
+                                      int32_t d_v, int32_t topk, float scale, int32_t dtype,
+                                      void *out, float *lse, void *workspace,
+                                      size_t workspace_bytes, void *stream) {
+  if (num_rows < 0 || num_heads <= 0 || d_qk <= 0 || d_v <= 0 || topk <= 0 || kv_rows < 0 ||
+      num_reqs <= 0 || bt_stride <= 0 || block_size <= 0 || physical_block_stride <= 0)
+    return HS_ERR_INVALID_ARG;
+  if (dtype != HS_BF16 && dtype != HS_F32) return HS_ERR_INVALID_ARG;
+  if (num_rows == 0) return HS_OK;
+  if (!q || !kv_pool || !topk_pos || !req_id || !causal_limit || !block_table || !out)
+    return HS_ERR_INVALID_ARG;
+  if (kv_rows > 0x7fffffffLL) return HS_ERR_INVALID_ARG;
+  if (dtype != HS_BF16 || d_qk != 576 || d_v != 512 || num_heads % 32 != 0)
+    return HS_ERR_UNSUPPORTED;
+  if (!aligned16(q) || !aligned16(kv_pool) || !aligned16(out)) return HS_ERR_INVALID_ARG;
+  const hs::AttnPlan plan = hs::plan_attn_bf16(num_rows, num_heads, topk);
+  if (plan.workspace > 0 &&
+      (workspace == nullptr || workspace_bytes < plan.workspace || !aligned16(workspace)))
+    return HS_ERR_INVALID_ARG;
+  const hs::PagedMap pg{req_id, causal_limit, block_table, num_reqs, bt_stride, block_size,
+                        physical_block_stride};
+  return from_hip(hs::launch_attn_bf16(q, kv_pool, kv_rows, topk_pos, num_rows, num_heads, topk,
+                                       scale, out, lse, workspace, plan, &pg,
+                                       static_cast<hipStream_t>(stream)));
 }
 
 hs_status hs_finalize_accepted(const hs_hot_state *st, const void *logits, int32_t vocab,

@@ -65,12 +65,12 @@ __device__ __forceinline__ void gather_part(const uint8_t *__restrict__ kv, cons
   }
 }
 
-template <bool kSplit>
+template <bool kSplit, bool kPaged>
 __global__ __launch_bounds__(kThreads8, 1) void attn_bf16_kernel(
     const __bf16 *__restrict__ q, const uint8_t *__restrict__ kv, int64_t kv_rows,
     const int32_t *__restrict__ indices, int32_t num_rows, int32_t num_heads, int32_t topk,
     int32_t keys_per_split, int32_t splits, float scale_log2, __bf16 *__restrict__ out,
-    float *__restrict__ lse, __bf16 *__restrict__ ws_o, float *__restrict__ ws_ml) {
+    float *__restrict__ lse, __bf16 *__restrict__ ws_o, float *__restrict__ ws_ml, PagedMap pg) {
   __shared__ __attribute__((aligned(16))) uint8_t s_kv0[kTileBytes];
   __shared__ __attribute__((aligned(16))) uint8_t s_kv1[kTileBytes];
   __shared__ __attribute__((aligned(16))) uint8_t s_p[kHG * kPStride];
@@ -100,15 +100,11 @@ __global__ __launch_bounds__(kThreads8, 1) void attn_bf16_kernel(
   const int kbeg = split * keys_per_split;
   const int kcnt = max(0, min(keys_per_split, topk - kbeg));
 
-  // ---- indices of this split (issued first: they gate the first KV gather) ----
+  // ---- indices (or token positions) of this split: they gate the first KV gather ----
   const int32_t *irow = indices + (int64_t)row * topk + kbeg;
   const int per = (kcnt + kThreads8 - 1) / kThreads8;  // <= 4
   int vals[kMaxKeysPerSplit / kThreads8];
-#pragma unroll
-  for (int k = 0; k < kMaxKeysPerSplit / kThreads8; ++k) {
-    const int j = tid * per + k;
-    vals[k] = (k < per && j < kcnt) ? irow[j] : -1;
-  }
+  load_split_indices<kPaged>(irow, per, kcnt, tid, pg, row, vals);
 
   // ---- Q (32 heads x 576), one copy per workgroup, staged through the second tile buffer.
   // Slot 18hb + ks (1 KiB) holds, at 16l, lane l's chunk of the B operand for head block hb:
@@ -230,8 +226,8 @@ __global__ __launch_bounds__(kThreads8, 1) void attn_bf16_kernel(
       lds_barrier();
       const bool more = t + 1 < ntiles;
 
-      // ---- S^T (this wave's 16 keys x 16 heads), K fragments read 6 at a time ahead; the
-      // next tile's 9 DMA slots go out 3 after each batch of 6 MFMAs ----
+      // ---- S^T (this wave's 16 keys x 16 heads), K fragments read 3 at a time ahead; the
+      // next tile's 9 DMA slots go out 2, 1, 2, 1, 2, 1 after the six batches of 3 MFMAs ----
       f32x4 sacc;
 #pragma unroll
       for (int i = 0; i < 4; ++i) sacc[i] = 0.f;
@@ -239,7 +235,7 @@ __global__ __launch_bounds__(kThreads8, 1) void attn_bf16_kernel(
         const int key = 16 * kq + (l & 15);
         const uint8_t *krow = cur + key * kRowBytes;
         const int sw = (key >> 1) & 7;
-        constexpr int kB = 6;
+        constexpr int kB = 3;
         bf16x8 kf[2][kB];
 #pragma unroll
         for (int j = 0; j < kB; ++j)
@@ -259,9 +255,12 @@ __global__ __launch_bounds__(kThreads8, 1) void attn_bf16_kernel(
           for (int j = 0; j < kB; ++j)
             sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[bt & 1][j], qreg[bt * kB + j], sacc, 0, 0, 0);
           if (more) {
-            if (bt == 0) gather_part<0, 3>(kv, s_sidx, n_valid, t + 1, nxt, w, l);
-            if (bt == 1) gather_part<3, 3>(kv, s_sidx, n_valid, t + 1, nxt, w, l);
-            if (bt == 2) gather_part<6, 3>(kv, s_sidx, n_valid, t + 1, nxt, w, l);
+            if (bt == 0) gather_part<0, 2>(kv, s_sidx, n_valid, t + 1, nxt, w, l);
+            if (bt == 1) gather_part<2, 1>(kv, s_sidx, n_valid, t + 1, nxt, w, l);
+            if (bt == 2) gather_part<3, 2>(kv, s_sidx, n_valid, t + 1, nxt, w, l);
+            if (bt == 3) gather_part<5, 1>(kv, s_sidx, n_valid, t + 1, nxt, w, l);
+            if (bt == 4) gather_part<6, 2>(kv, s_sidx, n_valid, t + 1, nxt, w, l);
+            if (bt == 5) gather_part<8, 1>(kv, s_sidx, n_valid, t + 1, nxt, w, l);
           }
           __builtin_amdgcn_sched_barrier(0);
         }
@@ -530,35 +529,47 @@ AttnPlan plan_attn_bf16(int32_t num_rows, int32_t num_heads, int32_t topk) {
   return p;
 }
 
-hipError_t launch_attn_bf16(const void *q, const void *kv, int64_t kv_rows, const int32_t *indices,
-                            int32_t num_rows, int32_t num_heads, int32_t topk, float scale,
-                            void *out, float *lse, void *workspace, const AttnPlan &plan,
-                            hipStream_t stream) {
-  if (plan.heads_per_wg == 64)
-    return launch_attn64(q, kv, kv_rows, indices, num_rows, num_heads, topk, scale, out, lse,
-                         workspace, plan, stream);
-  const int n_hg = num_heads / kHG;
-  const int units = num_rows * plan.splits * n_hg;
+template <bool kPaged>
+static hipError_t launch_attn32(const __bf16 *qb, const uint8_t *kvb, int64_t kv_rows,
+                                const int32_t *indices, int32_t num_rows, int32_t num_heads,
+                                int32_t topk, float scale_log2, __bf16 *ob, float *lse,
+                                void *workspace, const AttnPlan &plan, const PagedMap &pg,
+                                hipStream_t stream) {
+  const int units = num_rows * plan.splits * (num_heads / kHG);
   const int grid = (units + 7) / 8 * 8;
-  const float scale_log2 = scale * 1.44269504088896340736f;
-  const __bf16 *qb = static_cast<const __bf16 *>(q);
-  const uint8_t *kvb = static_cast<const uint8_t *>(kv);
-  __bf16 *ob = static_cast<__bf16 *>(out);
   if (plan.splits == 1) {
-    hipLaunchKernelGGL(attn_bf16_kernel<false>, dim3(grid), dim3(kThreads8), 0, stream, qb, kvb,
-                       kv_rows, indices, num_rows, num_heads, topk, plan.keys_per_split, 1,
-                       scale_log2, ob, lse, nullptr, nullptr);
+    hipLaunchKernelGGL((attn_bf16_kernel<false, kPaged>), dim3(grid), dim3(kThreads8), 0, stream,
+                       qb, kvb, kv_rows, indices, num_rows, num_heads, topk, plan.keys_per_split,
+                       1, scale_log2, ob, lse, nullptr, nullptr, pg);
     return hipGetLastError();
   }
   __bf16 *ws_o = static_cast<__bf16 *>(workspace);
   float *ws_ml = reinterpret_cast<float *>(ws_o + (size_t)plan.splits * num_rows * num_heads * kDV);
-  hipLaunchKernelGGL(attn_bf16_kernel<true>, dim3(grid), dim3(kThreads8), 0, stream, qb, kvb,
-                     kv_rows, indices, num_rows, num_heads, topk, plan.keys_per_split, plan.splits,
-                     scale_log2, ob, lse, ws_o, ws_ml);
+  hipLaunchKernelGGL((attn_bf16_kernel<true, kPaged>), dim3(grid), dim3(kThreads8), 0, stream, qb,
+                     kvb, kv_rows, indices, num_rows, num_heads, topk, plan.keys_per_split,
+                     plan.splits, scale_log2, ob, lse, ws_o, ws_ml, pg);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   launch_attn_combine(ws_o, ws_ml, plan.splits, num_rows, num_heads, ob, lse, stream);
   return hipGetLastError();
+}
+
+hipError_t launch_attn_bf16(const void *q, const void *kv, int64_t kv_rows, const int32_t *indices,
+                            int32_t num_rows, int32_t num_heads, int32_t topk, float scale,
+                            void *out, float *lse, void *workspace, const AttnPlan &plan,
+                            const PagedMap *paged, hipStream_t stream) {
+  if (plan.heads_per_wg == 64)
+    return launch_attn64(q, kv, kv_rows, indices, num_rows, num_heads, topk, scale, out, lse,
+                         workspace, plan, paged, stream);
+  const float scale_log2 = scale * 1.44269504088896340736f;
+  const __bf16 *qb = static_cast<const __bf16 *>(q);
+  const uint8_t *kvb = static_cast<const uint8_t *>(kv);
+  __bf16 *ob = static_cast<__bf16 *>(out);
+  if (paged != nullptr)
+    return launch_attn32<true>(qb, kvb, kv_rows, indices, num_rows, num_heads, topk, scale_log2, ob,
+                               lse, workspace, plan, *paged, stream);
+  return launch_attn32<false>(qb, kvb, kv_rows, indices, num_rows, num_heads, topk, scale_log2, ob,
+                              lse, workspace, plan, PagedMap{}, stream);
 }
 
 hipError_t launch_attn_f32(const float *q, const float *kv, int64_t kv_rows, const int32_t *indices,

@@ -61,13 +61,13 @@ __device__ __forceinline__ void gather64(const uint8_t *__restrict__ kv, const i
   }
 }
 
-template <bool kSplit>
+template <bool kSplit, bool kPaged>
 __global__ __launch_bounds__(kThreads, 1) void attn64_kernel(
     const __bf16 *__restrict__ q, const uint8_t *__restrict__ kv, int64_t kv_rows,
     const int32_t *__restrict__ indices, int32_t num_rows, int32_t num_heads, int32_t topk,
     int32_t keys_per_split, int32_t splits, int32_t units, float scale_log2,
     __bf16 *__restrict__ out, float *__restrict__ lse, __bf16 *__restrict__ ws_o,
-    float *__restrict__ ws_ml) {
+    float *__restrict__ ws_ml, PagedMap pg) {
   __shared__ __attribute__((aligned(16))) uint8_t s_kv0[kTileBytes];
   __shared__ __attribute__((aligned(16))) uint8_t s_kv1[kTileBytes];
   __shared__ __attribute__((aligned(16))) int32_t s_sidx[kMaxKeysPerSplit];
@@ -88,15 +88,11 @@ __global__ __launch_bounds__(kThreads, 1) void attn64_kernel(
   const int kbeg = split * keys_per_split;
   const int kcnt = max(0, min(keys_per_split, topk - kbeg));
 
-  // ---- indices of this split (they gate the first gather) ----
+  // ---- indices (or token positions) of this split: they gate the first gather ----
   const int32_t *irow = indices + (int64_t)row * topk + kbeg;
   const int pk = (kcnt + kThreads - 1) / kThreads;  // <= 8
   int vals[kMaxKeysPerSplit / kThreads];
-#pragma unroll
-  for (int k = 0; k < kMaxKeysPerSplit / kThreads; ++k) {
-    const int j = tid * pk + k;
-    vals[k] = (k < pk && j < kcnt) ? irow[j] : -1;
-  }
+  load_split_indices<kPaged>(irow, pk, kcnt, tid, pg, row, vals);
   // ---- Q of the wave's 16 heads: B operand of S^T = K Q^T (head l&15, dims 32ks+8(l>>4)..) ----
   bf16x8 qreg[kKSteps];
   {
@@ -313,32 +309,45 @@ __global__ __launch_bounds__(kThreads, 1) void attn64_kernel(
   }
 }
 
-}  // namespace
-
-hipError_t launch_attn64(const void *q, const void *kv, int64_t kv_rows, const int32_t *indices,
-                         int32_t num_rows, int32_t num_heads, int32_t topk, float scale, void *out,
-                         float *lse, void *workspace, const AttnPlan &plan, hipStream_t stream) {
+template <bool kPaged>
+static hipError_t launch64(const __bf16 *qb, const uint8_t *kvb, int64_t kv_rows,
+                           const int32_t *indices, int32_t num_rows, int32_t num_heads, int32_t topk,
+                           float scale_log2, __bf16 *ob, float *lse, void *workspace,
+                           const AttnPlan &plan, const PagedMap &pg, hipStream_t stream) {
   const int units = num_rows * (num_heads / kH64) * plan.splits;
   const int grid = (units + 7) / 8 * 8;
-  const float scale_log2 = scale * 1.44269504088896340736f;
-  const __bf16 *qb = static_cast<const __bf16 *>(q);
-  const uint8_t *kvb = static_cast<const uint8_t *>(kv);
-  __bf16 *ob = static_cast<__bf16 *>(out);
   if (plan.splits == 1) {
-    hipLaunchKernelGGL(attn64_kernel<false>, dim3(grid), dim3(kThreads), 0, stream, qb, kvb,
-                       kv_rows, indices, num_rows, num_heads, topk, plan.keys_per_split, 1, units,
-                       scale_log2, ob, lse, nullptr, nullptr);
+    hipLaunchKernelGGL((attn64_kernel<false, kPaged>), dim3(grid), dim3(kThreads), 0, stream, qb,
+                       kvb, kv_rows, indices, num_rows, num_heads, topk, plan.keys_per_split, 1,
+                       units, scale_log2, ob, lse, nullptr, nullptr, pg);
     return hipGetLastError();
   }
   __bf16 *ws_o = static_cast<__bf16 *>(workspace);
   float *ws_ml = reinterpret_cast<float *>(ws_o + (size_t)plan.splits * num_rows * num_heads * kDV);
-  hipLaunchKernelGGL(attn64_kernel<true>, dim3(grid), dim3(kThreads), 0, stream, qb, kvb, kv_rows,
-                     indices, num_rows, num_heads, topk, plan.keys_per_split, plan.splits, units,
-                     scale_log2, ob, lse, ws_o, ws_ml);
+  hipLaunchKernelGGL((attn64_kernel<true, kPaged>), dim3(grid), dim3(kThreads), 0, stream, qb, kvb,
+                     kv_rows, indices, num_rows, num_heads, topk, plan.keys_per_split, plan.splits,
+                     units, scale_log2, ob, lse, ws_o, ws_ml, pg);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   launch_attn_combine(ws_o, ws_ml, plan.splits, num_rows, num_heads, ob, lse, stream);
   return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_attn64(const void *q, const void *kv, int64_t kv_rows, const int32_t *indices,
+                         int32_t num_rows, int32_t num_heads, int32_t topk, float scale, void *out,
+                         float *lse, void *workspace, const AttnPlan &plan, const PagedMap *paged,
+                         hipStream_t stream) {
+  const float scale_log2 = scale * 1.44269504088896340736f;
+  const __bf16 *qb = static_cast<const __bf16 *>(q);
+  const uint8_t *kvb = static_cast<const uint8_t *>(kv);
+  __bf16 *ob = static_cast<__bf16 *>(out);
+  if (paged != nullptr)
+    return launch64<true>(qb, kvb, kv_rows, indices, num_rows, num_heads, topk, scale_log2, ob, lse,
+                          workspace, plan, *paged, stream);
+  return launch64<false>(qb, kvb, kv_rows, indices, num_rows, num_heads, topk, scale_log2, ob, lse,
+                         workspace, plan, PagedMap{}, stream);
 }
 
 }  // namespace hs

@@ -57,6 +57,48 @@ constexpr int vmcnt_imm(int n) { return ((n >> 4) & 3) << 14 | 0x3f70 | (n & 15)
 // v_max_f32 (inputs here are finite or -inf)
 __device__ __forceinline__ float vmax(float a, float b) { return __builtin_fmaxf(a, b); }
 
+// Load this thread's share of a split's indices: entry j = tid * per + k (k < per) of
+// `irow`.  With kPaged the entries are request-local token positions, resolved here exactly
+// as hs_resolve_topk does (P3 "vllm 分析（十二）——Hisparse下篇", resolve_topk listing:
+// position t of a row of request b is kept iff 0 <= t < causal_limit, its page t / block_size
+// is inside the table row and mapped; it becomes page * physical_block_stride + t % block_size;
+// P3 "数据 back up": rows of page p are p * block_size + offset).  All position loads are
+// issued before the block-table loads.  Invalid entries come back as -1.
+template <bool kPaged, int kN>
+__device__ __forceinline__ void load_split_indices(const int32_t *__restrict__ irow, int per,
+                                                   int kcnt, int tid, const PagedMap &pg, int row,
+                                                   int (&vals)[kN]) {
+#pragma unroll
+  for (int k = 0; k < kN; ++k) {
+    const int j = tid * per + k;
+    vals[k] = (k < per && j < kcnt) ? irow[j] : -1;
+  }
+  if constexpr (kPaged) {
+    const int b = pg.req_id[row];
+    const int lim = pg.causal_limit[row];
+    const bool req_ok = b >= 0 && b < pg.num_reqs;
+    const int32_t *bt = pg.block_table + (int64_t)(req_ok ? b : 0) * pg.bt_stride;
+    int pidx[kN], page[kN];
+#pragma unroll
+    for (int k = 0; k < kN; ++k) {
+      const int t = vals[k];
+      const bool ok = req_ok && t >= 0 && t < lim;
+      pidx[k] = ok ? t / pg.block_size : pg.bt_stride;
+      page[k] = pidx[k] < pg.bt_stride ? bt[pidx[k]] : -1;
+    }
+#pragma unroll
+    for (int k = 0; k < kN; ++k) {
+      int slot = -1;
+      if (page[k] >= 0) {
+        const int64_t r = (int64_t)page[k] * pg.physical_block_stride +
+                          (vals[k] - pidx[k] * pg.block_size);
+        slot = r < 0x7fffffffLL ? (int)r : -1;
+      }
+      vals[k] = slot;
+    }
+  }
+}
+
 // Scores are kept relative to a reference max m_ref per head (log2 domain).  P is formed
 // as 2^(s - m_ref) without re-normalising O every tile; only when a score exceeds m_ref
 // by more than kRescaleSlack (P would exceed 2^kRescaleSlack) is a new reference taken

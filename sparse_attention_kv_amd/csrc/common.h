@@ -34,6 +34,15 @@ hipError_t launch_swap_in(const hs_hot_state &st, const void *host_pool_dev,
                           int32_t *out_hot_idx, int32_t *out_miss_count, int32_t *out_miss_pos,
                           hipStream_t stream);
 
+// Block-table description for attention that resolves top-k token positions itself
+// (the fully resident batch); null = the indices are already KV rows.
+struct PagedMap {
+  const int32_t *req_id;        // [num_rows]
+  const int32_t *causal_limit;  // [num_rows]
+  const int32_t *block_table;   // [num_reqs, bt_stride]
+  int32_t num_reqs, bt_stride, block_size, physical_block_stride;
+};
+
 struct AttnPlan {
   int heads_per_wg;    // 64 (attn64_kernel) or 32 (attn_bf16_kernel)
   int splits;          // key splits per (row, head group); 1 = no combine pass
@@ -45,11 +54,12 @@ AttnPlan plan_attn_bf16(int32_t num_rows, int32_t num_heads, int32_t topk);
 hipError_t launch_attn_bf16(const void *q, const void *kv, int64_t kv_rows, const int32_t *indices,
                             int32_t num_rows, int32_t num_heads, int32_t topk, float scale,
                             void *out, float *lse, void *workspace, const AttnPlan &plan,
-                            hipStream_t stream);
+                            const PagedMap *paged, hipStream_t stream);
 
 hipError_t launch_attn64(const void *q, const void *kv, int64_t kv_rows, const int32_t *indices,
                          int32_t num_rows, int32_t num_heads, int32_t topk, float scale, void *out,
-                         float *lse, void *workspace, const AttnPlan &plan, hipStream_t stream);
+                         float *lse, void *workspace, const AttnPlan &plan, const PagedMap *paged,
+                         hipStream_t stream);
 
 hipError_t launch_attn_f32(const float *q, const float *kv, int64_t kv_rows, const int32_t *indices,
                            int32_t num_rows, int32_t num_heads, int32_t d_qk, int32_t d_v,

@@ -24,7 +24,7 @@ from typing import Optional
 import torch
 
 from . import (HotState, hs_attn_workspace_bytes, hs_finalize_accepted, hs_resolve_topk,
-               hs_sparse_decode_attn, hs_swap_in)
+               hs_sparse_decode_attn, hs_sparse_decode_attn_paged, hs_swap_in)
 
 
 def build_hot_state(init_pos: torch.Tensor, init_stamp: torch.Tensor, seq_len: torch.Tensor,
@@ -111,6 +111,15 @@ class DecodeStep:
         hs_resolve_topk(topk_pos, req_id, causal_limit, block_table, block_size, block_size,
                         b.slots, b.valid)
         hs_sparse_decode_attn(q, kv_pool, b.slots, scale, self.d_v, b.out, b.lse, b.workspace)
+
+    def run_resident_fused(self, topk_pos, req_id, causal_limit, block_table, block_size, q,
+                           kv_pool, scale):
+        """Same result as run_resident in one call: positions are resolved inside the
+        attention kernel (the rows are not written out)."""
+        b = self.buf
+        hs_sparse_decode_attn_paged(q, kv_pool, topk_pos, req_id, causal_limit, block_table,
+                                    block_size, block_size, scale, self.d_v, b.out, b.lse,
+                                    b.workspace)
 
     # -- swap batch (waves) -------------------------------------------------------------
     def run_swap(self, state: HotState, topk_pos, req_id, causal_limit, block_table, block_size,
