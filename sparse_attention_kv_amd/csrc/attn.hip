@@ -397,9 +397,13 @@ __global__ __launch_bounds__(64) void attn_combine_kernel(const __bf16 *__restri
                                                          int32_t num_heads,
                                                          __bf16 *__restrict__ out,
                                                          float *__restrict__ lse) {
-  const int64_t hi = blockIdx.x;  // row * num_heads + head
-  const int l = threadIdx.x;
+  // (row, head) units in row-major order, XCD x (dispatch i runs on XCD i % 8) taking units
+  // [x * per, (x + 1) * per): the XCD the attention kernel ran a row's splits on.
   const int64_t plane = (int64_t)num_rows * num_heads;
+  const int64_t per = (plane + 7) / 8;
+  const int64_t hi = (blockIdx.x & 7) * per + (blockIdx.x >> 3);  // row * num_heads + head
+  if (hi >= plane) return;
+  const int l = threadIdx.x;
   float M = -INFINITY, wsum = 0.f;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   for (int s0 = 0; s0 < splits; s0 += kCombineChunk) {
@@ -504,7 +508,8 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(const float *__restrict__ 
 
 void launch_attn_combine(const __bf16 *ws_o, const float *ws_ml, int32_t splits, int32_t num_rows,
                          int32_t num_heads, __bf16 *out, float *lse, hipStream_t stream) {
-  hipLaunchKernelGGL(attn_combine_kernel, dim3(num_rows * num_heads), dim3(64), 0, stream, ws_o,
+  const int units = num_rows * num_heads;
+  hipLaunchKernelGGL(attn_combine_kernel, dim3((units + 7) / 8 * 8), dim3(64), 0, stream, ws_o,
                      ws_ml, splits, num_rows, num_heads, out, lse);
 }
 
