@@ -17,7 +17,9 @@ on the host cores over the same workload.
 
 A second object, `swap_in`, measures the swap path on the 32-request MTP workload: the
 host-link reference rate (1 GiB pinned->device copy, and a cold swap-in wave that misses
-on every row), the swap-in kernel's rate over its miss bytes, and the whole step.
+on every row), the swap-in kernel's rate over its miss bytes, and the whole step.  A third,
+`finalize`, times greedy accept + accepted-prefix finalize on the mixed workload's verify
+shape (the argmax over 99.3 MB of logits is HBM-bound).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-swap]
 """
@@ -221,6 +223,61 @@ def measure_swap(dev, reps=5):
     }
 
 
+def measure_finalize(dev, reps=10):
+    """Greedy accept + accepted-prefix finalize on the mixed workload's verify shape: 128
+    requests x 3 rows, logits [384, 129280] bf16 (99.3 MB), 4096 hot slots per request.
+    The sequence lengths are drawn from [2048, 4096] instead of up to 128 K to keep the
+    pinned host pool small; the logits, rows and hot buffer are the workload's.  Hot state
+    is restored from a device snapshot before every repetition (not timed)."""
+    import numpy as np
+    import torch
+
+    import sparse_attention_kv_amd as hs
+    from sparse_attention_kv_amd.pipeline import build_hot_state
+    from workloads import generate, spec
+
+    s = spec("mixed_finalize", seq_rule=("uniform", 2048, 4096))
+    log(f"generate {s.name} (finalize shape)")
+    w = generate(s, pin_host_pool=True)
+
+    def d(a):
+        return torch.as_tensor(np.ascontiguousarray(a)).to(device=dev, dtype=torch.int32)
+
+    seq, bt = d(w.seq_len), d(w.block_table)
+    st = build_hot_state(torch.from_numpy(w.init_pos), torch.from_numpy(w.init_stamp), seq, bt,
+                         s.block_size, w.kv_pool, dev)
+    snap = [t.clone() for t in (st.slot_loc, st.slot_stamp, st.loc_to_hot)]
+    logits, draft, new_kv = w.logits.to(dev), d(w.draft_ids), w.new_kv.to(dev)
+    rows = s.rows
+    am = torch.empty(rows, dtype=torch.int32, device=dev)
+    acc = torch.empty(s.num_reqs, dtype=torch.int32, device=dev)
+    nxt = torch.empty(s.num_reqs, dtype=torch.int32, device=dev)
+    main = torch.cuda.current_stream()
+    times = []
+    for rep in range(reps + 2):
+        for t, c in zip((st.slot_loc, st.slot_stamp, st.loc_to_hot), snap):
+            t.copy_(c)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(main)
+        hs.hs_finalize_accepted(st, logits, draft, new_kv, s.rows_per_req, seq, bt, s.block_size,
+                                s.tick0 + s.rows_per_req, am, acc, nxt)
+        e1.record(main)
+        torch.cuda.synchronize()
+        if rep >= 2:
+            times.append(e0.elapsed_time(e1) * 1e3)
+    us = float(np.median(times))
+    logit_bytes = rows * s.vocab * 2
+    return {
+        "workload": "greedy accept + finalize: 128 requests x 3 rows, logits [384, 129280] bf16, "
+                    "4096 hot slots per request",
+        "call_us": us, "logits_bytes": logit_bytes,
+        "logits_GBps": logit_bytes / (us / 1e6) / 1e9,
+        "logits_frac_of_hbm_peak": logit_bytes / (us / 1e6) / 1e9 / HBM_PEAK_GBS,
+        "accept_length_histogram": np.bincount(acc.cpu().numpy(), minlength=s.rows_per_req).tolist(),
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -361,6 +418,8 @@ def main():
     if not args.no_swap:
         log("swap path")
         res["swap_in"] = measure_swap(dev)
+        log("finalize")
+        res["finalize"] = measure_finalize(dev)
     if not args.no_cpu:
         log("cpu baseline (oracle)")
         res["cpu_baseline"] = cpu_baseline(w, s)

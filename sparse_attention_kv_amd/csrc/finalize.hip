@@ -22,9 +22,11 @@
 namespace hs {
 namespace {
 
-constexpr int kArgThreads = 512;
+constexpr int kArgThreads = 256;
+constexpr int kArgUnroll = 8;  // 16-byte loads in flight per thread
 constexpr int kFinThreads = 256;
 constexpr int kMaxRowsPerReq = 64;
+constexpr int kKeysPerThread = 16;  // victim keys held in registers up to 4096 slots
 
 __device__ __forceinline__ float bf16_bits_to_float(uint16_t b) {
   return __uint_as_float(static_cast<uint32_t>(b) << 16);
@@ -34,6 +36,9 @@ __device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
   return v > bv || (v == bv && i < bi);
 }
 
+// One workgroup per row; several workgroups share a CU (small footprint), so the 384 rows
+// of a verify batch stream concurrently.  Each thread keeps kArgUnroll 16-byte loads in
+// flight and walks its chunks in increasing index order (first maximum kept).
 __global__ __launch_bounds__(kArgThreads) void argmax_kernel(const uint16_t *__restrict__ logits,
                                                              int32_t vocab,
                                                              int32_t *__restrict__ out_argmax) {
@@ -46,14 +51,36 @@ __global__ __launch_bounds__(kArgThreads) void argmax_kernel(const uint16_t *__r
   int bi = 0x7fffffff;
   if ((vocab & 7) == 0) {
     const int chunks = vocab >> 3;
-    for (int c = tid; c < chunks; c += kArgThreads) {
-      const i32x4 raw = *reinterpret_cast<const i32x4 *>(lr + 8 * c);
+    for (int c0 = tid; c0 < chunks; c0 += kArgThreads * kArgUnroll) {
+      i32x4 raw[kArgUnroll];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const uint16_t bits = static_cast<uint16_t>(static_cast<uint32_t>(raw[e >> 1]) >> (16 * (e & 1)));
-        float v = bf16_bits_to_float(bits);
-        v = v != v ? -INFINITY : v;  // NaN never wins
-        if (better(v, 8 * c + e, bv, bi)) { bv = v; bi = 8 * c + e; }
+      for (int k = 0; k < kArgUnroll; ++k) {
+        const int c = c0 + k * kArgThreads;
+        raw[k] = c < chunks ? *reinterpret_cast<const i32x4 *>(lr + 8 * c) : i32x4{0, 0, 0, 0};
+      }
+#pragma unroll
+      for (int k = 0; k < kArgUnroll; ++k) {
+        const int c = c0 + k * kArgThreads;
+        if (c >= chunks) break;
+        // chunk maximum first (v_max_f32 returns the non-NaN operand, so NaN never wins);
+        // the index is searched only when the chunk beats the running best
+        float v[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          v[e] = __uint_as_float((e & 1) ? (static_cast<uint32_t>(raw[k][e >> 1]) & 0xffff0000u)
+                                         : (static_cast<uint32_t>(raw[k][e >> 1]) << 16));
+        const float cm = __builtin_fmaxf(
+            __builtin_fmaxf(__builtin_fmaxf(v[0], v[1]), __builtin_fmaxf(v[2], v[3])),
+            __builtin_fmaxf(__builtin_fmaxf(v[4], v[5]), __builtin_fmaxf(v[6], v[7])));
+        if (cm > bv) {
+          int e0 = 7;
+#pragma unroll
+          for (int e = 7; e >= 0; --e) e0 = v[e] == cm ? e : e0;
+          bv = cm;
+          bi = 8 * c + e0;
+        } else if (bi == 0x7fffffff) {
+          bi = 8 * c;  // every value so far is -inf or NaN: the lowest index stands
+        }
       }
     }
   } else {
@@ -114,13 +141,18 @@ __global__ __launch_bounds__(kFinThreads) void finalize_kernel(
   const int R = rows_per_req;
   const int64_t slot_base = (int64_t)b * capacity;
 
-  if (tid == 0) {
-    int L = 0;
-    while (L < R - 1 && draft_ids[(int64_t)(L + 1) * num_reqs + b] == argmax[(int64_t)L * num_reqs + b]) ++L;
-    out_accept_len[b] = L;
-    out_next_token[b] = argmax[(int64_t)L * num_reqs + b];
-    s_L = L;
-    s_nmiss = 0;
+  // Acceptance length, wave-parallel (R <= 64): lane r checks draft r+1 against the argmax
+  // of row r; L is the number of leading matches.
+  if (tid < 64) {
+    const bool match = tid < R - 1 && draft_ids[(int64_t)(tid + 1) * num_reqs + b] ==
+                                          argmax[(int64_t)tid * num_reqs + b];
+    const uint64_t mism = ~__builtin_amdgcn_ballot_w64(match);
+    const int L = min(static_cast<int>(__builtin_ctzll(mism)), R - 1);
+    if (tid == 0) {
+      out_accept_len[b] = L;
+      out_next_token[b] = argmax[(int64_t)L * num_reqs + b];
+      s_L = L;
+    }
   }
   if (tid < R) {
     // host row of position seq_len - R + tid (same block-table mapping as resolve_topk)
@@ -141,6 +173,18 @@ __global__ __launch_bounds__(kFinThreads) void finalize_kernel(
   }
   __syncthreads();
   const int L = s_L;
+  const int chunks = row_bytes >> 4;
+
+  // kept rows' new KV -> their host-pool rows (device stores over the host link); issued
+  // first so the link transfer overlaps the slot bookkeeping below
+  for (int c = tid; c < (L + 1) * chunks; c += kFinThreads) {
+    const int r = c / chunks;
+    const int part = c - r * chunks;
+    const int loc = s_loc[r];
+    if (loc < 0) continue;
+    const i32x4 v = *reinterpret_cast<const i32x4 *>(new_kv + ((int64_t)r * num_reqs + b) * row_bytes + part * 16);
+    *reinterpret_cast<i32x4 *>(host_pool + (int64_t)loc * row_bytes + part * 16) = v;
+  }
 
   // dropped rows: empty the slot that holds them (host rows untouched)
   if (tid < R && tid > L) {
@@ -155,44 +199,79 @@ __global__ __launch_bounds__(kFinThreads) void finalize_kernel(
     }
   }
   __syncthreads();
-  // kept rows: hit -> its slot (pinned), miss -> queued for install
-  if (tid == 0) {
-    int nm = 0;
-    for (int r = 0; r <= L; ++r) {
-      const int loc = s_loc[r];
-      if (loc < 0) continue;
+  // kept rows (wave-parallel): hit -> its slot (pinned), miss -> listed in row order
+  if (tid < 64) {
+    const int r = tid;
+    const int loc = r <= L && r < R ? s_loc[r] : -1;
+    bool miss = false;
+    if (loc >= 0) {
       const int g = loc_to_hot[loc];
       if (g >= slot_base && g < slot_base + capacity) s_slot[r] = (int)(g - slot_base);
-      else s_miss[nm++] = r;
+      else miss = true;
     }
-    s_nmiss = nm;
+    const uint64_t mm = __builtin_amdgcn_ballot_w64(miss);
+    if (miss) s_miss[__builtin_popcountll(mm & ((1ull << r) - 1))] = r;
+    if (tid == 0) s_nmiss = __builtin_popcountll(mm);
   }
   __syncthreads();
   const int nmiss = s_nmiss;
 
-  // victims: repeatedly the least-recently-used unpinned, unchosen slot (nmiss <= R)
-  for (int k = 0; k < nmiss; ++k) {
-    uint64_t best = ~0ull;
-    for (int s = tid; s < capacity; s += kFinThreads) {
-      bool taken = false;
-      for (int r = 0; r <= L; ++r) taken |= s_slot[r] == s;
-      if (taken) continue;
-      const uint64_t key = (static_cast<uint64_t>(static_cast<uint32_t>(slot_stamp[slot_base + s]) ^ 0x80000000u) << 32) |
-                           static_cast<uint32_t>(s);
-      best = key < best ? key : best;
+  // victims: repeatedly the least-recently-used unpinned, unchosen slot (nmiss <= R).  Up
+  // to 4096 slots the (stamp, slot) keys stay in registers: one pass of loads, then nmiss
+  // block minima.  (A candidate always exists when rows_per_req <= capacity, which the
+  // host checks.)
+  auto slot_key = [&](int sl) -> uint64_t {
+    return (static_cast<uint64_t>(static_cast<uint32_t>(slot_stamp[slot_base + sl]) ^ 0x80000000u) << 32) |
+           static_cast<uint32_t>(sl);
+  };
+  if (nmiss > 0 && capacity <= kFinThreads * kKeysPerThread) {
+    uint64_t keys[kKeysPerThread];
+#pragma unroll
+    for (int i = 0; i < kKeysPerThread; ++i) {
+      const int sl = tid + i * kFinThreads;
+      keys[i] = sl < capacity ? slot_key(sl) : ~0ull;
     }
-    best = block_min_u64(best, s_red);
-    // (a candidate always exists when rows_per_req <= capacity, which the host checks)
-    if (tid == 0) s_slot[s_miss[k]] = best == ~0ull ? -1 : static_cast<int>(best & 0xffffffffu);
+    for (int r = 0; r <= L; ++r) {  // kept hits are pinned
+      const int ps = s_slot[r];
+#pragma unroll
+      for (int i = 0; i < kKeysPerThread; ++i)
+        if (tid + i * kFinThreads == ps) keys[i] = ~0ull;
+    }
+    for (int k = 0; k < nmiss; ++k) {
+      uint64_t best = ~0ull;
+#pragma unroll
+      for (int i = 0; i < kKeysPerThread; ++i) best = keys[i] < best ? keys[i] : best;
+      best = block_min_u64(best, s_red);
+#pragma unroll
+      for (int i = 0; i < kKeysPerThread; ++i)
+        if (keys[i] == best) keys[i] = ~0ull;  // chosen: not a candidate again
+      if (tid == 0) s_slot[s_miss[k]] = best == ~0ull ? -1 : static_cast<int>(best & 0xffffffffu);
+    }
     __syncthreads();
+  } else {
+    for (int k = 0; k < nmiss; ++k) {
+      uint64_t best = ~0ull;
+      for (int sl = tid; sl < capacity; sl += kFinThreads) {
+        bool taken = false;
+        for (int r = 0; r <= L; ++r) taken |= s_slot[r] == sl;
+        if (taken) continue;
+        const uint64_t key = slot_key(sl);
+        best = key < best ? key : best;
+      }
+      best = block_min_u64(best, s_red);
+      if (tid == 0) s_slot[s_miss[k]] = best == ~0ull ? -1 : static_cast<int>(best & 0xffffffffu);
+      __syncthreads();
+    }
   }
-  // Victims were chosen in LRU order; pair them with the misses in ascending slot order.
-  if (tid == 0 && nmiss > 1) {
-    int vs[kMaxRowsPerReq];
-    for (int k = 0; k < nmiss; ++k) vs[k] = s_slot[s_miss[k]];
-    for (int i = 1; i < nmiss; ++i)
-      for (int j = i; j > 0 && vs[j - 1] > vs[j]; --j) { const int t = vs[j]; vs[j] = vs[j - 1]; vs[j - 1] = t; }
-    for (int k = 0; k < nmiss; ++k) s_slot[s_miss[k]] = vs[k];
+  // Victims were chosen in LRU order; pair them with the misses in ascending slot order:
+  // miss k takes the victim of rank k (victims are distinct slots).  One wave; every lane
+  // reads all victims before any lane writes.
+  if (tid < 64 && nmiss > 1) {
+    const int v = tid < nmiss ? s_slot[s_miss[tid]] : 0x7fffffff;
+    int rank = 0;
+    for (int j = 0; j < nmiss; ++j) rank += s_slot[s_miss[j]] < v;
+    __builtin_amdgcn_wave_barrier();
+    if (tid < nmiss) s_slot[s_miss[rank]] = v;
   }
   __syncthreads();
   if (tid < nmiss && s_slot[s_miss[tid]] >= 0) {
@@ -205,17 +284,13 @@ __global__ __launch_bounds__(kFinThreads) void finalize_kernel(
     loc_to_hot[s_loc[r]] = (int32_t)g;
   }
   if (tid <= L && tid < R && s_slot[tid] >= 0) slot_stamp[slot_base + s_slot[tid]] = tick;
-  // row copies: new KV -> host pool row and hot slot (16 bytes per lane access)
-  const int chunks = row_bytes >> 4;
+  // kept rows' new KV -> their hot slots (16 bytes per lane access)
   for (int c = tid; c < (L + 1) * chunks; c += kFinThreads) {
     const int r = c / chunks;
     const int part = c - r * chunks;
-    const int loc = s_loc[r];
-    if (loc < 0) continue;
+    if (s_loc[r] < 0 || s_slot[r] < 0) continue;
     const i32x4 v = *reinterpret_cast<const i32x4 *>(new_kv + ((int64_t)r * num_reqs + b) * row_bytes + part * 16);
-    *reinterpret_cast<i32x4 *>(host_pool + (int64_t)loc * row_bytes + part * 16) = v;
-    if (s_slot[r] >= 0)
-      *reinterpret_cast<i32x4 *>(hot_kv + (slot_base + s_slot[r]) * row_bytes + part * 16) = v;
+    *reinterpret_cast<i32x4 *>(hot_kv + (slot_base + s_slot[r]) * row_bytes + part * 16) = v;
   }
 }
 
