@@ -52,7 +52,7 @@ def attn_alg_bytes(valid_per_row, heads, d_qk, d_v, topk, elem=2):
     return kv + rows * (heads * d_qk * elem + heads * d_v * elem + topk * 4)
 
 
-ATTN_SOURCES = ("attn.hip", "attn64.hip", "attn_tile.h", "common.h")
+ATTN_SOURCES = ("attn.hip", "attn64.hip", "attn128.hip", "attn_tile.h", "common.h")
 
 
 def kernel_source_hash():

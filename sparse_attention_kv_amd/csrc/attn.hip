@@ -31,6 +31,10 @@ namespace {
 
 constexpr int kHG = 32;                       // heads per workgroup
 constexpr int kMinGroups64 = 32;              // (row, 64-head) groups from which attn64 runs
+// (row, 128-head) groups from which attn128 runs.  It reads each KV row once per row instead
+// of twice, but with fewer workgroups than compute units (even after key splits) the 64-head
+// kernel measures faster.
+constexpr int kMinGroups128 = 256;
 constexpr int kThreads8 = 512;                // 8 waves: two per SIMD
 constexpr int kWaves8 = kThreads8 / 64;
 constexpr int kSlots8 = tile::kTK * tile::kRowChunks / kThreads8;  // 9 gather slots per wave
@@ -519,9 +523,10 @@ AttnPlan plan_attn_bf16(int32_t num_rows, int32_t num_heads, int32_t topk) {
   // throughput from 32 rows of 128 heads up) once there are enough (row, 64-head) groups
   // to fill the chip; the 32-head kernel has the shorter critical path for small batches.
   p.heads_per_wg = (num_heads % 64 == 0 && num_rows * (num_heads / 64) >= kMinGroups64) ? 64 : kHG;
+  if (num_heads % 128 == 0 && num_rows * (num_heads / 128) >= kMinGroups128) p.heads_per_wg = 128;
   const int groups = num_rows * (num_heads / p.heads_per_wg);
   // Enough workgroups to cover the 256 CUs once, but keep every split >= min_tiles tiles.
-  const int min_keys = (p.heads_per_wg == 64 ? 2 : 4) * kTK;
+  const int min_keys = (p.heads_per_wg == kHG ? 4 : 2) * kTK;
   int splits = (topk + kMaxKeysPerSplit - 1) / kMaxKeysPerSplit;
   while (groups * splits < 256 && (topk + 2 * splits - 1) / (2 * splits) >= min_keys) splits *= 2;
   int kps = (topk + splits - 1) / splits;
@@ -563,6 +568,9 @@ hipError_t launch_attn_bf16(const void *q, const void *kv, int64_t kv_rows, cons
                             int32_t num_rows, int32_t num_heads, int32_t topk, float scale,
                             void *out, float *lse, void *workspace, const AttnPlan &plan,
                             const PagedMap *paged, hipStream_t stream) {
+  if (plan.heads_per_wg == 128)
+    return launch_attn128(q, kv, kv_rows, indices, num_rows, num_heads, topk, scale, out, lse,
+                          workspace, plan, paged, stream);
   if (plan.heads_per_wg == 64)
     return launch_attn64(q, kv, kv_rows, indices, num_rows, num_heads, topk, scale, out, lse,
                          workspace, plan, paged, stream);

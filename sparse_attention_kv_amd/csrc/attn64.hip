@@ -31,9 +31,14 @@ constexpr int kHW = 16;                 // heads per wave
 constexpr int kH64 = kHW * kWaves;      // heads per workgroup
 constexpr int kKSteps = kD / 32;        // 18 k-steps of 32 over the latent row
 constexpr int kNB = kDV / 16;           // 32 value-dim blocks of 16
+constexpr int kVDepth = 6;              // V operand ring: value blocks in flight
 constexpr int kOStride = kDV * 2 + 16;  // epilogue staging row stride in bytes
 static_assert(kKSteps == kLoadsPerThread, "one gather slot per k-step");
 static_assert(kWaves * kHW * kOStride <= kTileBytes, "O staging fits one tile buffer");
+
+// Part (0..3) of a 32-dim k-step that lane group G of an MFMA operand holds.  Any order
+// works as long as K and Q agree; this one keeps the K reads free of bank conflicts.
+__device__ __forceinline__ int kPartOf(int g) { return ((g & 1) << 1) | (g >> 1); }
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x8 __attribute__((ext_vector_type(8)));
@@ -42,9 +47,12 @@ typedef short s16x8 __attribute__((ext_vector_type(8)));
 //   18432 (k >> 4) + 9216 h + 1024 (p >> 3) + 16 ((k & 7) + 8 ((p & 7) ^ h)),  h = (k >> 3) & 1.
 // Wave w gathers keys 16w .. 16w+15 as 18 one-KiB slots (h, p >> 3): lane l of a slot
 // brings part 8 (p >> 3) + ((l >> 3) ^ h) of key 16w + 8h + (l & 7), i.e. 8 rows x 128 B
-// per instruction.  QK^T operand reads (16 keys x one part) cover 256 distinct bytes per
-// 16 lanes, and the transposed PV reads of a half wave cover 256 distinct bytes: no LDS
-// bank conflicts, and every access of a k-step or value block is base + immediate.
+// per instruction.  A 16-byte LDS read serves the lane octets in the pairs (0,3), (1,2),
+// (4,7), (5,6); a pair is conflict free when it covers 256 distinct bytes mod 256.  The
+// QK^T operand reads let lane group G take part 4 ks + kPartOf(G) (Q uses the same order),
+// which gives every octet pair both 128-byte halves; the transposed PV reads of a half
+// wave cover 256 distinct bytes.  So no LDS bank conflicts, and every access of a k-step
+// or value block is base + immediate.
 constexpr int kRegionBytes = 16 * kRowBytes;  // 18432: one wave's 16 keys
 constexpr int kHalfBytes = 8 * kRowBytes;     // 9216: 8 keys
 
@@ -93,10 +101,11 @@ __global__ __launch_bounds__(kThreads, 1) void attn64_kernel(
   const int pk = (kcnt + kThreads - 1) / kThreads;  // <= 8
   int vals[kMaxKeysPerSplit / kThreads];
   load_split_indices<kPaged>(irow, pk, kcnt, tid, pg, row, vals);
-  // ---- Q of the wave's 16 heads: B operand of S^T = K Q^T (head l&15, dims 32ks+8(l>>4)..) ----
+  // ---- Q of the wave's 16 heads: B operand of S^T = K Q^T (head l&15, dims 32ks +
+  // 8 kPartOf(l>>4) ..) ----
   bf16x8 qreg[kKSteps];
   {
-    const __bf16 *qh = q + ((int64_t)row * num_heads + hw + (l & 15)) * kD + 8 * (l >> 4);
+    const __bf16 *qh = q + ((int64_t)row * num_heads + hw + (l & 15)) * kD + 8 * kPartOf(l >> 4);
 #pragma unroll
     for (int ks = 0; ks < kKSteps; ++ks) qreg[ks] = *reinterpret_cast<const bf16x8 *>(qh + 32 * ks);
   }
@@ -140,10 +149,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn64_kernel(
   float l_run = 0.f;        // this lane's share of that head's softmax sum
   const int G = l >> 4;
 
-  // K operand (A of S^T): lane l reads key 16kb + (l&15), part 4ks + G, which the tile
-  // layout puts at kb region + 9216 h + 16 ((l & 7) + 8 (G ^ h)) + 512 ks.
+  // K operand (A of S^T): lane l reads key 16kb + (l&15), part 4ks + kPartOf(G), which the
+  // tile layout puts at kb region + 9216 h + 16 ((l & 7) + 8 (kPartOf(G) ^ h)) + 512 ks.
   const int hl = (l >> 3) & 1;
-  const int k_off = hl * kHalfBytes + 16 * ((l & 7) + 8 * (G ^ hl));
+  const int k_off = hl * kHalfBytes + 16 * ((l & 7) + 8 * (kPartOf(G) ^ hl));
 
   // O^T += V^T P^T for one tile.  p[4kb + r] is the probability of key 16kb + 4G + r.
   // PV step st covers keys 32st .. 32st + 31; its k-slots for lane group G are keys
@@ -163,20 +172,26 @@ __global__ __launch_bounds__(kThreads, 1) void attn64_kernel(
       for (int e = 0; e < 8; ++e) pa[e] = (__bf16)p[8 * st + e];
       const uint8_t *blo = cur + (2 * st) * kRegionBytes + v_off;      // keys 32st + 4G + r
       const uint8_t *bhi = cur + (2 * st + 1) * kRegionBytes + v_off;  // keys 32st + 16 + 4G + r
-      s16x4 vlo[2], vhi[2];
+      // Ring of kVDepth value fragments: the reads for block nb + kVDepth go out right after
+      // block nb's MFMA (one wave per SIMD: nothing else covers LDS latency); the scheduling
+      // barriers keep that order.
+      s16x4 vlo[kVDepth], vhi[kVDepth];
       auto load_v = [&](int nb, int bb) {
         vlo[bb] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((HS_LDS s16x4 *)(blo + 256 * nb));
         vhi[bb] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((HS_LDS s16x4 *)(bhi + 256 * nb));
       };
-      load_v(0, 0);
+#pragma unroll
+      for (int i = 0; i < kVDepth; ++i) load_v(i, i);
 #pragma unroll
       for (int nb = 0; nb < kNB; ++nb) {
-        if (nb + 1 < kNB) load_v(nb + 1, (nb + 1) & 1);
-        const int bb = nb & 1;
+        const int bb = nb % kVDepth;
         const s16x8 vv = {vlo[bb][0], vlo[bb][1], vlo[bb][2], vlo[bb][3],
                           vhi[bb][0], vhi[bb][1], vhi[bb][2], vhi[bb][3]};
+        __builtin_amdgcn_sched_barrier(0);
         oacc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vv), pa,
                                                            oacc[nb], 0, 0, 0);
+        if (nb + kVDepth < kNB) load_v(nb + kVDepth, bb);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
   };

@@ -44,7 +44,7 @@ struct PagedMap {
 };
 
 struct AttnPlan {
-  int heads_per_wg;    // 64 (attn64_kernel) or 32 (attn_bf16_kernel)
+  int heads_per_wg;    // 128 (attn128_kernel), 64 (attn64_kernel) or 32 (attn_bf16_kernel)
   int splits;          // key splits per (row, head group); 1 = no combine pass
   int keys_per_split;  // multiple of the key tile
   size_t workspace;    // bytes
@@ -60,6 +60,11 @@ hipError_t launch_attn64(const void *q, const void *kv, int64_t kv_rows, const i
                          int32_t num_rows, int32_t num_heads, int32_t topk, float scale, void *out,
                          float *lse, void *workspace, const AttnPlan &plan, const PagedMap *paged,
                          hipStream_t stream);
+
+hipError_t launch_attn128(const void *q, const void *kv, int64_t kv_rows, const int32_t *indices,
+                          int32_t num_rows, int32_t num_heads, int32_t topk, float scale, void *out,
+                          float *lse, void *workspace, const AttnPlan &plan, const PagedMap *paged,
+                          hipStream_t stream);
 
 hipError_t launch_attn_f32(const float *q, const float *kv, int64_t kv_rows, const int32_t *indices,
                            int32_t num_rows, int32_t num_heads, int32_t d_qk, int32_t d_v,

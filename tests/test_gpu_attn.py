@@ -97,7 +97,7 @@ def test_attn_bf16_empty_single_duplicate_and_zero_query():
 def test_attn_split_and_unsplit_agree():
     """One row alone (key-split + combine) vs the same row in a large batch (no split)."""
     import sparse_attention_kv_amd as hs
-    H, kv_rows, topk, big_rows = 128, 20000, 2048, 128
+    H, kv_rows, topk, big_rows = 128, 20000, 2048, 256
     assert hs.hs_attn_workspace_bytes(1, H, 576, 512, topk, torch.bfloat16) > 0
     assert hs.hs_attn_workspace_bytes(big_rows, H, 576, 512, topk, torch.bfloat16) == 0
     q = _rand_bf16((big_rows, H, 576), 21)
@@ -106,7 +106,7 @@ def test_attn_split_and_unsplit_agree():
     idx = to_dev(np.stack([rng.choice(kv_rows, topk, replace=False) for _ in range(big_rows)]).astype(np.int32))
     log("attn split vs unsplit")
     big, big_lse = _attn(q, kv, idx, 1 / 24, 512)
-    for r in (0, 33, 127):
+    for r in (0, 33, 255):
         one, one_lse = _attn(q[r:r + 1].contiguous(), kv, idx[r:r + 1].contiguous(), 1 / 24, 512)
         assert_close(out_f64(one[0]), out_f64(big[r]), (1e-2, 1e-2), "split vs unsplit")
         assert_close(one_lse[0].cpu().double().numpy(), big_lse[r].cpu().double().numpy(), LSE_TOL, "lse")
@@ -154,6 +154,56 @@ def test_attn_bf16_64head_path_zero_query_and_large_scores():
     kv = _rand_bf16((kv_rows, 576), 79)
     idx = np.stack([rng.choice(kv_rows, topk, replace=False) for _ in range(rows)]).astype(np.int32)
     _check(q, kv, to_dev(idx), 1 / 24, 512, BF16_TOL, "64-head zero query / large scores")
+
+
+# >= 256 (row, 128-head) groups take the 128-head kernel: the same cases on that path.  The
+# kernel runs on all 256 rows; the oracle checks a sample that holds every special row.
+_SAMPLE128 = [0, 1, 2, 3, 4, 5, 6, 7, 100, 199, 255]
+
+
+def _check_sampled(q, kv, idx, scale, d_v, what, sample):
+    log(f"attn {what}: rows={q.shape[0]} H={q.shape[1]} topk={idx.shape[1]} sampled {len(sample)}")
+    out, lse = _attn(q, kv, idx, scale, d_v)
+    sel = torch.as_tensor(sample)
+    ref, rlse = oracle.sparse_decode_attn(raw(q.cpu()[sel]), raw(kv.cpu()), idx.cpu().numpy()[sample], scale, d_v)
+    assert_close(out_f64(out[sel.to(out.device)]), ref, BF16_TOL, what)
+    g = lse[sel.to(lse.device)].cpu().double().numpy()
+    fin = np.isfinite(rlse)
+    assert np.array_equal(np.isfinite(g), fin), what
+    assert_close(g[fin], rlse[fin], LSE_TOL, what + " lse")
+    assert torch.isfinite(out).all(), what + " non-finite output"
+
+
+@pytest.mark.parametrize("topk", [1, 65, 2047, 4500])
+def test_attn_bf16_128head_path_ragged_topk(topk):
+    import sparse_attention_kv_amd as hs
+    rows, H, kv_rows = 256, 128, 6000
+    if topk <= 2048:  # one split holds at most 2048 keys; longer lists always split
+        assert hs.hs_attn_workspace_bytes(rows, H, 576, 512, topk, torch.bfloat16) == 0
+    rng = np.random.default_rng(500 + topk)
+    q = _rand_bf16((rows, H, 576), 600 + topk)
+    kv = _rand_bf16((kv_rows, 576), 700 + topk)
+    idx = np.stack([rng.choice(kv_rows, topk, replace=False) for _ in range(rows)]).astype(np.int32)
+    idx[1, rng.random(topk) < 0.3] = -1
+    idx[2, rng.random(topk) < 0.2] = kv_rows + 7
+    idx[3, :] = -1
+    if topk > 1:
+        idx[4, :] = idx[4, 0]  # one key repeated
+    idx[199, : topk // 2] = -1  # leading padding
+    _check_sampled(q, kv, to_dev(idx), 1 / 24, 512, f"128-head ragged topk={topk}", _SAMPLE128)
+
+
+def test_attn_bf16_128head_path_zero_query_and_large_scores():
+    rows, H, kv_rows, topk = 256, 128, 3000, 700
+    rng = np.random.default_rng(88)
+    q = _rand_bf16((rows, H, 576), 89)
+    q[0] = 0   # uniform softmax
+    q[1] *= 8  # large scores: the reference maximum moves several times
+    q[2] *= 32
+    q[255] *= 16
+    kv = _rand_bf16((kv_rows, 576), 90)
+    idx = np.stack([rng.choice(kv_rows, topk, replace=False) for _ in range(rows)]).astype(np.int32)
+    _check_sampled(q, kv, to_dev(idx), 1 / 24, 512, "128-head zero query / large scores", _SAMPLE128)
 
 
 def test_attn_deterministic_and_index_order_invariant():
