@@ -43,9 +43,15 @@ constexpr int kPStride = tile::kTK * 2 + 16;  // P tile row stride in bytes (pad
 constexpr int kQSlots = kHG * tile::kRowBytes / 1024;  // 36 one-KiB DMA slots of Q per workgroup
 using namespace tile;
 
+// Tile layout: physical 16-byte chunk c holds (key c/72, logical part (c%72) ^ swz(key)).
+// Rows are 1152 bytes, so key bit 0 alone moves a chunk by half the 256-byte bank period.
+// A transposed PV read of a half wave touches keys k0 + {0..3} and four parts, and needs 16
+// distinct 16-byte bank slots: swz puts key bit 1 on part bit 2, which no lane of the half
+// varies.  Key bit 2 goes to part bit 1, which keeps the row-wise QK^T reads (lane octet
+// pairs (0,3), (1,2), (4,7), (5,6) of a 16-byte read share a cycle) conflict free too.
+__device__ __forceinline__ int swz(int key) { return ((key << 1) & 4) | ((key >> 1) & 2); }
+
 // Gather tile t (selected rows t*64 .. t*64+63 of the compacted list) into LDS buffer dst.
-// Layout: physical 16-byte chunk c holds (key c/72, logical part (c%72) ^ ((key>>1)&7)); the
-// XOR keeps the row-wise 16-byte reads (QK^T) and transposed 8-byte reads (PV) conflict free.
 // Keys past n_valid re-load the last valid row; their scores are masked to -inf.  Wave w
 // issues the 9 one-KiB slots n = 9w .. 9w+8 (lane l's chunk in slot n is c = 64n + l).
 template <int kFirst, int kCount>
@@ -60,7 +66,7 @@ __device__ __forceinline__ void gather_part(const uint8_t *__restrict__ kv, cons
     const int key = c / kRowChunks;
     const int kk = t * kTK + key;
     rows[i] = sidx[kk < last ? kk : last];
-    parts[i] = (c - key * kRowChunks) ^ ((key >> 1) & 7);
+    parts[i] = (c - key * kRowChunks) ^ swz(key);
   }
 #pragma unroll
   for (int i = 0; i < kCount; ++i) {
@@ -195,9 +201,9 @@ __global__ __launch_bounds__(kThreads8, 1) void attn_bf16_kernel(
       for (int nb = 0; nb < 2; ++nb) {
         const int part = voff[nb] >> 3, off = (voff[nb] & 7) * 2;
         vlo[buf][nb] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (HS_LDS s16x4 *)(cur + key0 * kRowBytes + ((part ^ ((key0 >> 1) & 7)) << 4) + off));
+            (HS_LDS s16x4 *)(cur + key0 * kRowBytes + ((part ^ swz(key0)) << 4) + off));
         vhi[buf][nb] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (HS_LDS s16x4 *)(cur + key1 * kRowBytes + ((part ^ ((key1 >> 1) & 7)) << 4) + off));
+            (HS_LDS s16x4 *)(cur + key1 * kRowBytes + ((part ^ swz(key1)) << 4) + off));
       }
     };
     load_step(0, 0);
@@ -238,7 +244,7 @@ __global__ __launch_bounds__(kThreads8, 1) void attn_bf16_kernel(
       {
         const int key = 16 * kq + (l & 15);
         const uint8_t *krow = cur + key * kRowBytes;
-        const int sw = (key >> 1) & 7;
+        const int sw = swz(key);
         constexpr int kB = 3;
         bf16x8 kf[2][kB];
 #pragma unroll
