@@ -319,9 +319,13 @@ def main():
                       device=dev)
     b = step.buf
 
+    # resolve + attention in one C-ABI call (positions are resolved in the attention
+    # prologue), its arguments marshalled once: the decode buffers stay at fixed addresses.
+    fused_call = hs.PagedAttnCall(q, kv, topk_pos, req_id, lim, bt, s.block_size, s.block_size,
+                                  s.scale, s.d_v, b.out, b.lse, b.workspace)
+
     def run_step():
-        # resolve + attention in one call: positions are resolved in the attention prologue
-        step.run_resident_fused(topk_pos, req_id, lim, bt, s.block_size, q, kv, s.scale)
+        fused_call()
 
     def run_step_two_calls():
         step.run_resident(topk_pos, req_id, lim, bt, s.block_size, q, kv, s.scale)
@@ -403,7 +407,7 @@ def main():
         "config": {"workload": "resident decode: 8 requests, seq_len U[6144,8192], 1 row each, "
                                "top-k 2048, block 64, 128 heads x 576/512 bf16 latent KV",
                    "rows_per_step": s.rows, "topk": s.topk, "heads": s.num_heads,
-                   "timing": "K eager steps on one stream between synchronisations",
+                   "timing": "K eager steps on one stream between synchronisations (one C-ABI call per step, arguments marshalled once)",
                    "eager_ms_per_step": eager_ms, "graph_ms_per_step": graph_ms,
                    "two_call_ms_per_step": two_call_ms,
                    "attn_split_workspace_bytes": plan_ws},

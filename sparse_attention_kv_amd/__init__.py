@@ -42,7 +42,7 @@ class HsHotState(ctypes.Structure):
 def _load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is missing: build it first "
-                          "(python -m sparse_attention_kv_amd.build)")
+                          "(python sparse_attention_kv_amd/build.py)")
     lib = ctypes.CDLL(LIB_PATH)
     i32, i64, vp, f32, sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p, ctypes.c_float, ctypes.c_size_t
     lib.hs_resolve_topk.argtypes = [vp, i32, i32, vp, vp, i32, vp, i32, i32, i32, vp, vp, vp]
@@ -193,13 +193,9 @@ def hs_sparse_decode_attn(q: torch.Tensor, kv: torch.Tensor, indices: torch.Tens
         _stream(stream)))
 
 
-def hs_sparse_decode_attn_paged(q: torch.Tensor, kv_pool: torch.Tensor, topk_pos: torch.Tensor,
-                                req_id: torch.Tensor, causal_limit: torch.Tensor,
-                                block_table: torch.Tensor, block_size: int,
-                                physical_block_stride: int, scale: float, d_v: int,
-                                out: torch.Tensor, lse: Optional[torch.Tensor] = None,
-                                workspace: Optional[torch.Tensor] = None, stream=None):
-    """Resolve + attention of a fully resident batch in one call (see include/hisparse.h)."""
+def _paged_args(q, kv_pool, topk_pos, req_id, causal_limit, block_table, block_size,
+                physical_block_stride, scale, d_v, out, lse, workspace):
+    """Checks and converts the arguments of hs_sparse_decode_attn_paged (all but the stream)."""
     i32 = torch.int32
     _dev(q, "q"); _dev(kv_pool, "kv_pool"); _dev(out, "out", q.dtype)
     _dev(topk_pos, "topk_pos", i32); _dev(req_id, "req_id", i32)
@@ -212,12 +208,47 @@ def hs_sparse_decode_attn_paged(q: torch.Tensor, kv_pool: torch.Tensor, topk_pos
         _dev(workspace, "workspace")
     rows, heads, d_qk = q.shape
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check("hs_sparse_decode_attn_paged", _lib.hs_sparse_decode_attn_paged(
-        _ptr(q), _ptr(kv_pool), kv_pool.shape[0], _ptr(topk_pos), _ptr(req_id),
-        _ptr(causal_limit), block_table.shape[0], _ptr(block_table), block_table.shape[1],
-        block_size, physical_block_stride, rows, heads, d_qk, d_v, topk_pos.shape[1],
-        float(scale), _dtype_code(q.dtype), _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes,
-        _stream(stream)))
+    return (_ptr(q), _ptr(kv_pool), kv_pool.shape[0], _ptr(topk_pos), _ptr(req_id),
+            _ptr(causal_limit), block_table.shape[0], _ptr(block_table), block_table.shape[1],
+            block_size, physical_block_stride, rows, heads, d_qk, d_v, topk_pos.shape[1],
+            float(scale), _dtype_code(q.dtype), _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes)
+
+
+def hs_sparse_decode_attn_paged(q: torch.Tensor, kv_pool: torch.Tensor, topk_pos: torch.Tensor,
+                                req_id: torch.Tensor, causal_limit: torch.Tensor,
+                                block_table: torch.Tensor, block_size: int,
+                                physical_block_stride: int, scale: float, d_v: int,
+                                out: torch.Tensor, lse: Optional[torch.Tensor] = None,
+                                workspace: Optional[torch.Tensor] = None, stream=None):
+    """Resolve + attention of a fully resident batch in one call (see include/hisparse.h)."""
+    args = _paged_args(q, kv_pool, topk_pos, req_id, causal_limit, block_table, block_size,
+                       physical_block_stride, scale, d_v, out, lse, workspace)
+    _check("hs_sparse_decode_attn_paged", _lib.hs_sparse_decode_attn_paged(*args, _stream(stream)))
+
+
+class PagedAttnCall:
+    """hs_sparse_decode_attn_paged with its arguments checked and marshalled once.
+
+    For callers whose decode buffers stay at fixed addresses from step to step: each call
+    passes the stored pointers and sizes, plus the current (or given) stream, to the same C
+    entry point.  The tensors are referenced here, so the stored pointers stay valid; their
+    contents may change between calls.
+    """
+
+    def __init__(self, q, kv_pool, topk_pos, req_id, causal_limit, block_table, block_size,
+                 physical_block_stride, scale, d_v, out, lse=None, workspace=None):
+        args = _paged_args(q, kv_pool, topk_pos, req_id, causal_limit, block_table, block_size,
+                           physical_block_stride, scale, d_v, out, lse, workspace)
+        types = _lib.hs_sparse_decode_attn_paged.argtypes
+        self._args = tuple(a if isinstance(a, ctypes.c_void_p) or a is None else t(a)
+                           for a, t in zip(args, types))
+        self._keep = (q, kv_pool, topk_pos, req_id, causal_limit, block_table, out, lse, workspace)
+        self._fn = _lib.hs_sparse_decode_attn_paged
+
+    def __call__(self, stream=None):
+        status = self._fn(*self._args, _stream(stream))
+        if status != HS_OK:
+            raise HsError("hs_sparse_decode_attn_paged", status, status_string(status))
 
 
 def hs_finalize_accepted(state: HotState, logits: torch.Tensor, draft_ids: torch.Tensor,

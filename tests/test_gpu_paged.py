@@ -97,6 +97,31 @@ def test_paged_fail_closed_cases(num_reqs, topk):
     assert torch.equal(lse, lse2)
 
 
+def test_prepared_call_matches_plain_call_and_follows_input_changes():
+    """PagedAttnCall forwards the same arguments: bit-identical to the plain call, and a
+    change to the inputs in place is seen by the next call."""
+    import sparse_attention_kv_amd as hs
+    s, w = make("resident", num_reqs=3, topk=500, seq_rule=("uniform", 900, 1500))
+    g = gpu_inputs(s, w)
+    q = g["q"]
+    rows, H, D = q.shape
+    wsb = hs.hs_attn_workspace_bytes(rows, H, D, 512, g["topk_pos"].shape[1], q.dtype)
+    ws = torch.empty((wsb,), dtype=torch.uint8, device=dev()) if wsb else None
+    out = torch.empty((rows, H, 512), dtype=q.dtype, device=dev())
+    lse = torch.empty((rows, H), dtype=torch.float32, device=dev())
+    call = hs.PagedAttnCall(q, w.kv_pool, g["topk_pos"], g["req_id"], g["causal_limit"],
+                            g["block_table"], s.block_size, s.block_size, s.scale, 512, out, lse, ws)
+    log("prepared paged call")
+    for step in range(2):
+        call()
+        torch.cuda.synchronize()
+        ref_out, ref_lse = _paged(q, w.kv_pool, g["topk_pos"], g["req_id"], g["causal_limit"],
+                                  g["block_table"], s.block_size, s.scale)
+        assert torch.equal(out, ref_out), step
+        assert torch.equal(lse, ref_lse), step
+        q.mul_(-0.5)  # new query values at the same address
+
+
 def test_paged_rejects_fp32_and_bad_sizes():
     import sparse_attention_kv_amd as hs
     q = torch.zeros((2, 4, 64), dtype=torch.float32, device=dev())
