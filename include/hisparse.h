@@ -241,6 +241,46 @@ hs_status hs_finalize_accepted(const hs_hot_state *st, const void *logits, int32
                                int32_t *out_argmax, int32_t *out_accept_len,
                                int32_t *out_next_token, void *stream);
 
+/*
+ * Device -> host backup of KV rows: the copy behind prefill staging and page spills.
+ * P3 "数据 back up": HiSparseWorker._enqueue_transfers turns page transfers into source
+ * slots (block id * kernel block size + offset, one list per cache) and destination host
+ * rows ((destination block * blocks per KV block + page offset) * kernel block size +
+ * offset), then launches hisparse_backup_layers, which copies those rows of every layer
+ * from the device cache into the pinned host cache, and records an event.  P1 "3.
+ * HiSparse staging": admit_request_into_staging backs a prefill's KV up to the host pool
+ * asynchronously; collect_ready_reqs polls that event before the request decodes.
+ *
+ * For layer l < num_layers and entry i < num_rows:
+ *   s = src_slots[(src_per_layer ? l * num_rows : 0) + i]    slot in the device cache
+ *   p = (s / src_block_size) * src_block_stride + s % src_block_size   its physical row
+ *   d = dst_rows[i]                                          row of the host cache
+ *   host_cache row (l * host_layer_rows + d) <- dev_cache row (l * dev_layer_rows + p),
+ *   row_bytes bytes, bit for bit.
+ * Entries with s < 0, d < 0, p >= dev_layer_rows or d >= host_layer_rows write nothing,
+ * so row lists may be padded with -1.  Nothing else of the host cache is written.
+ *
+ *   dev_cache    [num_layers * dev_layer_rows, row_bytes] bytes
+ *   host_cache   PINNED HOST [num_layers * host_layer_rows, row_bytes] bytes,
+ *                device-accessible; written by device stores over the host link
+ *   src_slots    [src_per_layer ? num_layers : 1, num_rows] int32
+ *   dst_rows     [num_rows] int32.  Its non-negative entries must be distinct (the
+ *                pages' planner gives every transfer its own host page).  With a
+ *                duplicate, each 16-byte part of that host row comes from one of its
+ *                sources, and the parts may come from different ones.
+ *
+ * Completion: the host rows hold the copies once the work queued on `stream` up to this
+ * call has finished (record an event after the call; poll or wait on it before the host
+ * reads them).  Returns HS_OK at once when num_rows == 0.
+ * Errors: HS_ERR_INVALID_ARG (null pointers, non-positive sizes, row_bytes not a multiple
+ * of 16, misaligned caches, host_cache not pinned, row counts beyond int32).
+ */
+hs_status hs_backup_rows(const void *dev_cache, int64_t dev_layer_rows, void *host_cache,
+                         int64_t host_layer_rows, int32_t num_layers, int32_t row_bytes,
+                         const int32_t *src_slots, int32_t src_per_layer,
+                         const int32_t *dst_rows, int32_t num_rows, int32_t src_block_size,
+                         int32_t src_block_stride, void *stream);
+
 /* Static description of a status code. */
 const char *hs_status_string(int32_t status);
 

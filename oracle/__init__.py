@@ -18,6 +18,8 @@ Sources (the three web pages the method is described on):
   ``HiSparseResidentSpec`` classes, the "数据 back up" section
   (``HiSparseWorker._enqueue_transfers`` address arithmetic) and
   ``build_offload_command`` / ``are_requests_fully_resident``.
+* P1 "3. HiSparse staging" and P3 "数据 back up" also describe the device -> host
+  backup of new KV rows (``plan_backup_rows``, ``backup_rows``).
 
 Every function is pinned by ``tests/test_oracle_*.py`` against things other than
 itself (worked example, closed forms, brute force, library routines).
@@ -25,10 +27,13 @@ itself (worked example, closed forms, brute force, library routines).
 
 from .hisparse_ref import (  # noqa: F401
     HotState,
+    PageTransfer,
     as_f64,
+    backup_rows,
     build_hot_state,
     finalize_accepted,
     greedy_accept,
+    plan_backup_rows,
     resolve_topk,
     sparse_decode_attn,
     swap_in,

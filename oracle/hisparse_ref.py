@@ -1,4 +1,4 @@
-"""Reference (oracle) implementation of the four HiSparse decode calls.
+"""Reference (oracle) implementation of the HiSparse decode calls and the host backup.
 
 TEST INFRASTRUCTURE: imported only by tests, the smoke check and the benchmark's
 CPU-baseline leg.  numpy only; float64 for every floating-point step.
@@ -314,3 +314,73 @@ def finalize_accepted(st: HotState, host_pool: np.ndarray, new_kv: np.ndarray,
             st.slot_stamp[b, v] = tick
         committed[b] = n + L + 1
     return committed
+
+
+# --------------------------------------------------------------------------------------
+# 5. device -> host backup (prefill staging, page spills)
+# --------------------------------------------------------------------------------------
+@dataclass
+class PageTransfer:
+    """One page spill as P3's ``SparseKVPageTransfer``: the source block of every cache
+    (``source_block_ids``), the destination host block and the page inside it."""
+    source_block_ids: tuple
+    destination_block_id: int
+    destination_page_offset: int
+
+
+def plan_backup_rows(transfers, kernel_block_size: int, blocks_per_kv_block: int,
+                     num_caches: int):
+    """Page transfers -> row lists, as P3 "数据 back up" (``HiSparseWorker._enqueue_transfers``)
+    fills its staging arrays.
+
+    Transfer ``t`` owns entries ``[t*kbs, (t+1)*kbs)``.  For cache ``c`` the source rows
+    are ``source_block_ids[c] * kbs + offset``; the host page is
+    ``destination_block_id * blocks_per_kv_block + destination_page_offset`` and the
+    destination rows are ``host_page * kbs + offset``, for ``offset`` in ``[0, kbs)``.
+    Returns ``(src [num_caches, n], dst [n])`` as int64.
+    """
+    kbs = kernel_block_size
+    n = len(transfers) * kbs
+    src = np.zeros((num_caches, n), dtype=np.int64)
+    dst = np.zeros(n, dtype=np.int64)
+    for t, tr in enumerate(transfers):
+        for off in range(kbs):
+            e = t * kbs + off
+            for c in range(num_caches):
+                src[c, e] = tr.source_block_ids[c] * kbs + off
+            host_page = tr.destination_block_id * blocks_per_kv_block + tr.destination_page_offset
+            dst[e] = host_page * kbs + off
+    return src, dst
+
+
+def backup_rows(dev_cache: np.ndarray, host_cache: np.ndarray, src_slots: np.ndarray,
+                dst_rows: np.ndarray, src_block_size: int = 1, src_block_stride: int = 1):
+    """Copy the listed device rows into the host cache, every layer; returns the new host cache.
+
+    P3 "数据 back up": the backup op copies, for each cache (layer), the rows named by the
+    source slot list into the host cache rows named by the destination list; the slot of
+    block ``b`` at offset ``o`` lives at physical row ``b * block_stride + o`` of the device
+    cache (the op takes the source block size and stride).  P1 "3. HiSparse staging": this
+    is how prefill KV reaches the host pool.
+
+    ``dev_cache`` [L, dev_rows, E] raw, ``host_cache`` [L, host_rows, E] raw (not modified),
+    ``src_slots`` [L, n] or [n] (shared by all layers), ``dst_rows`` [n].  Reading: an entry
+    whose slot or destination is negative or out of range is skipped; rows are copied bit
+    for bit; entries are applied in order (a repeated destination keeps the last source).
+    """
+    out = host_cache.copy()
+    L, dev_rows = dev_cache.shape[0], dev_cache.shape[1]
+    host_rows = host_cache.shape[1]
+    n = len(dst_rows)
+    per_layer = src_slots.ndim == 2
+    for layer in range(L):
+        for i in range(n):
+            s = int(src_slots[layer, i] if per_layer else src_slots[i])
+            d = int(dst_rows[i])
+            if s < 0 or d < 0 or d >= host_rows:
+                continue
+            p = (s // src_block_size) * src_block_stride + s % src_block_size
+            if p >= dev_rows:
+                continue
+            out[layer, d] = dev_cache[layer, p]
+    return out

@@ -22,7 +22,8 @@ HS_OK, HS_ERR_INVALID_ARG, HS_ERR_CAPACITY, HS_ERR_UNSUPPORTED, HS_ERR_HIP = 0, 
 HS_BF16, HS_F32 = 0, 1
 
 EXPORTED = ("hs_resolve_topk", "hs_swap_in", "hs_sparse_decode_attn", "hs_sparse_decode_attn_paged",
-            "hs_attn_workspace_bytes", "hs_finalize_accepted", "hs_status_string", "hs_version")
+            "hs_attn_workspace_bytes", "hs_finalize_accepted", "hs_backup_rows", "hs_status_string",
+            "hs_version")
 
 
 class HsError(RuntimeError):
@@ -61,6 +62,8 @@ def _load() -> ctypes.CDLL:
     lib.hs_finalize_accepted.argtypes = [ctypes.POINTER(HsHotState), vp, i32, vp, vp, i32, vp, vp,
                                          i32, i32, i32, vp, vp, vp, vp]
     lib.hs_finalize_accepted.restype = i32
+    lib.hs_backup_rows.argtypes = [vp, i64, vp, i64, i32, i32, vp, i32, vp, i32, i32, i32, vp]
+    lib.hs_backup_rows.restype = i32
     lib.hs_status_string.argtypes = [i32]
     lib.hs_status_string.restype = ctypes.c_char_p
     lib.hs_version.argtypes = []
@@ -267,3 +270,45 @@ def hs_finalize_accepted(state: HotState, logits: torch.Tensor, draft_ids: torch
         ctypes.byref(st), _ptr(logits), logits.shape[1], _ptr(draft_ids), _ptr(new_kv),
         rows_per_req, _ptr(seq_len), _ptr(block_table), block_table.shape[1], block_size, tick,
         _ptr(out_argmax), _ptr(out_accept_len), _ptr(out_next_token), _stream(stream)))
+
+
+def hs_backup_rows(dev_cache: torch.Tensor, host_cache: torch.Tensor, src_slots: torch.Tensor,
+                   dst_rows: torch.Tensor, src_block_size: int = 1, src_block_stride: int = 1,
+                   stream=None):
+    """Device -> host backup of KV rows (see include/hisparse.h).
+
+    ``dev_cache`` [layers, rows, elems] (or [rows, elems] for one layer) on the device;
+    ``host_cache`` pinned CPU tensor of the same dtype and layer count; ``src_slots``
+    int32 [layers, n] (one list per layer) or [n] (shared); ``dst_rows`` int32 [n].
+    """
+    _dev(dev_cache, "dev_cache"); _dev(src_slots, "src_slots", torch.int32)
+    _dev(dst_rows, "dst_rows", torch.int32)
+    if host_cache.is_cuda or not host_cache.is_pinned() or not host_cache.is_contiguous():
+        raise ValueError("host_cache must be a contiguous pinned host tensor")
+    if host_cache.dtype != dev_cache.dtype or host_cache.dim() != dev_cache.dim():
+        raise ValueError("host_cache must match dev_cache in dtype and rank")
+    if dev_cache.dim() == 2:
+        layers, dev_rows, elems = 1, dev_cache.shape[0], dev_cache.shape[1]
+        host_rows, host_elems = host_cache.shape
+    elif dev_cache.dim() == 3:
+        layers, dev_rows, elems = dev_cache.shape
+        host_layers, host_rows, host_elems = host_cache.shape
+        if host_layers != layers:
+            raise ValueError("host_cache and dev_cache differ in layer count")
+    else:
+        raise ValueError("dev_cache must be [rows, elems] or [layers, rows, elems]")
+    if host_elems != elems:
+        raise ValueError("host_cache and dev_cache rows differ in size")
+    n = dst_rows.shape[0]
+    if src_slots.dim() == 2:
+        if src_slots.shape != (layers, n):
+            raise ValueError("src_slots must be [layers, n] or [n]")
+        per_layer = 1
+    elif src_slots.dim() == 1 and src_slots.shape[0] == n:
+        per_layer = 0
+    else:
+        raise ValueError("src_slots must be [layers, n] or [n]")
+    _check("hs_backup_rows", _lib.hs_backup_rows(
+        _ptr(dev_cache), dev_rows, ctypes.c_void_p(host_cache.data_ptr()), host_rows, layers,
+        elems * dev_cache.element_size(), _ptr(src_slots), per_layer, _ptr(dst_rows), n,
+        src_block_size, src_block_stride, _stream(stream)))

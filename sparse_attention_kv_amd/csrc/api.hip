@@ -89,6 +89,33 @@ hs_status hs_swap_in(const hs_hot_state *st, const int32_t *wave_rows, int32_t t
                                      out_miss_pos, static_cast<hipStream_t>(stream)));
 }
 
+hs_status hs_backup_rows(const void *dev_cache, int64_t dev_layer_rows, void *host_cache,
+                         int64_t host_layer_rows, int32_t num_layers, int32_t row_bytes,
+                         const int32_t *src_slots, int32_t src_per_layer,
+                         const int32_t *dst_rows, int32_t num_rows, int32_t src_block_size,
+                         int32_t src_block_stride, void *stream) {
+  if (num_rows < 0 || num_layers <= 0 || row_bytes <= 0 || row_bytes % 16 != 0 ||
+      dev_layer_rows <= 0 || host_layer_rows <= 0 || src_block_size <= 0 || src_block_stride <= 0)
+    return HS_ERR_INVALID_ARG;
+  if (num_rows == 0) return HS_OK;
+  if (!dev_cache || !host_cache || !src_slots || !dst_rows) return HS_ERR_INVALID_ARG;
+  if (dev_layer_rows > 0x7fffffffLL || host_layer_rows > 0x7fffffffLL) return HS_ERR_INVALID_ARG;
+  if (!aligned16(dev_cache) || !aligned16(host_cache)) return HS_ERR_INVALID_ARG;
+  const void *host_dev = nullptr;
+  hs_status s = device_view(host_cache, &host_dev);
+  if (s != HS_OK) return s;
+  hipPointerAttribute_t attr;
+  std::memset(&attr, 0, sizeof(attr));
+  if (hipPointerGetAttributes(&attr, host_cache) != hipSuccess || attr.type != hipMemoryTypeHost) {
+    (void)hipGetLastError();
+    return HS_ERR_INVALID_ARG;  // the destination must be the pinned host cache
+  }
+  return from_hip(hs::launch_backup_rows(dev_cache, dev_layer_rows, const_cast<void *>(host_dev),
+                                         host_layer_rows, num_layers, row_bytes, src_slots,
+                                         src_per_layer, dst_rows, num_rows, src_block_size,
+                                         src_block_stride, static_cast<hipStream_t>(stream)));
+}
+
 size_t hs_attn_workspace_bytes(int32_t num_rows, int32_t num_heads, int32_t d_qk, int32_t d_v,
                                int32_t topk, int32_t dtype) {
   if (dtype != HS_BF16 || num_rows <= 0 || topk <= 0 || num_heads <= 0 || num_heads % 32 != 0 ||

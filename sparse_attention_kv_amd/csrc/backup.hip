@@ -1,0 +1,81 @@
+// backup_rows: device -> host copy of KV rows (gfx950).
+//
+// P3 "vllm 分析（十二）——Hisparse下篇", "数据 back up": the worker turns page transfers into
+// per-cache source slots and host destination rows and launches a multi-layer backup op
+// that copies those rows from the device cache into the pinned host cache; an event marks
+// completion.  P1 "hiSparse-MTP", "3. HiSparse staging": the prefill KV is backed up to the
+// host pool asynchronously and the request decodes once that event has fired.
+//
+// The copy is a zero-copy scatter: every thread reads 16-byte chunks of source rows from
+// HBM and writes them with vector stores straight into the pinned host cache through its
+// device mapping.  Chunks are numbered (layer, entry, chunk of row) so that consecutive
+// lanes write consecutive 16 bytes of one host row and a wave's stores form whole lines
+// on the host link.  Each thread keeps kUnroll chunk loads in flight before it stores.
+
+#include <algorithm>
+
+#include "common.h"
+
+namespace hs {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kUnroll = 8;
+constexpr int kMaxBlocks = 2048;
+
+__global__ __launch_bounds__(kThreads) void backup_rows_kernel(
+    const uint8_t *__restrict__ dev_cache, int64_t dev_layer_rows, uint8_t *__restrict__ host_cache,
+    int64_t host_layer_rows, int32_t row_bytes, const int32_t *__restrict__ src_slots,
+    int32_t src_per_layer, const int32_t *__restrict__ dst_rows, int32_t num_rows,
+    int32_t src_block_size, int32_t src_block_stride, int64_t total_chunks) {
+  const int chunks = row_bytes >> 4;
+  const int64_t stride = (int64_t)gridDim.x * kThreads * kUnroll;
+  for (int64_t base = (int64_t)blockIdx.x * kThreads * kUnroll + threadIdx.x; base < total_chunks;
+       base += stride) {
+    i32x4 v[kUnroll];
+    int64_t dst[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int64_t c = base + (int64_t)u * kThreads;
+      dst[u] = -1;
+      if (c < total_chunks) {
+        const int64_t r = c / chunks;  // (layer, entry) pair
+        const int part = (int)(c - r * chunks);
+        const int layer = (int)(r / num_rows);
+        const int i = (int)(r - (int64_t)layer * num_rows);
+        const int s = src_slots[(src_per_layer ? (int64_t)layer * num_rows : 0) + i];
+        const int d = dst_rows[i];
+        if (s >= 0 && d >= 0 && d < host_layer_rows) {
+          const int64_t p = (int64_t)(s / src_block_size) * src_block_stride + s % src_block_size;
+          if (p < dev_layer_rows) {
+            v[u] = *reinterpret_cast<const i32x4 *>(
+                dev_cache + ((int64_t)layer * dev_layer_rows + p) * row_bytes + part * 16);
+            dst[u] = ((int64_t)layer * host_layer_rows + d) * row_bytes + part * 16;
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u)
+      if (dst[u] >= 0) *reinterpret_cast<i32x4 *>(host_cache + dst[u]) = v[u];
+  }
+}
+
+}  // namespace
+
+hipError_t launch_backup_rows(const void *dev_cache, int64_t dev_layer_rows, void *host_cache_dev,
+                              int64_t host_layer_rows, int32_t num_layers, int32_t row_bytes,
+                              const int32_t *src_slots, int32_t src_per_layer,
+                              const int32_t *dst_rows, int32_t num_rows, int32_t src_block_size,
+                              int32_t src_block_stride, hipStream_t stream) {
+  const int64_t total = (int64_t)num_layers * num_rows * (row_bytes >> 4);
+  const int64_t per_block = (int64_t)kThreads * kUnroll;
+  const int blocks = (int)std::min<int64_t>((total + per_block - 1) / per_block, kMaxBlocks);
+  hipLaunchKernelGGL(backup_rows_kernel, dim3(blocks), dim3(kThreads), 0, stream,
+                     static_cast<const uint8_t *>(dev_cache), dev_layer_rows,
+                     static_cast<uint8_t *>(host_cache_dev), host_layer_rows, row_bytes, src_slots,
+                     src_per_layer, dst_rows, num_rows, src_block_size, src_block_stride, total);
+  return hipGetLastError();
+}
+
+}  // namespace hs

@@ -76,6 +76,13 @@ hipError_t launch_finalize(const hs_hot_state &st, const void *host_pool_dev, co
                            int32_t bt_stride, int32_t block_size, int32_t tick, int32_t *out_argmax,
                            int32_t *out_accept_len, int32_t *out_next_token, hipStream_t stream);
 
+// Device -> host row backup; host_cache_dev is the pinned host cache's device address.
+hipError_t launch_backup_rows(const void *dev_cache, int64_t dev_layer_rows, void *host_cache_dev,
+                              int64_t host_layer_rows, int32_t num_layers, int32_t row_bytes,
+                              const int32_t *src_slots, int32_t src_per_layer,
+                              const int32_t *dst_rows, int32_t num_rows, int32_t src_block_size,
+                              int32_t src_block_stride, hipStream_t stream);
+
 // ---- small device helpers ----
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 

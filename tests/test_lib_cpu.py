@@ -121,3 +121,33 @@ def test_finalize_validation():
     assert lib.hs_finalize_accepted(*args(R=25)) == hs.HS_ERR_INVALID_ARG   # > capacity
     big = _state(hs, capacity=200)
     assert lib.hs_finalize_accepted(*args(st=big, R=65)) == hs.HS_ERR_UNSUPPORTED
+
+
+def test_backup_validation():
+    hs, lib = _lib()
+    f = lib.hs_backup_rows
+    P = 4096  # fake non-null, 16-byte aligned pointers (never dereferenced on these paths)
+    ok = dict(dev=P, dev_rows=10, host=P, host_rows=10, layers=1, row_bytes=1152, src=P,
+              per_layer=0, dst=P, n=4, bs=1, stride=1)
+
+    def call(**kw):
+        a = {**ok, **kw}
+        return f(a["dev"], a["dev_rows"], a["host"], a["host_rows"], a["layers"], a["row_bytes"],
+                 a["src"], a["per_layer"], a["dst"], a["n"], a["bs"], a["stride"], None)
+
+    assert call(n=0) == hs.HS_OK  # nothing to copy: returns before any HIP call
+    bad = hs.HS_ERR_INVALID_ARG
+    assert call(n=-1) == bad
+    assert call(layers=0) == bad
+    assert call(row_bytes=12) == bad
+    assert call(row_bytes=0) == bad
+    assert call(dev_rows=0) == bad
+    assert call(host_rows=0) == bad
+    assert call(bs=0) == bad
+    assert call(stride=0) == bad
+    assert call(dev=None) == bad
+    assert call(host=None) == bad
+    assert call(src=None) == bad
+    assert call(dst=None) == bad
+    assert call(dev_rows=1 << 31) == bad
+    assert call(dev=P + 8) == bad  # misaligned
