@@ -278,6 +278,66 @@ def measure_finalize(dev, reps=10):
     }
 
 
+def measure_backup(dev, reps=5):
+    """Device -> host backup of prefill KV (staging): 8 requests x 4096 prompt tokens in
+    pages of 64 rows, 4 layers of 576 bf16 latent rows -> 512 page transfers, 131072 rows,
+    151 MB over the host link.  Device cache 4 x 65536 rows, pinned host cache 4 x 65536
+    rows (302 MB each).  Timed: the backup kernel alone (index lists already on the device)
+    and the whole BackupStager enqueue (host planning, index copies, kernel), against a
+    device -> pinned copy of the same byte count."""
+    import numpy as np
+    import torch
+
+    import sparse_attention_kv_amd as hs
+    from sparse_attention_kv_amd.pipeline import BackupStager, PageTransfer
+
+    L, kbs, per, dev_blocks, host_blocks, pages = 4, 64, 4, 1024, 256, 512
+    rows_per_layer = dev_blocks * kbs
+    dev_cache = torch.randn((L, rows_per_layer, 576), device=dev).to(torch.bfloat16)
+    host_cache = torch.empty((L, host_blocks * per * kbs, 576), dtype=torch.bfloat16,
+                             pin_memory=True)
+    rng = np.random.default_rng(0)
+    src_blocks = rng.permutation(dev_blocks)[:pages]
+    host_pages = rng.permutation(host_blocks * per)[:pages]
+    transfers = [PageTransfer((int(src_blocks[i]),) * L, int(host_pages[i]) // per,
+                              int(host_pages[i]) % per) for i in range(pages)]
+    n = pages * kbs
+    off = np.arange(kbs)
+    src = torch.as_tensor((src_blocks[:, None] * kbs + off).reshape(n).astype(np.int32), device=dev)
+    dst = torch.as_tensor((host_pages[:, None] * kbs + off).reshape(n).astype(np.int32), device=dev)
+    nbytes = L * n * 1152
+    main_s = torch.cuda.current_stream()
+
+    def timed(fn):
+        times = []
+        for rep in range(reps + 2):
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(main_s)
+            fn()
+            e1.record(main_s)
+            torch.cuda.synchronize()
+            if rep >= 2:
+                times.append(e0.elapsed_time(e1) * 1e3)
+        return float(np.median(times))
+
+    kern_us = timed(lambda: hs.hs_backup_rows(dev_cache, host_cache, src, dst))
+    stager = BackupStager(dev_cache, host_cache, kbs, per, max_pages=pages)
+    stage_us = timed(lambda: stager.enqueue(transfers))
+    flat_dev = dev_cache.view(-1)[: nbytes // 2]
+    flat_host = host_cache.view(-1)[: nbytes // 2]
+    copy_us = timed(lambda: flat_host.copy_(flat_dev, non_blocking=True))
+    b_d2h = nbytes / (copy_us / 1e6) / 1e9
+    gbs = nbytes / (kern_us / 1e6) / 1e9
+    return {
+        "workload": "prefill staging backup: 8 requests x 4096 tokens, 512 pages of 64 rows, "
+                    "4 layers of 1152-B rows, device -> pinned host",
+        "rows": L * n, "bytes": nbytes, "kernel_us": kern_us, "kernel_GBps": gbs,
+        "stager_us": stage_us, "stager_GBps": nbytes / (stage_us / 1e6) / 1e9,
+        "memcpy_device_to_pinned_GBps": b_d2h, "kernel_frac_of_memcpy": gbs / b_d2h,
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -424,6 +484,8 @@ def main():
         res["swap_in"] = measure_swap(dev)
         log("finalize")
         res["finalize"] = measure_finalize(dev)
+        log("backup")
+        res["backup"] = measure_backup(dev)
     if not args.no_cpu:
         log("cpu baseline (oracle)")
         res["cpu_baseline"] = cpu_baseline(w, s)

@@ -14,17 +14,22 @@ resident batch reads the paged device cache directly, otherwise KV is swapped in
 The copy stream waits for the attention of wave r-2 before swapping wave r (victims of
 wave r are never slots wave r-1 used when capacity >= 2*topk); with a smaller hot
 buffer it waits for wave r-1.  Both streams run at the default priority.
+
+Backup (P1 "3. HiSparse staging", P3 "数据 back up"): BackupStager turns page transfers
+into row lists in pinned staging buffers, copies them to the device without blocking,
+launches hs_backup_rows and records an event that `ready` polls.
 """
 
 from __future__ import annotations
 
 from dataclasses import dataclass
-from typing import Optional
+from typing import Optional, Sequence
 
+import numpy as np
 import torch
 
-from . import (HotState, hs_attn_workspace_bytes, hs_finalize_accepted, hs_resolve_topk,
-               hs_sparse_decode_attn, hs_sparse_decode_attn_paged, hs_swap_in)
+from . import (HotState, hs_attn_workspace_bytes, hs_backup_rows, hs_finalize_accepted,
+               hs_resolve_topk, hs_sparse_decode_attn, hs_sparse_decode_attn_paged, hs_swap_in)
 
 
 def build_hot_state(init_pos: torch.Tensor, init_stamp: torch.Tensor, seq_len: torch.Tensor,
@@ -150,3 +155,88 @@ class DecodeStep:
                                  finalize["new_kv"], R, finalize["seq_len"], block_table,
                                  block_size, tick0 + R, b.argmax, b.accept_len, b.next_token,
                                  stream=main)
+
+
+
+@dataclass
+class PageTransfer:
+    """One page to back up: the source block of every cache (layer), the destination host
+    block and the page inside it (P3's SparseKVPageTransfer fields)."""
+    source_block_ids: Sequence[int]
+    destination_block_id: int
+    destination_page_offset: int
+
+
+class BackupStager:
+    """Device -> host backup of whole pages, as P3's HiSparseWorker._enqueue_transfers.
+
+    The control plane stays on the host, as on the pages.  Row lists are written into one
+    of two pinned staging buffers: a buffer is reused only after the event recorded after
+    its device copy has fired.  The lists are copied to the device with non-blocking
+    copies, hs_backup_rows copies the rows of every layer on the same stream, and an
+    event is recorded after it.  ``ready(ticket)`` polls that event
+    (P1 "3. HiSparse staging": collect_ready_reqs waits on the backup event).
+    """
+
+    def __init__(self, dev_cache: torch.Tensor, host_cache: torch.Tensor, kernel_block_size: int,
+                 blocks_per_kv_block: int, max_pages: int, src_block_size: int = 1,
+                 src_block_stride: int = 1):
+        self.dev_cache, self.host_cache = dev_cache, host_cache
+        self.layers = dev_cache.shape[0] if dev_cache.dim() == 3 else 1
+        self.kbs, self.per = kernel_block_size, blocks_per_kv_block
+        self.src_bs, self.src_stride = src_block_size, src_block_stride
+        n = max_pages * kernel_block_size
+        dev = dev_cache.device
+        # flat buffers: the first layers * n entries are viewed as [layers, n] per call
+        self._src_cpu = [torch.empty((self.layers * n,), dtype=torch.int32, pin_memory=True)
+                         for _ in range(2)]
+        self._dst_cpu = [torch.empty((n,), dtype=torch.int32, pin_memory=True) for _ in range(2)]
+        self._staging_done = [None, None]
+        self._src_dev = torch.empty((self.layers * n,), dtype=torch.int32, device=dev)
+        self._dst_dev = torch.empty((n,), dtype=torch.int32, device=dev)
+        self._next = 0
+        self.max_pages = max_pages
+
+    def enqueue(self, transfers: Sequence[PageTransfer], stream=None) -> torch.cuda.Event:
+        """Queue the backup of `transfers`; returns the event that marks the host rows
+        written."""
+        if not transfers:
+            ev = torch.cuda.Event()
+            ev.record(stream)
+            return ev
+        if len(transfers) > self.max_pages:
+            raise ValueError(f"{len(transfers)} pages exceed the stager's {self.max_pages}")
+        i = self._next
+        self._next ^= 1
+        if self._staging_done[i] is not None:
+            self._staging_done[i].synchronize()  # the copy that last read this buffer is done
+        kbs, n = self.kbs, len(transfers) * self.kbs
+        off = np.arange(kbs, dtype=np.int64)
+        src_blocks = np.array([t.source_block_ids for t in transfers], dtype=np.int64)  # [P, L]
+        if src_blocks.shape[1] != self.layers:
+            raise ValueError("each transfer needs one source block per layer")
+        host_pages = np.array([t.destination_block_id * self.per + t.destination_page_offset
+                               for t in transfers], dtype=np.int64)
+        m = self.layers * n
+        src = self._src_cpu[i].numpy()
+        dst = self._dst_cpu[i].numpy()
+        src[:m] = (src_blocks.T[:, :, None] * kbs + off).reshape(m)  # layer-major
+        dst[:n] = (host_pages[:, None] * kbs + off).reshape(n)
+        s = torch.cuda.current_stream() if stream is None else stream
+        with torch.cuda.stream(s):
+            self._src_dev[:m].copy_(self._src_cpu[i][:m], non_blocking=True)
+            self._dst_dev[:n].copy_(self._dst_cpu[i][:n], non_blocking=True)
+            staged = torch.cuda.Event()
+            staged.record(s)
+            self._staging_done[i] = staged
+            src_dev = self._src_dev[:m].view(self.layers, n) if self.layers > 1 else self._src_dev[:n]
+            hs_backup_rows(self.dev_cache, self.host_cache, src_dev, self._dst_dev[:n], self.src_bs,
+                           self.src_stride, stream=s)
+            written = torch.cuda.Event()
+            written.record(s)
+        return written
+
+    @staticmethod
+    def ready(written: torch.cuda.Event) -> bool:
+        """True once the host rows of that enqueue hold the copies (non-blocking poll)."""
+        return written.query()

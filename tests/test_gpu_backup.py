@@ -147,3 +147,35 @@ def test_backup_rejects_bad_arguments():
                                 idx.data_ptr(), 2, 1, 1, None)
         hs._check("hs_backup_rows", st)
     assert e.value.status == hs.HS_ERR_INVALID_ARG
+
+
+def test_stager_pages_match_oracle_plan_and_copy():
+    """BackupStager (host planning, pinned staging, async index copies, backup kernel,
+    event) against the oracle's plan_backup_rows + backup_rows, over three enqueues so the
+    two staging buffers are reused."""
+    from sparse_attention_kv_amd.pipeline import BackupStager, PageTransfer
+    rng = np.random.default_rng(17)
+    L, kbs, per, dev_blocks, host_blocks = 3, 64, 4, 40, 10
+    dev_np = rng.integers(0, 2 ** 16, size=(L, dev_blocks * kbs, 576), dtype=np.uint16)
+    host_np = rng.integers(0, 2 ** 16, size=(L, host_blocks * per * kbs, 576), dtype=np.uint16)
+    dev_t = torch.from_numpy(dev_np.view(np.int16)).view(torch.bfloat16).to(dev())
+    host_t = _pinned_like(host_np, torch.bfloat16)
+    stager = BackupStager(dev_t, host_t, kbs, per, max_pages=8)
+    pages = [(hb, po) for hb in range(host_blocks) for po in range(per)]
+    order = rng.permutation(len(pages))
+    ref = host_np
+    events = []
+    for call in range(3):
+        chosen = [pages[k] for k in order[call * 6:(call + 1) * 6]]
+        trs = [PageTransfer(tuple(int(x) for x in rng.integers(0, dev_blocks, size=L)), hb, po)
+               for hb, po in chosen]
+        events.append(stager.enqueue(trs))
+        otr = [oracle.PageTransfer(tuple(t.source_block_ids), t.destination_block_id,
+                                   t.destination_page_offset) for t in trs]
+        src, dst = oracle.plan_backup_rows(otr, kbs, per, L)
+        ref = oracle.backup_rows(dev_np, ref, src, dst)
+    log("backup stager")
+    while not BackupStager.ready(events[-1]):
+        pass
+    assert all(BackupStager.ready(e) for e in events)
+    assert np.array_equal(raw(host_t), ref)
