@@ -199,6 +199,36 @@ def measure_swap(dev, reps=5):
         wave_bytes.append(int(b.miss_count[r].sum().item()) * row_bytes)
     warm_gbs = sum(wave_bytes) / (sum(wave_us) / 1e6) / 1e9
 
+    # plan reuse: the leader's swap plan applied to 2 follower layers (own hot buffers and
+    # pinned host pools, same slot assignment), wave by wave from the same starting state
+    C = 2
+    host_rows = w.kv_pool.shape[0]
+    f_hot = torch.empty((C, s.num_reqs * s.capacity, s.d_qk), dtype=torch.bfloat16, device=dev)
+    f_pool = torch.empty((C, host_rows, s.d_qk), dtype=torch.bfloat16, pin_memory=True)
+    mpos = torch.empty((s.num_reqs, s.topk), dtype=torch.int32, device=dev)
+    for r in range(s.rows_per_req):  # untimed pass: the GPU's first touch of the new pools
+        lo, hi = r * s.num_reqs, (r + 1) * s.num_reqs
+        hs.hs_swap_in(st, b.slots[lo:hi], s.tick0 + r, b.hot_idx[lo:hi], b.miss_count[r], mpos)
+        hs.hs_apply_plan(f_hot, f_pool, b.slots[lo:hi], b.hot_idx[lo:hi], b.miss_count[r], mpos,
+                         s.capacity)
+    restore()
+    torch.cuda.synchronize()
+    lead_us, apply_us = [], []
+    for r in range(s.rows_per_req):
+        lo, hi = r * s.num_reqs, (r + 1) * s.num_reqs
+        a, m, z = ev(), ev(), ev()
+        a.record(main)
+        hs.hs_swap_in(st, b.slots[lo:hi], s.tick0 + r, b.hot_idx[lo:hi], b.miss_count[r], mpos)
+        m.record(main)
+        hs.hs_apply_plan(f_hot, f_pool, b.slots[lo:hi], b.hot_idx[lo:hi], b.miss_count[r], mpos,
+                         s.capacity)
+        z.record(main)
+        torch.cuda.synchronize()
+        lead_us.append(a.elapsed_time(m) * 1e3)
+        apply_us.append(m.elapsed_time(z) * 1e3)
+    apply_gbs = C * sum(wave_bytes) / (sum(apply_us) / 1e6) / 1e9
+    del f_hot, f_pool
+
     # cold wave: empty hot buffer, every selected row is a miss (streaming zero-copy read)
     st.slot_loc.fill_(-1)
     st.slot_stamp.fill_(-1)
@@ -220,6 +250,8 @@ def measure_swap(dev, reps=5):
         "swap_waves_us": wave_us, "swap_miss_bytes": wave_bytes,
         "swap_GBps": warm_gbs, "swap_frac_of_B_host": warm_gbs / b_host,
         "cold_wave_us": cold_us, "cold_wave_bytes": cold_bytes, "cold_wave_GBps": cold_gbs,
+        "plan_reuse": {"followers": C, "leader_swap_us": lead_us, "apply_plan_us": apply_us,
+                       "apply_GBps": apply_gbs, "apply_frac_of_B_host": apply_gbs / b_host},
     }
 
 

@@ -146,6 +146,38 @@ hs_status hs_swap_in(const hs_hot_state *st, const int32_t *wave_rows, int32_t t
                      void *stream);
 
 /*
+ * hs_apply_plan -- P3 resolve_topk listing: a runtime that has a leader does not swap
+ * on its own but applies the leader's plan (apply_plan); the leader's swap_in produces
+ * that plan for its followers and, with prefetch_followers, fills their caches too.
+ * Here the plan is what hs_swap_in returned for one wave: the hot index of every entry
+ * and, per request, the entries that missed.  A follower cache (another layer, same
+ * slot assignment) then needs only the missed rows copied from its own host pool into
+ * its own hot buffer; classification and victim choice are not repeated.
+ *
+ * For cache c < num_caches, request b and m < miss_count[b]:
+ *   e = miss_pos[b, m],  row = wave_rows[b, e],  g = hot_idx[b, e]
+ *   hot_kv[c, g] <- host_pool[c, row]   (row_bytes bytes, bit for bit)
+ * Entries whose e, row or g is out of range write nothing.
+ *
+ *   hot_kv     [num_caches, num_reqs*capacity, row_bytes] bytes, the followers' hot buffers
+ *   host_pool  PINNED HOST [num_caches, host_rows, row_bytes] bytes, device-accessible
+ *   wave_rows, hot_idx, miss_pos  [num_reqs, topk] int32; miss_count [num_reqs] int32:
+ *              the leader's hs_swap_in input and outputs for the wave (miss_pos required)
+ *
+ * Afterwards each follower's hot_kv[c, s] equals host_pool[c, slot_loc[s]] for the slots
+ * the wave filled, so attention over layer c can use hot_idx as it is.  Plan rows for a
+ * subset of query rows (the pages' plan_row_offset) are passed by offsetting the
+ * pointers.  Runs on `stream` after the leader's swap (order them with the stream or an
+ * event).
+ * Errors: HS_ERR_INVALID_ARG (null pointers, non-positive sizes, row_bytes not a multiple
+ * of 16, misaligned buffers, host_pool not pinned, counts beyond int32 rows).
+ */
+hs_status hs_apply_plan(void *hot_kv, const void *host_pool, int64_t host_rows,
+                        int32_t num_caches, int32_t num_reqs, int32_t capacity, int32_t row_bytes,
+                        const int32_t *wave_rows, int32_t topk, const int32_t *hot_idx,
+                        const int32_t *miss_count, const int32_t *miss_pos, void *stream);
+
+/*
  * hs_sparse_decode_attn -- P1 startup: the DSA attention backend reads KV through
  * HiSparse; P3 resolve_topk: attention receives the cache and per-row indices.  For each
  * row i and head h, over S_i = {j : 0 <= indices[i,j] < kv_rows}:

@@ -180,6 +180,37 @@ def swap_in(st: HotState, wave_rows: np.ndarray, tick: int, host_pool: np.ndarra
     return hot_idx, miss_count, miss_pos
 
 
+def apply_plan(hot_kv: np.ndarray, host_pool: np.ndarray, wave_rows: np.ndarray,
+               hot_idx: np.ndarray, miss_count: np.ndarray, miss_pos: np.ndarray):
+    """A follower cache applies the leader's swap plan; returns its new hot buffers.
+
+    P3 ``resolve_topk`` listing: a runtime with a leader returns ``apply_plan(...)``
+    instead of swapping itself; the leader's ``swap_in`` produces the plan for its
+    followers (and with ``prefetch_followers`` fills them).  Reading: the plan of one wave
+    is the leader's ``(hot_idx, miss_count, miss_pos)``; a follower shares the slot
+    assignment but has its own hot buffer and host pool, so for every cache ``c``, request
+    ``b`` and ``m < miss_count[b]``, with ``e = miss_pos[b, m]``, row ``wave_rows[b, e]``
+    of ``host_pool[c]`` is copied bitwise to row ``hot_idx[b, e]`` of ``hot_kv[c]``.
+    Entries out of range are skipped.
+
+    ``hot_kv`` [C, B*cap, E] raw (not modified), ``host_pool`` [C, host_rows, E] raw.
+    """
+    out = hot_kv.copy()
+    C, hot_rows = hot_kv.shape[0], hot_kv.shape[1]
+    host_rows = host_pool.shape[1]
+    B, K = wave_rows.shape
+    for c in range(C):
+        for b in range(B):
+            for m in range(min(max(int(miss_count[b]), 0), K)):
+                e = int(miss_pos[b, m])
+                if e < 0 or e >= K:
+                    continue
+                row, g = int(wave_rows[b, e]), int(hot_idx[b, e])
+                if 0 <= row < host_rows and 0 <= g < hot_rows:
+                    out[c, g] = host_pool[c, row]
+    return out
+
+
 # --------------------------------------------------------------------------------------
 # 3. sparse decode attention
 # --------------------------------------------------------------------------------------

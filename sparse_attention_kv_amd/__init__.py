@@ -22,8 +22,8 @@ HS_OK, HS_ERR_INVALID_ARG, HS_ERR_CAPACITY, HS_ERR_UNSUPPORTED, HS_ERR_HIP = 0, 
 HS_BF16, HS_F32 = 0, 1
 
 EXPORTED = ("hs_resolve_topk", "hs_swap_in", "hs_sparse_decode_attn", "hs_sparse_decode_attn_paged",
-            "hs_attn_workspace_bytes", "hs_finalize_accepted", "hs_backup_rows", "hs_status_string",
-            "hs_version")
+            "hs_attn_workspace_bytes", "hs_finalize_accepted", "hs_backup_rows", "hs_apply_plan",
+            "hs_status_string", "hs_version")
 
 
 class HsError(RuntimeError):
@@ -64,6 +64,8 @@ def _load() -> ctypes.CDLL:
     lib.hs_finalize_accepted.restype = i32
     lib.hs_backup_rows.argtypes = [vp, i64, vp, i64, i32, i32, vp, i32, vp, i32, i32, i32, vp]
     lib.hs_backup_rows.restype = i32
+    lib.hs_apply_plan.argtypes = [vp, vp, i64, i32, i32, i32, i32, vp, i32, vp, vp, vp, vp]
+    lib.hs_apply_plan.restype = i32
     lib.hs_status_string.argtypes = [i32]
     lib.hs_status_string.restype = ctypes.c_char_p
     lib.hs_version.argtypes = []
@@ -312,3 +314,45 @@ def hs_backup_rows(dev_cache: torch.Tensor, host_cache: torch.Tensor, src_slots:
         _ptr(dev_cache), dev_rows, ctypes.c_void_p(host_cache.data_ptr()), host_rows, layers,
         elems * dev_cache.element_size(), _ptr(src_slots), per_layer, _ptr(dst_rows), n,
         src_block_size, src_block_stride, _stream(stream)))
+
+
+
+def hs_apply_plan(hot_kv: torch.Tensor, host_pool: torch.Tensor, wave_rows: torch.Tensor,
+                  hot_idx: torch.Tensor, miss_count: torch.Tensor, miss_pos: torch.Tensor,
+                  capacity: int, stream=None):
+    """Fill follower caches from the leader's swap plan (see include/hisparse.h).
+
+    ``hot_kv`` [caches, num_reqs*capacity, elems] (or [num_reqs*capacity, elems]) on the
+    device; ``host_pool`` pinned [caches, host_rows, elems] (or 2-D) of the same dtype;
+    ``wave_rows``, ``hot_idx``, ``miss_pos`` int32 [num_reqs, topk] and ``miss_count``
+    int32 [num_reqs]: the leader's hs_swap_in input and outputs.
+    """
+    i32 = torch.int32
+    _dev(hot_kv, "hot_kv"); _dev(wave_rows, "wave_rows", i32); _dev(hot_idx, "hot_idx", i32)
+    _dev(miss_count, "miss_count", i32); _dev(miss_pos, "miss_pos", i32)
+    if host_pool.is_cuda or not host_pool.is_pinned() or not host_pool.is_contiguous():
+        raise ValueError("host_pool must be a contiguous pinned host tensor")
+    if host_pool.dtype != hot_kv.dtype or host_pool.dim() != hot_kv.dim():
+        raise ValueError("host_pool must match hot_kv in dtype and rank")
+    if hot_kv.dim() == 2:
+        caches, elems, host_rows = 1, hot_kv.shape[1], host_pool.shape[0]
+        host_elems = host_pool.shape[1]
+    elif hot_kv.dim() == 3:
+        caches, elems = hot_kv.shape[0], hot_kv.shape[2]
+        if host_pool.shape[0] != caches:
+            raise ValueError("host_pool and hot_kv differ in cache count")
+        host_rows, host_elems = host_pool.shape[1], host_pool.shape[2]
+    else:
+        raise ValueError("hot_kv must be [rows, elems] or [caches, rows, elems]")
+    if host_elems != elems:
+        raise ValueError("host_pool and hot_kv rows differ in size")
+    num_reqs, topk = wave_rows.shape
+    if hot_kv.shape[-2] != num_reqs * capacity:
+        raise ValueError("hot_kv must hold num_reqs * capacity rows per cache")
+    if hot_idx.shape != wave_rows.shape or miss_pos.shape != wave_rows.shape or \
+            miss_count.shape != (num_reqs,):
+        raise ValueError("plan tensors must be [num_reqs, topk] (miss_count [num_reqs])")
+    _check("hs_apply_plan", _lib.hs_apply_plan(
+        _ptr(hot_kv), ctypes.c_void_p(host_pool.data_ptr()), host_rows, caches, num_reqs,
+        capacity, elems * hot_kv.element_size(), _ptr(wave_rows), topk, _ptr(hot_idx),
+        _ptr(miss_count), _ptr(miss_pos), _stream(stream)))

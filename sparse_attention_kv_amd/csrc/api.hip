@@ -116,6 +116,26 @@ hs_status hs_backup_rows(const void *dev_cache, int64_t dev_layer_rows, void *ho
                                          src_block_stride, static_cast<hipStream_t>(stream)));
 }
 
+hs_status hs_apply_plan(void *hot_kv, const void *host_pool, int64_t host_rows,
+                        int32_t num_caches, int32_t num_reqs, int32_t capacity, int32_t row_bytes,
+                        const int32_t *wave_rows, int32_t topk, const int32_t *hot_idx,
+                        const int32_t *miss_count, const int32_t *miss_pos, void *stream) {
+  if (host_rows <= 0 || num_caches <= 0 || num_reqs <= 0 || capacity <= 0 || row_bytes <= 0 ||
+      row_bytes % 16 != 0 || topk <= 0)
+    return HS_ERR_INVALID_ARG;
+  if (!hot_kv || !host_pool || !wave_rows || !hot_idx || !miss_count || !miss_pos)
+    return HS_ERR_INVALID_ARG;
+  if (host_rows > 0x7fffffffLL || static_cast<int64_t>(num_reqs) * capacity > 0x7fffffffLL)
+    return HS_ERR_INVALID_ARG;
+  if (!aligned16(hot_kv) || !aligned16(host_pool)) return HS_ERR_INVALID_ARG;
+  const void *pool = nullptr;
+  hs_status s = device_view(host_pool, &pool);
+  if (s != HS_OK) return s;
+  return from_hip(hs::launch_apply_plan(hot_kv, pool, host_rows, num_caches, num_reqs, capacity,
+                                        row_bytes, wave_rows, topk, hot_idx, miss_count, miss_pos,
+                                        static_cast<hipStream_t>(stream)));
+}
+
 size_t hs_attn_workspace_bytes(int32_t num_rows, int32_t num_heads, int32_t d_qk, int32_t d_v,
                                int32_t topk, int32_t dtype) {
   if (dtype != HS_BF16 || num_rows <= 0 || topk <= 0 || num_heads <= 0 || num_heads % 32 != 0 ||

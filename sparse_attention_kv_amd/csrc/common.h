@@ -83,6 +83,13 @@ hipError_t launch_backup_rows(const void *dev_cache, int64_t dev_layer_rows, voi
                               const int32_t *dst_rows, int32_t num_rows, int32_t src_block_size,
                               int32_t src_block_stride, hipStream_t stream);
 
+// Follower caches from the leader's swap plan; host_pool_dev is the pinned pools' device address.
+hipError_t launch_apply_plan(void *hot_kv, const void *host_pool_dev, int64_t host_rows,
+                             int32_t num_caches, int32_t num_reqs, int32_t capacity,
+                             int32_t row_bytes, const int32_t *wave_rows, int32_t topk,
+                             const int32_t *hot_idx, const int32_t *miss_count,
+                             const int32_t *miss_pos, hipStream_t stream);
+
 // ---- small device helpers ----
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 

@@ -151,3 +151,22 @@ def test_backup_validation():
     assert call(dst=None) == bad
     assert call(dev_rows=1 << 31) == bad
     assert call(dev=P + 8) == bad  # misaligned
+
+
+def test_apply_plan_validation():
+    hs, lib = _lib()
+    f = lib.hs_apply_plan
+    P = 4096
+    ok = dict(hot=P, pool=P, host_rows=100, caches=1, reqs=2, cap=8, row_bytes=1152, rows=P,
+              topk=4, idx=P, mc=P, mp=P)
+
+    def call(**kw):
+        a = {**ok, **kw}
+        return f(a["hot"], a["pool"], a["host_rows"], a["caches"], a["reqs"], a["cap"],
+                 a["row_bytes"], a["rows"], a["topk"], a["idx"], a["mc"], a["mp"], None)
+
+    bad = hs.HS_ERR_INVALID_ARG
+    for kw in (dict(host_rows=0), dict(caches=0), dict(reqs=0), dict(cap=0), dict(row_bytes=24),
+               dict(topk=0), dict(hot=None), dict(pool=None), dict(rows=None), dict(idx=None),
+               dict(mc=None), dict(mp=None), dict(host_rows=1 << 31), dict(hot=P + 4)):
+        assert call(**kw) == bad, kw
