@@ -183,6 +183,35 @@ def measure_swap(dev, reps=5):
             times.append(e0.elapsed_time(e1))
     step_ms = float(np.median(times))
 
+    # mixed batch (per-request residency): 16 of the 32 requests lost one resident page and
+    # swap in; the other 16 read a resident pool (a device copy of the host pool, same rows)
+    from sparse_attention_kv_amd.pipeline import ResidencyTracker
+    tracker = ResidencyTracker(w.block_table, w.seq_len, s.block_size)
+    for bq in range(0, s.num_reqs, 2):
+        page = next(p for (bb, p) in tracker.reclaimable_pages() if bb == bq)
+        tracker.release_resident_page(bq, page)
+    n_resident = int(tracker.fully_resident().sum())
+    req_res, req_swap, sel = tracker.row_inputs(w.req_id, dev)
+    res_bt = tracker.table(dev)
+    dev_pool = w.kv_pool.to(dev)
+    mstep = DecodeStep(num_reqs=s.num_reqs, rows_per_req=s.rows_per_req, topk=s.topk,
+                       num_heads=s.num_heads, d_qk=s.d_qk, d_v=s.d_v, dtype=torch.bfloat16,
+                       capacity=s.capacity, mixed=True, device=dev)
+    mtimes = []
+    for rep in range(reps + 2):
+        restore()
+        torch.cuda.synchronize()
+        e0.record(main)
+        mstep.run_mixed(st, topk_pos, req_res, req_swap, sel, lim, res_bt, bt, s.block_size, q,
+                        dev_pool, s.scale, s.tick0)
+        main.wait_stream(mstep.copy_stream)
+        e1.record(main)
+        torch.cuda.synchronize()
+        if rep >= 2:
+            mtimes.append(e0.elapsed_time(e1))
+    mixed_ms = float(np.median(mtimes))
+    del dev_pool, mstep
+
     # swap-in alone, wave by wave, from the same starting state
     restore()
     hs.hs_resolve_topk(topk_pos, req_id, lim, bt, s.block_size, s.block_size, b.slots, b.valid)
@@ -250,6 +279,8 @@ def measure_swap(dev, reps=5):
         "swap_waves_us": wave_us, "swap_miss_bytes": wave_bytes,
         "swap_GBps": warm_gbs, "swap_frac_of_B_host": warm_gbs / b_host,
         "cold_wave_us": cold_us, "cold_wave_bytes": cold_bytes, "cold_wave_GBps": cold_gbs,
+        "mixed_batch": {"resident_requests": n_resident, "step_ms": mixed_ms,
+                        "rows_per_s": s.rows / (mixed_ms / 1e3), "all_swap_step_ms": step_ms},
         "plan_reuse": {"followers": C, "leader_swap_us": lead_us, "apply_plan_us": apply_us,
                        "apply_GBps": apply_gbs, "apply_frac_of_B_host": apply_gbs / b_host},
     }

@@ -241,6 +241,35 @@ size_t hs_attn_workspace_bytes(int32_t num_rows, int32_t num_heads, int32_t d_qk
                                int32_t topk, int32_t dtype);
 
 /*
+ * hs_sparse_decode_attn_mixed -- attention over a batch whose rows read two caches.
+ * P3 resolve_topk listing: a fully resident batch reads the resident (paged) cache
+ * directly, any other batch swaps into the hot cache; P3 reclaim_resident_blocks: once
+ * part of a request's resident KV is reclaimed the request is no longer fully resident,
+ * and build_offload_command / are_requests_fully_resident make the choice for the whole
+ * batch.  This call lets each row take its own source, so resident requests keep reading
+ * the resident pool while reclaimed ones go through hs_swap_in and the hot buffer.
+ *
+ * Row i is computed exactly as hs_sparse_decode_attn computes it over
+ *   (kv_a, kv_a_rows, indices_a[i])  when row_sel[i] == 0, or
+ *   (kv_b, kv_b_rows, indices_b[i])  otherwise.
+ *
+ *   kv_a, kv_b            [kv_*_rows, d_qk] bf16 (e.g. resident pool and hot buffer)
+ *   indices_a, indices_b  [num_rows, topk] int32 rows into their cache, -1 = none
+ *   row_sel               [num_rows] int32 source of each row
+ *   workspace             as hs_sparse_decode_attn (hs_attn_workspace_bytes)
+ *
+ * Errors: as hs_sparse_decode_attn; HS_ERR_UNSUPPORTED for fp32 or shapes other than
+ * d_qk 576, d_v 512, heads a multiple of 32.
+ */
+hs_status hs_sparse_decode_attn_mixed(const void *q, const void *kv_a, int64_t kv_a_rows,
+                                      const int32_t *indices_a, const void *kv_b,
+                                      int64_t kv_b_rows, const int32_t *indices_b,
+                                      const int32_t *row_sel, int32_t num_rows, int32_t num_heads,
+                                      int32_t d_qk, int32_t d_v, int32_t topk, float scale,
+                                      int32_t dtype, void *out, float *lse, void *workspace,
+                                      size_t workspace_bytes, void *stream);
+
+/*
  * hs_finalize_accepted -- P2 ④: the target verifies [anchor, drafts] in one causal pass;
  * row r's logits judge draft r+1; drafts are kept while they equal the target's greedy
  * choice; only the accepted prefix's KV is kept and the replacement (or bonus) token has

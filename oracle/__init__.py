@@ -34,8 +34,11 @@ from .hisparse_ref import (  # noqa: F401
     build_hot_state,
     finalize_accepted,
     greedy_accept,
+    is_fully_resident,
     plan_backup_rows,
+    reclaimable_pages,
     resolve_topk,
     sparse_decode_attn,
+    sparse_decode_attn_mixed,
     swap_in,
 )

@@ -248,6 +248,54 @@ def sparse_decode_attn(q: np.ndarray, kv: np.ndarray, indices: np.ndarray, scale
     return out, lse
 
 
+def sparse_decode_attn_mixed(q: np.ndarray, kv_a: np.ndarray, idx_a: np.ndarray,
+                             kv_b: np.ndarray, idx_b: np.ndarray, row_sel: np.ndarray,
+                             scale: float, d_v: int):
+    """Attention of a batch whose rows read one of two caches.
+
+    P3 resolve_topk listing: a fully resident batch reads the resident cache, any other
+    batch the hot cache after swap-in; P3 reclaim_resident_blocks: a request whose resident
+    pages were reclaimed is no longer fully resident.  Reading (per-request residency): row
+    ``i`` is attended exactly as ``sparse_decode_attn`` over ``(kv_b, idx_b[i])`` when
+    ``row_sel[i] != 0``, else over ``(kv_a, idx_a[i])``.  Returns ``(out, lse)`` float64.
+    """
+    rows, H, _ = q.shape
+    out = np.zeros((rows, H, d_v), dtype=np.float64)
+    lse = np.full((rows, H), -np.inf, dtype=np.float64)
+    for i in range(rows):
+        kv, idx = (kv_b, idx_b) if row_sel[i] != 0 else (kv_a, idx_a)
+        o, l = sparse_decode_attn(q[i:i + 1], kv, idx[i:i + 1], scale, d_v)
+        out[i], lse[i] = o[0], l[0]
+    return out, lse
+
+
+def reclaimable_pages(block_table: np.ndarray, seq_len: np.ndarray, block_size: int):
+    """Resident pages the coordinator may reclaim: P3 reclaim_resident_blocks, where the
+    resident manager scans every request and offers its older blocks, never the last two.
+
+    Reading: request ``b`` uses pages ``0 .. ceil(seq_len[b] / block_size) - 1``; the mapped
+    ones (table entry >= 0) below index ``used - 2`` are offered, as ``(b, page_index)``
+    in request then page order."""
+    out = []
+    for b in range(block_table.shape[0]):
+        used = -(-int(seq_len[b]) // block_size)
+        for p in range(max(0, used - 2)):
+            if block_table[b, p] >= 0:
+                out.append((b, p))
+    return out
+
+
+def is_fully_resident(block_table: np.ndarray, seq_len: np.ndarray, block_size: int) -> np.ndarray:
+    """Per request: every page that holds one of its tokens is still mapped in the resident
+    pool (P3: once any of a request's resident KV is reclaimed, fully_resident is false;
+    are_requests_fully_resident asks it of every request of a batch)."""
+    res = np.zeros(block_table.shape[0], dtype=bool)
+    for b in range(block_table.shape[0]):
+        used = -(-int(seq_len[b]) // block_size)
+        res[b] = used <= block_table.shape[1] and bool((block_table[b, :used] >= 0).all())
+    return res
+
+
 # --------------------------------------------------------------------------------------
 # 4. greedy accept + accepted-prefix finalize
 # --------------------------------------------------------------------------------------

@@ -22,6 +22,7 @@ HS_OK, HS_ERR_INVALID_ARG, HS_ERR_CAPACITY, HS_ERR_UNSUPPORTED, HS_ERR_HIP = 0, 
 HS_BF16, HS_F32 = 0, 1
 
 EXPORTED = ("hs_resolve_topk", "hs_swap_in", "hs_sparse_decode_attn", "hs_sparse_decode_attn_paged",
+            "hs_sparse_decode_attn_mixed",
             "hs_attn_workspace_bytes", "hs_finalize_accepted", "hs_backup_rows", "hs_apply_plan",
             "hs_status_string", "hs_version")
 
@@ -57,6 +58,9 @@ def _load() -> ctypes.CDLL:
                                                 i32, i32, i32, i32, i32, f32, i32, vp, vp, vp, sz,
                                                 vp]
     lib.hs_sparse_decode_attn_paged.restype = i32
+    lib.hs_sparse_decode_attn_mixed.argtypes = [vp, vp, i64, vp, vp, i64, vp, vp, i32, i32, i32,
+                                                i32, i32, f32, i32, vp, vp, vp, sz, vp]
+    lib.hs_sparse_decode_attn_mixed.restype = i32
     lib.hs_attn_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32]
     lib.hs_attn_workspace_bytes.restype = sz
     lib.hs_finalize_accepted.argtypes = [ctypes.POINTER(HsHotState), vp, i32, vp, vp, i32, vp, vp,
@@ -356,3 +360,27 @@ def hs_apply_plan(hot_kv: torch.Tensor, host_pool: torch.Tensor, wave_rows: torc
         _ptr(hot_kv), ctypes.c_void_p(host_pool.data_ptr()), host_rows, caches, num_reqs,
         capacity, elems * hot_kv.element_size(), _ptr(wave_rows), topk, _ptr(hot_idx),
         _ptr(miss_count), _ptr(miss_pos), _stream(stream)))
+
+
+def hs_sparse_decode_attn_mixed(q: torch.Tensor, kv_a: torch.Tensor, indices_a: torch.Tensor,
+                                kv_b: torch.Tensor, indices_b: torch.Tensor,
+                                row_sel: torch.Tensor, scale: float, d_v: int, out: torch.Tensor,
+                                lse: Optional[torch.Tensor] = None,
+                                workspace: Optional[torch.Tensor] = None, stream=None):
+    """Attention whose rows read one of two caches (see include/hisparse.h)."""
+    i32 = torch.int32
+    _dev(q, "q"); _dev(kv_a, "kv_a", q.dtype); _dev(kv_b, "kv_b", q.dtype)
+    _dev(indices_a, "indices_a", i32); _dev(indices_b, "indices_b", i32)
+    _dev(row_sel, "row_sel", i32); _dev(out, "out", q.dtype)
+    if lse is not None:
+        _dev(lse, "lse", torch.float32)
+    if workspace is not None:
+        _dev(workspace, "workspace")
+    rows, heads, d_qk = q.shape
+    if indices_a.shape != indices_b.shape or indices_a.shape[0] != rows or row_sel.shape != (rows,):
+        raise ValueError("indices_a, indices_b must be [rows, topk] and row_sel [rows]")
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("hs_sparse_decode_attn_mixed", _lib.hs_sparse_decode_attn_mixed(
+        _ptr(q), _ptr(kv_a), kv_a.shape[0], _ptr(indices_a), _ptr(kv_b), kv_b.shape[0],
+        _ptr(indices_b), _ptr(row_sel), rows, heads, d_qk, d_v, indices_a.shape[1], float(scale),
+        _dtype_code(q.dtype), _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes, _stream(stream)))

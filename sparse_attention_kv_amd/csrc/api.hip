@@ -164,7 +164,7 @@ hs_status hs_sparse_decode_attn(const void *q, const void *kv, int64_t kv_rows,
                                !aligned16(workspace)))
       return HS_ERR_INVALID_ARG;
     return from_hip(hs::launch_attn_bf16(q, kv, kv_rows, indices, num_rows, num_heads, topk, scale,
-                                         out, lse, workspace, plan, nullptr, st));
+                                         out, lse, workspace, plan, nullptr, nullptr, st));
   }
   if (d_qk > hs::attn_f32_max_d() || d_v > d_qk || topk > hs::attn_f32_max_topk())
     return HS_ERR_UNSUPPORTED;
@@ -200,7 +200,36 @@ hs_status hs_sparse_decode_attn_paged(const void *q, const void *kv_pool, int64_
   const hs::PagedMap pg{req_id, causal_limit, block_table, num_reqs, bt_stride, block_size,
                         physical_block_stride};
   return from_hip(hs::launch_attn_bf16(q, kv_pool, kv_rows, topk_pos, num_rows, num_heads, topk,
-                                       scale, out, lse, workspace, plan, &pg,
+                                       scale, out, lse, workspace, plan, &pg, nullptr,
+                                       static_cast<hipStream_t>(stream)));
+}
+
+hs_status hs_sparse_decode_attn_mixed(const void *q, const void *kv_a, int64_t kv_a_rows,
+                                      const int32_t *indices_a, const void *kv_b,
+                                      int64_t kv_b_rows, const int32_t *indices_b,
+                                      const int32_t *row_sel, int32_t num_rows, int32_t num_heads,
+                                      int32_t d_qk, int32_t d_v, int32_t topk, float scale,
+                                      int32_t dtype, void *out, float *lse, void *workspace,
+                                      size_t workspace_bytes, void *stream) {
+  if (num_rows < 0 || num_heads <= 0 || d_qk <= 0 || d_v <= 0 || topk <= 0 || kv_a_rows < 0 ||
+      kv_b_rows < 0)
+    return HS_ERR_INVALID_ARG;
+  if (dtype != HS_BF16 && dtype != HS_F32) return HS_ERR_INVALID_ARG;
+  if (dtype != HS_BF16) return HS_ERR_UNSUPPORTED;
+  if (num_rows == 0) return HS_OK;
+  if (!q || !kv_a || !indices_a || !kv_b || !indices_b || !row_sel || !out)
+    return HS_ERR_INVALID_ARG;
+  if (kv_a_rows > 0x7fffffffLL || kv_b_rows > 0x7fffffffLL) return HS_ERR_INVALID_ARG;
+  if (d_qk != 576 || d_v != 512 || num_heads % 32 != 0) return HS_ERR_UNSUPPORTED;
+  if (!aligned16(q) || !aligned16(kv_a) || !aligned16(kv_b) || !aligned16(out))
+    return HS_ERR_INVALID_ARG;
+  const hs::AttnPlan plan = hs::plan_attn_bf16(num_rows, num_heads, topk);
+  if (plan.workspace > 0 &&
+      (workspace == nullptr || workspace_bytes < plan.workspace || !aligned16(workspace)))
+    return HS_ERR_INVALID_ARG;
+  const hs::AltSource alt{static_cast<const uint8_t *>(kv_b), kv_b_rows, indices_b, row_sel};
+  return from_hip(hs::launch_attn_bf16(q, kv_a, kv_a_rows, indices_a, num_rows, num_heads, topk,
+                                       scale, out, lse, workspace, plan, nullptr, &alt,
                                        static_cast<hipStream_t>(stream)));
 }
 

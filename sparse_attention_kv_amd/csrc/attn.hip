@@ -80,7 +80,8 @@ __global__ __launch_bounds__(kThreads8, 1) void attn_bf16_kernel(
     const __bf16 *__restrict__ q, const uint8_t *__restrict__ kv, int64_t kv_rows,
     const int32_t *__restrict__ indices, int32_t num_rows, int32_t num_heads, int32_t topk,
     int32_t keys_per_split, int32_t splits, float scale_log2, __bf16 *__restrict__ out,
-    float *__restrict__ lse, __bf16 *__restrict__ ws_o, float *__restrict__ ws_ml, PagedMap pg) {
+    float *__restrict__ lse, __bf16 *__restrict__ ws_o, float *__restrict__ ws_ml, PagedMap pg,
+    AltSource alt) {
   __shared__ __attribute__((aligned(16))) uint8_t s_kv0[kTileBytes];
   __shared__ __attribute__((aligned(16))) uint8_t s_kv1[kTileBytes];
   __shared__ __attribute__((aligned(16))) uint8_t s_p[kHG * kPStride];
@@ -106,6 +107,11 @@ __global__ __launch_bounds__(kThreads8, 1) void attn_bf16_kernel(
   const int hg = u % n_hg;
   const int split = (u / n_hg) % splits;
   const int row = u / (n_hg * splits);
+  if (alt.row_sel != nullptr && alt.row_sel[row] != 0) {  // this row reads the second source
+    kv = alt.kv;
+    kv_rows = alt.kv_rows;
+    indices = alt.indices;
+  }
   const int h0 = hg * kHG;
   const int kbeg = split * keys_per_split;
   const int kcnt = max(0, min(keys_per_split, topk - kbeg));
@@ -550,20 +556,20 @@ static hipError_t launch_attn32(const __bf16 *qb, const uint8_t *kvb, int64_t kv
                                 const int32_t *indices, int32_t num_rows, int32_t num_heads,
                                 int32_t topk, float scale_log2, __bf16 *ob, float *lse,
                                 void *workspace, const AttnPlan &plan, const PagedMap &pg,
-                                hipStream_t stream) {
+                                const AltSource &alt, hipStream_t stream) {
   const int units = num_rows * plan.splits * (num_heads / kHG);
   const int grid = (units + 7) / 8 * 8;
   if (plan.splits == 1) {
     hipLaunchKernelGGL((attn_bf16_kernel<false, kPaged>), dim3(grid), dim3(kThreads8), 0, stream,
                        qb, kvb, kv_rows, indices, num_rows, num_heads, topk, plan.keys_per_split,
-                       1, scale_log2, ob, lse, nullptr, nullptr, pg);
+                       1, scale_log2, ob, lse, nullptr, nullptr, pg, alt);
     return hipGetLastError();
   }
   __bf16 *ws_o = static_cast<__bf16 *>(workspace);
   float *ws_ml = reinterpret_cast<float *>(ws_o + (size_t)plan.splits * num_rows * num_heads * kDV);
   hipLaunchKernelGGL((attn_bf16_kernel<true, kPaged>), dim3(grid), dim3(kThreads8), 0, stream, qb,
                      kvb, kv_rows, indices, num_rows, num_heads, topk, plan.keys_per_split,
-                     plan.splits, scale_log2, ob, lse, ws_o, ws_ml, pg);
+                     plan.splits, scale_log2, ob, lse, ws_o, ws_ml, pg, alt);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   launch_attn_combine(ws_o, ws_ml, plan.splits, num_rows, num_heads, ob, lse, stream);
@@ -573,22 +579,23 @@ static hipError_t launch_attn32(const __bf16 *qb, const uint8_t *kvb, int64_t kv
 hipError_t launch_attn_bf16(const void *q, const void *kv, int64_t kv_rows, const int32_t *indices,
                             int32_t num_rows, int32_t num_heads, int32_t topk, float scale,
                             void *out, float *lse, void *workspace, const AttnPlan &plan,
-                            const PagedMap *paged, hipStream_t stream) {
+                            const PagedMap *paged, const AltSource *alt, hipStream_t stream) {
   if (plan.heads_per_wg == 128)
     return launch_attn128(q, kv, kv_rows, indices, num_rows, num_heads, topk, scale, out, lse,
-                          workspace, plan, paged, stream);
+                          workspace, plan, paged, alt, stream);
   if (plan.heads_per_wg == 64)
     return launch_attn64(q, kv, kv_rows, indices, num_rows, num_heads, topk, scale, out, lse,
-                         workspace, plan, paged, stream);
+                         workspace, plan, paged, alt, stream);
   const float scale_log2 = scale * 1.44269504088896340736f;
   const __bf16 *qb = static_cast<const __bf16 *>(q);
   const uint8_t *kvb = static_cast<const uint8_t *>(kv);
   __bf16 *ob = static_cast<__bf16 *>(out);
   if (paged != nullptr)
     return launch_attn32<true>(qb, kvb, kv_rows, indices, num_rows, num_heads, topk, scale_log2, ob,
-                               lse, workspace, plan, *paged, stream);
+                               lse, workspace, plan, *paged, AltSource{}, stream);
   return launch_attn32<false>(qb, kvb, kv_rows, indices, num_rows, num_heads, topk, scale_log2, ob,
-                              lse, workspace, plan, PagedMap{}, stream);
+                              lse, workspace, plan, PagedMap{},
+                              alt ? *alt : AltSource{}, stream);
 }
 
 hipError_t launch_attn_f32(const float *q, const float *kv, int64_t kv_rows, const int32_t *indices,

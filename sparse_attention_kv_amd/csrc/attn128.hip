@@ -83,7 +83,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn128_kernel(
     const int32_t *__restrict__ indices, int32_t num_rows, int32_t num_heads, int32_t topk,
     int32_t keys_per_split, int32_t splits, int32_t units, float scale_log2,
     __bf16 *__restrict__ out, float *__restrict__ lse, __bf16 *__restrict__ ws_o,
-    float *__restrict__ ws_ml, PagedMap pg) {
+    float *__restrict__ ws_ml, PagedMap pg, AltSource alt) {
   __shared__ __attribute__((aligned(16))) uint8_t s_kv[2 * kTileBytes];
   __shared__ __attribute__((aligned(16))) int32_t s_sidx[kMaxKeysPerSplit];
   __shared__ int s_scan[kWaves];
@@ -98,6 +98,11 @@ __global__ __launch_bounds__(kThreads, 1) void attn128_kernel(
   const int hg = u % n_hg;
   const int split = (u / n_hg) % splits;
   const int row = u / (n_hg * splits);
+  if (alt.row_sel != nullptr && alt.row_sel[row] != 0) {  // this row reads the second source
+    kv = alt.kv;
+    kv_rows = alt.kv_rows;
+    indices = alt.indices;
+  }
   const int hw = hg * kH128 + kHW * w;  // first head of this wave
   const int kbeg = split * keys_per_split;
   const int kcnt = max(0, min(keys_per_split, topk - kbeg));
@@ -363,20 +368,21 @@ template <bool kPaged>
 static hipError_t launch128(const __bf16 *qb, const uint8_t *kvb, int64_t kv_rows,
                             const int32_t *indices, int32_t num_rows, int32_t num_heads,
                             int32_t topk, float scale_log2, __bf16 *ob, float *lse, void *workspace,
-                            const AttnPlan &plan, const PagedMap &pg, hipStream_t stream) {
+                            const AttnPlan &plan, const PagedMap &pg,
+                            const AltSource &alt, hipStream_t stream) {
   const int units = num_rows * (num_heads / kH128) * plan.splits;
   const int grid = (units + 7) / 8 * 8;
   if (plan.splits == 1) {
     hipLaunchKernelGGL((attn128_kernel<false, kPaged>), dim3(grid), dim3(kThreads), 0, stream, qb,
                        kvb, kv_rows, indices, num_rows, num_heads, topk, plan.keys_per_split, 1,
-                       units, scale_log2, ob, lse, nullptr, nullptr, pg);
+                       units, scale_log2, ob, lse, nullptr, nullptr, pg, alt);
     return hipGetLastError();
   }
   __bf16 *ws_o = static_cast<__bf16 *>(workspace);
   float *ws_ml = reinterpret_cast<float *>(ws_o + (size_t)plan.splits * num_rows * num_heads * kDV);
   hipLaunchKernelGGL((attn128_kernel<true, kPaged>), dim3(grid), dim3(kThreads), 0, stream, qb,
                      kvb, kv_rows, indices, num_rows, num_heads, topk, plan.keys_per_split,
-                     plan.splits, units, scale_log2, ob, lse, ws_o, ws_ml, pg);
+                     plan.splits, units, scale_log2, ob, lse, ws_o, ws_ml, pg, alt);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   launch_attn_combine(ws_o, ws_ml, plan.splits, num_rows, num_heads, ob, lse, stream);
@@ -388,16 +394,17 @@ static hipError_t launch128(const __bf16 *qb, const uint8_t *kvb, int64_t kv_row
 hipError_t launch_attn128(const void *q, const void *kv, int64_t kv_rows, const int32_t *indices,
                           int32_t num_rows, int32_t num_heads, int32_t topk, float scale, void *out,
                           float *lse, void *workspace, const AttnPlan &plan, const PagedMap *paged,
-                          hipStream_t stream) {
+                          const AltSource *alt, hipStream_t stream) {
   const float scale_log2 = scale * 1.44269504088896340736f;
   const __bf16 *qb = static_cast<const __bf16 *>(q);
   const uint8_t *kvb = static_cast<const uint8_t *>(kv);
   __bf16 *ob = static_cast<__bf16 *>(out);
   if (paged != nullptr)
     return launch128<true>(qb, kvb, kv_rows, indices, num_rows, num_heads, topk, scale_log2, ob,
-                           lse, workspace, plan, *paged, stream);
+                           lse, workspace, plan, *paged, AltSource{}, stream);
   return launch128<false>(qb, kvb, kv_rows, indices, num_rows, num_heads, topk, scale_log2, ob,
-                          lse, workspace, plan, PagedMap{}, stream);
+                          lse, workspace, plan, PagedMap{},
+                          alt ? *alt : AltSource{}, stream);
 }
 
 }  // namespace hs

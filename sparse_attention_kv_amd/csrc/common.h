@@ -43,6 +43,16 @@ struct PagedMap {
   int32_t num_reqs, bt_stride, block_size, physical_block_stride;
 };
 
+// Second (cache, indices) source for attention over a mixed batch: a row with
+// row_sel[row] != 0 reads alt kv rows through alt indices (per-request residency: resident
+// requests read the paged pool, swapped requests the hot buffer).  row_sel == null: none.
+struct AltSource {
+  const uint8_t *kv;
+  int64_t kv_rows;
+  const int32_t *indices;  // [num_rows, topk]
+  const int32_t *row_sel;  // [num_rows]
+};
+
 struct AttnPlan {
   int heads_per_wg;    // 128 (attn128_kernel), 64 (attn64_kernel) or 32 (attn_bf16_kernel)
   int splits;          // key splits per (row, head group); 1 = no combine pass
@@ -54,17 +64,17 @@ AttnPlan plan_attn_bf16(int32_t num_rows, int32_t num_heads, int32_t topk);
 hipError_t launch_attn_bf16(const void *q, const void *kv, int64_t kv_rows, const int32_t *indices,
                             int32_t num_rows, int32_t num_heads, int32_t topk, float scale,
                             void *out, float *lse, void *workspace, const AttnPlan &plan,
-                            const PagedMap *paged, hipStream_t stream);
+                            const PagedMap *paged, const AltSource *alt, hipStream_t stream);
 
 hipError_t launch_attn64(const void *q, const void *kv, int64_t kv_rows, const int32_t *indices,
                          int32_t num_rows, int32_t num_heads, int32_t topk, float scale, void *out,
                          float *lse, void *workspace, const AttnPlan &plan, const PagedMap *paged,
-                         hipStream_t stream);
+                         const AltSource *alt, hipStream_t stream);
 
 hipError_t launch_attn128(const void *q, const void *kv, int64_t kv_rows, const int32_t *indices,
                           int32_t num_rows, int32_t num_heads, int32_t topk, float scale, void *out,
                           float *lse, void *workspace, const AttnPlan &plan, const PagedMap *paged,
-                          hipStream_t stream);
+                          const AltSource *alt, hipStream_t stream);
 
 hipError_t launch_attn_f32(const float *q, const float *kv, int64_t kv_rows, const int32_t *indices,
                            int32_t num_rows, int32_t num_heads, int32_t d_qk, int32_t d_v,

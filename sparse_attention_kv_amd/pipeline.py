@@ -15,6 +15,10 @@ The copy stream waits for the attention of wave r-2 before swapping wave r (vict
 wave r are never slots wave r-1 used when capacity >= 2*topk); with a smaller hot
 buffer it waits for wave r-1.  Both streams run at the default priority.
 
+Mixed batch (P3 reclaim_resident_blocks, build_offload_command): ResidencyTracker keeps
+the resident block table and tells which requests are still fully resident; run_mixed lets
+those read the resident pool while the rest swap in, instead of one switch per batch.
+
 Backup (P1 "3. HiSparse staging", P3 "数据 back up"): BackupStager turns page transfers
 into row lists in pinned staging buffers, copies them to the device without blocking,
 launches hs_backup_rows and records an event that `ready` polls.
@@ -29,7 +33,8 @@ import numpy as np
 import torch
 
 from . import (HotState, hs_attn_workspace_bytes, hs_backup_rows, hs_finalize_accepted,
-               hs_resolve_topk, hs_sparse_decode_attn, hs_sparse_decode_attn_paged, hs_swap_in)
+               hs_resolve_topk, hs_sparse_decode_attn, hs_sparse_decode_attn_mixed,
+               hs_sparse_decode_attn_paged, hs_swap_in)
 
 
 def build_hot_state(init_pos: torch.Tensor, init_stamp: torch.Tensor, seq_len: torch.Tensor,
@@ -73,6 +78,7 @@ class StepBuffers:
     argmax: Optional[torch.Tensor] = None
     accept_len: Optional[torch.Tensor] = None
     next_token: Optional[torch.Tensor] = None
+    slots_res: Optional[torch.Tensor] = None  # [rows, topk] resident-pool rows (mixed batch)
 
 
 class DecodeStep:
@@ -80,7 +86,7 @@ class DecodeStep:
 
     def __init__(self, *, num_reqs: int, rows_per_req: int, topk: int, num_heads: int,
                  d_qk: int, d_v: int, dtype: torch.dtype, capacity: int = 0,
-                 finalize: bool = False, want_miss_pos: bool = False,
+                 finalize: bool = False, want_miss_pos: bool = False, mixed: bool = False,
                  device: torch.device = torch.device("cuda")):
         self.B, self.R, self.K = num_reqs, rows_per_req, topk
         self.H, self.d_qk, self.d_v, self.dtype = num_heads, d_qk, d_v, dtype
@@ -103,6 +109,7 @@ class DecodeStep:
             argmax=torch.empty((rows,), **i32) if finalize else None,
             accept_len=torch.empty((num_reqs,), **i32) if finalize else None,
             next_token=torch.empty((num_reqs,), **i32) if finalize else None,
+            slots_res=torch.empty((rows, topk), **i32) if (swap and mixed) else None,
         )
         self.copy_stream = torch.cuda.Stream(device=device) if swap else None
         self.e_resolve = torch.cuda.Event()
@@ -155,6 +162,97 @@ class DecodeStep:
                                  finalize["new_kv"], R, finalize["seq_len"], block_table,
                                  block_size, tick0 + R, b.argmax, b.accept_len, b.next_token,
                                  stream=main)
+
+    # -- mixed batch: per-request residency ---------------------------------------------
+    def run_mixed(self, state: HotState, topk_pos, req_id_resident, req_id_swap, row_sel,
+                  causal_limit, resident_block_table, host_block_table, block_size, q, kv_pool,
+                  scale, tick0: int):
+        """A batch in which fully resident requests read the resident pool and the others
+        swap into the hot buffer (the per-batch switch of P3's build_offload_command made
+        per request).  ``req_id_resident`` / ``req_id_swap`` are the rows' request ids with
+        the other kind's rows set to -1, ``row_sel`` is 1 on rows that read the hot buffer
+        (see ResidencyTracker.row_inputs)."""
+        b, B, R = self.buf, self.B, self.R
+        main = torch.cuda.current_stream()
+        copy = self.copy_stream
+        serialize = self.capacity < 2 * self.K
+        hs_resolve_topk(topk_pos, req_id_swap, causal_limit, host_block_table, block_size,
+                        block_size, b.slots, b.valid)
+        self.e_resolve.record(main)
+        copy.wait_event(self.e_resolve)
+        hs_resolve_topk(topk_pos, req_id_resident, causal_limit, resident_block_table,
+                        block_size, block_size, b.slots_res, None)
+        for r in range(R):
+            lo, hi = r * B, (r + 1) * B
+            if r >= 1 and serialize:
+                copy.wait_event(self.e_attn[r - 1])
+            elif r >= 2:
+                copy.wait_event(self.e_attn[r - 2])
+            hs_swap_in(state, b.slots[lo:hi], tick0 + r, b.hot_idx[lo:hi], b.miss_count[r],
+                       None if b.miss_pos is None else b.miss_pos[lo:hi], stream=copy)
+            self.e_swap[r].record(copy)
+            main.wait_event(self.e_swap[r])
+            hs_sparse_decode_attn_mixed(q[lo:hi], kv_pool, b.slots_res[lo:hi], state.hot_kv,
+                                        b.hot_idx[lo:hi], row_sel[lo:hi], scale, self.d_v,
+                                        b.out[lo:hi], b.lse[lo:hi], b.workspace, stream=main)
+            self.e_attn[r].record(main)
+
+
+class ResidencyTracker:
+    """Host bookkeeping of which requests still have all their KV in the resident pool.
+
+    P3 reclaim_resident_blocks: when the cache manager runs short, the coordinator asks the
+    resident manager for reclaimable pages (every request's older pages, never its last
+    two), picks victims, and releases them: the table entry becomes null and the block
+    returns to the pool.  A request with a released page is no longer fully resident.
+    This tracker keeps the resident block table on the host, answers those questions and
+    builds the per-row inputs of DecodeStep.run_mixed.
+    """
+
+    def __init__(self, block_table: np.ndarray, seq_len: np.ndarray, block_size: int):
+        self.block_table = np.array(block_table, dtype=np.int32, copy=True)
+        self.seq_len = np.asarray(seq_len, dtype=np.int64)
+        self.block_size = block_size
+        self.free_blocks: list[int] = []
+
+    def _used_pages(self) -> np.ndarray:
+        return (self.seq_len + self.block_size - 1) // self.block_size
+
+    def reclaimable_pages(self) -> list[tuple[int, int]]:
+        used = self._used_pages()
+        out = []
+        for b in range(self.block_table.shape[0]):
+            pages = np.flatnonzero(self.block_table[b, :max(0, int(used[b]) - 2)] >= 0)
+            out.extend((b, int(p)) for p in pages)
+        return out
+
+    def release_resident_page(self, b: int, page: int) -> None:
+        blk = int(self.block_table[b, page])
+        if blk >= 0:
+            self.block_table[b, page] = -1
+            self.free_blocks.append(blk)
+
+    def fully_resident(self) -> np.ndarray:
+        used = self._used_pages()
+        width = self.block_table.shape[1]
+        cols = np.arange(width)[None, :]
+        need = cols < used[:, None]
+        mapped = (self.block_table >= 0) | ~need
+        return (used <= width) & mapped.all(axis=1)
+
+    def row_inputs(self, req_id_rows: np.ndarray, device) -> tuple:
+        """(req_id_resident, req_id_swap, row_sel) device int32 arrays for run_mixed."""
+        res = self.fully_resident()
+        req = np.asarray(req_id_rows, dtype=np.int64)
+        ok = (req >= 0) & (req < len(res))
+        row_res = np.zeros(len(req), dtype=bool)
+        row_res[ok] = res[req[ok]]
+        to = lambda a: torch.as_tensor(a.astype(np.int32)).to(device)  # noqa: E731
+        return (to(np.where(row_res, req, -1)), to(np.where(row_res, -1, req)),
+                to((~row_res).astype(np.int32)))
+
+    def table(self, device) -> torch.Tensor:
+        return torch.as_tensor(self.block_table).to(device)
 
 
 

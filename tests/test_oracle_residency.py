@@ -1,0 +1,58 @@
+"""Pins of the oracle's per-request residency pieces: mixed-source attention, reclaimable
+pages and the fully-resident test.
+
+Mixed attention is checked against single-source attention over the two caches laid end
+to end (an independent formulation); the residency rules against a hand-worked example
+of the pages' description (P3 reclaim_resident_blocks: never the last two blocks).
+"""
+
+import numpy as np
+
+import oracle
+
+
+def _raw_bf16(rng, shape):
+    x = rng.standard_normal(shape).astype(np.float32)
+    return (x.view(np.uint32) >> 16).astype(np.uint16)
+
+
+def test_mixed_equals_attention_over_concatenated_caches():
+    rng = np.random.default_rng(2)
+    rows, H, D, DV, K = 6, 4, 64, 48, 20
+    q = _raw_bf16(rng, (rows, H, D))
+    kv_a = _raw_bf16(rng, (50, D))
+    kv_b = _raw_bf16(rng, (30, D))
+    idx_a = rng.integers(-2, 55, size=(rows, K))   # some past kv_a's end
+    idx_b = rng.integers(-2, 35, size=(rows, K))   # some past kv_b's end
+    sel = np.array([0, 1, 1, 0, 1, 0])
+    out, lse = oracle.sparse_decode_attn_mixed(q, kv_a, idx_a, kv_b, idx_b, sel, 0.125, DV)
+    cat = np.concatenate([kv_a, kv_b])
+    a_ok = np.where((idx_a >= 0) & (idx_a < 50), idx_a, -1)
+    b_ok = np.where((idx_b >= 0) & (idx_b < 30), idx_b + 50, -1)
+    idx = np.where(sel[:, None] != 0, b_ok, a_ok)
+    ref, rlse = oracle.sparse_decode_attn(q, cat, idx, 0.125, DV)
+    assert np.allclose(out, ref, rtol=1e-12, atol=1e-12)
+    assert np.allclose(lse, rlse, rtol=1e-12, atol=1e-12)
+
+
+def test_mixed_with_one_source_is_plain_attention():
+    rng = np.random.default_rng(8)
+    q = _raw_bf16(rng, (3, 2, 32))
+    kv_a, kv_b = _raw_bf16(rng, (20, 32)), _raw_bf16(rng, (25, 32))
+    idx = rng.integers(-1, 20, size=(3, 7))
+    for sel, kv in ((np.zeros(3, int), kv_a), (np.ones(3, int), kv_b)):
+        out, lse = oracle.sparse_decode_attn_mixed(q, kv_a, idx, kv_b, idx, sel, 0.2, 16)
+        ref, rlse = oracle.sparse_decode_attn(q, kv, idx, 0.2, 16)
+        assert np.array_equal(out, ref) and np.array_equal(lse, rlse)
+
+
+def test_residency_rules_hand_worked():
+    # block size 4.  Request 0: 18 tokens -> pages 0..4 used, page 2 reclaimed already.
+    # Request 1: 8 tokens -> pages 0..1 (only the last two: nothing reclaimable).
+    # Request 2: 13 tokens -> pages 0..3 used; page 5 mapped but unused.
+    bt = np.array([[3, 8, -1, 4, 9, -1, -1],
+                   [5, 6, -1, -1, -1, -1, -1],
+                   [0, 1, 2, 7, -1, 11, -1]])
+    seq = np.array([18, 8, 13])
+    assert oracle.reclaimable_pages(bt, seq, 4) == [(0, 0), (0, 1), (2, 0), (2, 1)]
+    assert oracle.is_fully_resident(bt, seq, 4).tolist() == [False, True, True]
