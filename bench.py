@@ -330,6 +330,28 @@ def measure_finalize(dev, reps=10):
         if rep >= 2:
             times.append(e0.elapsed_time(e1) * 1e3)
     us = float(np.median(times))
+    # draft-model context KV append of the accepted prefix (P2 ⑤): 128 requests, context
+    # cache of 8 pages x 64 rows each, the verify rows' context K/V as new rows
+    ctx_bs, ctx_pages = 64, 8
+    ctx_cache = torch.zeros((s.num_reqs * ctx_pages * ctx_bs, s.d_qk), dtype=torch.bfloat16,
+                            device=dev)
+    ctx_bt = torch.arange(s.num_reqs * ctx_pages, dtype=torch.int32, device=dev).view(
+        s.num_reqs, ctx_pages)
+    ctx_len0 = torch.full((s.num_reqs,), 100, dtype=torch.int32, device=dev)
+    ctx_len = ctx_len0.clone()
+    app_times = []
+    for rep in range(reps + 2):
+        ctx_len.copy_(ctx_len0)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(main)
+        hs.hs_append_accepted(ctx_cache, ctx_bt, ctx_len, new_kv, acc, ctx_bs, ctx_bs,
+                              s.rows_per_req)
+        e1.record(main)
+        torch.cuda.synchronize()
+        if rep >= 2:
+            app_times.append(e0.elapsed_time(e1) * 1e3)
+    app_rows = int((acc.clamp(0, s.rows_per_req - 1) + 1).sum().item())
     logit_bytes = rows * s.vocab * 2
     return {
         "workload": "greedy accept + finalize: 128 requests x 3 rows, logits [384, 129280] bf16, "
@@ -338,6 +360,7 @@ def measure_finalize(dev, reps=10):
         "logits_GBps": logit_bytes / (us / 1e6) / 1e9,
         "logits_frac_of_hbm_peak": logit_bytes / (us / 1e6) / 1e9 / HBM_PEAK_GBS,
         "accept_length_histogram": np.bincount(acc.cpu().numpy(), minlength=s.rows_per_req).tolist(),
+        "dflash_context_append_us": float(np.median(app_times)), "dflash_rows_appended": app_rows,
     }
 
 

@@ -342,6 +342,37 @@ hs_status hs_backup_rows(const void *dev_cache, int64_t dev_layer_rows, void *ho
                          const int32_t *dst_rows, int32_t num_rows, int32_t src_block_size,
                          int32_t src_block_stride, void *stream);
 
+/*
+ * hs_append_accepted -- P2 ⑤: after target verification only the accepted prefix's
+ * target features go through the draft model's context K/V branch and are appended to
+ * its context KV cache (KV_D(P) -> KV_D(P + [a0, b1]) in the worked example; the KV the
+ * draft round made for itself is not used).  ⑥ and the timeline table: the context then
+ * covers every confirmed position except the newest token, which is the next anchor.
+ *
+ * For request b with L = clamp(accept_len[b], 0, rows_per_req - 1) and r = 0 .. L:
+ *   pos = ctx_len[b] + r,  page = ctx_block_table[b, pos / block_size]
+ *   ctx_cache row (page * physical_block_stride + pos % block_size)
+ *       <- new_rows row (r * num_reqs + b)          (row_bytes bytes, bit for bit)
+ * then ctx_len[b] += L + 1.  A position whose page is unmapped (-1, or past bt_stride)
+ * or whose row is past ctx_rows is not written (the caller maps pages ahead); ctx_len
+ * still advances.
+ *
+ *   ctx_cache        [ctx_rows, row_bytes] bytes, the draft model's context KV
+ *   ctx_block_table  [num_reqs, bt_stride] int32
+ *   ctx_len          [num_reqs] int32, read and advanced in place
+ *   new_rows         [num_reqs*rows_per_req, row_bytes] bytes, wave-major verify rows
+ *                    (context K/V of each row from the target's features)
+ *   accept_len       [num_reqs] int32 (hs_finalize_accepted's out_accept_len)
+ *
+ * Errors: HS_ERR_INVALID_ARG (null pointers, non-positive sizes, row_bytes not a multiple
+ * of 16, misaligned buffers, ctx_rows beyond int32).
+ */
+hs_status hs_append_accepted(void *ctx_cache, int64_t ctx_rows, int32_t row_bytes,
+                             const int32_t *ctx_block_table, int32_t bt_stride,
+                             int32_t block_size, int32_t physical_block_stride, int32_t *ctx_len,
+                             const void *new_rows, const int32_t *accept_len, int32_t num_reqs,
+                             int32_t rows_per_req, void *stream);
+
 /* Static description of a status code. */
 const char *hs_status_string(int32_t status);
 

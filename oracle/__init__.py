@@ -28,6 +28,7 @@ itself (worked example, closed forms, brute force, library routines).
 from .hisparse_ref import (  # noqa: F401
     HotState,
     PageTransfer,
+    append_accepted,
     apply_plan,
     as_f64,
     backup_rows,

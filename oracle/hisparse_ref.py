@@ -463,3 +463,41 @@ def backup_rows(dev_cache: np.ndarray, host_cache: np.ndarray, src_slots: np.nda
                 continue
             out[layer, d] = dev_cache[layer, p]
     return out
+
+
+# --------------------------------------------------------------------------------------
+# 6. draft-model context KV append
+# --------------------------------------------------------------------------------------
+def append_accepted(ctx_cache: np.ndarray, ctx_block_table: np.ndarray, ctx_len: np.ndarray,
+                    new_rows: np.ndarray, accept_len: np.ndarray, rows_per_req: int,
+                    block_size: int, physical_block_stride: int):
+    """The draft model's context cache grows by each request's accepted prefix.
+
+    P2 ⑤: after target verification, only the accepted prefix's target features go
+    through the draft model's context K/V branch and are appended to its context cache
+    (``KV_D(P) -> KV_D(P + [a0, b1])``); the KV of the draft round is not used.  ⑥ and the
+    timeline table: the context then covers the confirmed positions except the newest
+    token.  Reading: verify rows are wave-major (row ``r * B + b``); with
+    ``L = clamp(accept_len[b], 0, rows_per_req - 1)``, rows ``r = 0 .. L`` go to positions
+    ``ctx_len[b] + r`` through the block table (row ``page * stride + pos % block_size``);
+    unmapped positions are skipped; ``ctx_len[b]`` advances by ``L + 1``.
+    Returns ``(new ctx_cache, new ctx_len)``; the inputs are not modified.
+    """
+    cache = ctx_cache.copy()
+    lens = np.array(ctx_len, dtype=np.int64, copy=True)
+    B = len(ctx_len)
+    for b in range(B):
+        L = min(max(int(accept_len[b]), 0), rows_per_req - 1)
+        for r in range(L + 1):
+            pos = int(ctx_len[b]) + r
+            pidx = pos // block_size
+            if pos < 0 or pidx >= ctx_block_table.shape[1]:
+                continue
+            page = int(ctx_block_table[b, pidx])
+            if page < 0:
+                continue
+            row = page * physical_block_stride + pos % block_size
+            if row < cache.shape[0]:
+                cache[row] = new_rows[r * B + b]
+        lens[b] = int(ctx_len[b]) + L + 1
+    return cache, lens

@@ -24,6 +24,7 @@ HS_BF16, HS_F32 = 0, 1
 EXPORTED = ("hs_resolve_topk", "hs_swap_in", "hs_sparse_decode_attn", "hs_sparse_decode_attn_paged",
             "hs_sparse_decode_attn_mixed",
             "hs_attn_workspace_bytes", "hs_finalize_accepted", "hs_backup_rows", "hs_apply_plan",
+            "hs_append_accepted",
             "hs_status_string", "hs_version")
 
 
@@ -70,6 +71,8 @@ def _load() -> ctypes.CDLL:
     lib.hs_backup_rows.restype = i32
     lib.hs_apply_plan.argtypes = [vp, vp, i64, i32, i32, i32, i32, vp, i32, vp, vp, vp, vp]
     lib.hs_apply_plan.restype = i32
+    lib.hs_append_accepted.argtypes = [vp, i64, i32, vp, i32, i32, i32, vp, vp, vp, i32, i32, vp]
+    lib.hs_append_accepted.restype = i32
     lib.hs_status_string.argtypes = [i32]
     lib.hs_status_string.restype = ctypes.c_char_p
     lib.hs_version.argtypes = []
@@ -384,3 +387,26 @@ def hs_sparse_decode_attn_mixed(q: torch.Tensor, kv_a: torch.Tensor, indices_a: 
         _ptr(q), _ptr(kv_a), kv_a.shape[0], _ptr(indices_a), _ptr(kv_b), kv_b.shape[0],
         _ptr(indices_b), _ptr(row_sel), rows, heads, d_qk, d_v, indices_a.shape[1], float(scale),
         _dtype_code(q.dtype), _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+
+def hs_append_accepted(ctx_cache: torch.Tensor, ctx_block_table: torch.Tensor,
+                       ctx_len: torch.Tensor, new_rows: torch.Tensor, accept_len: torch.Tensor,
+                       block_size: int, physical_block_stride: int, rows_per_req: int,
+                       stream=None):
+    """Append each request's accepted prefix to the draft model's context cache and advance
+    ctx_len in place (see include/hisparse.h)."""
+    i32 = torch.int32
+    _dev(ctx_cache, "ctx_cache"); _dev(ctx_block_table, "ctx_block_table", i32)
+    _dev(ctx_len, "ctx_len", i32); _dev(new_rows, "new_rows", ctx_cache.dtype)
+    _dev(accept_len, "accept_len", i32)
+    num_reqs = ctx_len.shape[0]
+    if ctx_cache.dim() != 2 or new_rows.dim() != 2 or new_rows.shape[1] != ctx_cache.shape[1]:
+        raise ValueError("ctx_cache and new_rows must be [rows, elems] of the same width")
+    if new_rows.shape[0] != num_reqs * rows_per_req or accept_len.shape != (num_reqs,) or \
+            ctx_block_table.shape[0] != num_reqs:
+        raise ValueError("new_rows must hold num_reqs * rows_per_req rows")
+    _check("hs_append_accepted", _lib.hs_append_accepted(
+        _ptr(ctx_cache), ctx_cache.shape[0], ctx_cache.shape[1] * ctx_cache.element_size(),
+        _ptr(ctx_block_table), ctx_block_table.shape[1], block_size, physical_block_stride,
+        _ptr(ctx_len), _ptr(new_rows), _ptr(accept_len), num_reqs, rows_per_req, _stream(stream)))

@@ -3,7 +3,7 @@
 
 #include <cstring>
 
-#include "common.h"
+#include "ops.h"
 
 namespace hs {
 int attn_f32_max_topk();
@@ -134,6 +134,24 @@ hs_status hs_apply_plan(void *hot_kv, const void *host_pool, int64_t host_rows,
   return from_hip(hs::launch_apply_plan(hot_kv, pool, host_rows, num_caches, num_reqs, capacity,
                                         row_bytes, wave_rows, topk, hot_idx, miss_count, miss_pos,
                                         static_cast<hipStream_t>(stream)));
+}
+
+hs_status hs_append_accepted(void *ctx_cache, int64_t ctx_rows, int32_t row_bytes,
+                             const int32_t *ctx_block_table, int32_t bt_stride,
+                             int32_t block_size, int32_t physical_block_stride, int32_t *ctx_len,
+                             const void *new_rows, const int32_t *accept_len, int32_t num_reqs,
+                             int32_t rows_per_req, void *stream) {
+  if (ctx_rows <= 0 || row_bytes <= 0 || row_bytes % 16 != 0 || bt_stride <= 0 ||
+      block_size <= 0 || physical_block_stride <= 0 || num_reqs <= 0 || rows_per_req <= 0)
+    return HS_ERR_INVALID_ARG;
+  if (!ctx_cache || !ctx_block_table || !ctx_len || !new_rows || !accept_len)
+    return HS_ERR_INVALID_ARG;
+  if (ctx_rows > 0x7fffffffLL) return HS_ERR_INVALID_ARG;
+  if (!aligned16(ctx_cache) || !aligned16(new_rows)) return HS_ERR_INVALID_ARG;
+  return from_hip(hs::launch_append_accepted(ctx_cache, ctx_rows, row_bytes, ctx_block_table,
+                                             bt_stride, block_size, physical_block_stride, ctx_len,
+                                             new_rows, accept_len, num_reqs, rows_per_req,
+                                             static_cast<hipStream_t>(stream)));
 }
 
 size_t hs_attn_workspace_bytes(int32_t num_rows, int32_t num_heads, int32_t d_qk, int32_t d_v,

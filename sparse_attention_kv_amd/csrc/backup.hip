@@ -14,7 +14,7 @@
 
 #include <algorithm>
 
-#include "common.h"
+#include "ops.h"
 
 namespace hs {
 namespace {

@@ -1,4 +1,6 @@
-// Internal declarations shared by the library's translation units (gfx950 only).
+// Internal declarations shared by the library's translation units (gfx950 only): vector
+// types, the attention structs and launchers, small device helpers.  The other kernel
+// families' launchers are in ops.h.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -16,24 +18,7 @@ typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 
 #define HS_LDS __attribute__((address_space(3)))
 
-// Largest hot-buffer capacity the swap-in kernel's LDS arrays are sized for.
-constexpr int kMaxCapacity = 16384;
-// Largest top-k a swap-in call accepts (it is also bounded by the capacity); the
-// per-entry LDS arrays of the swap-in kernel are sized by it.
-constexpr int kMaxSwapTopk = 4096;
-
-// ---- launchers (one per kernel family); return hipSuccess or the launch error ----
-hipError_t launch_resolve_topk(const int32_t *topk_pos, int32_t num_rows, int32_t topk,
-                               const int32_t *req_id, const int32_t *causal_limit,
-                               int32_t num_reqs, const int32_t *block_table, int32_t bt_stride,
-                               int32_t block_size, int32_t physical_block_stride,
-                               int32_t *out_slots, int32_t *out_valid, hipStream_t stream);
-
-hipError_t launch_swap_in(const hs_hot_state &st, const void *host_pool_dev,
-                          const int32_t *wave_rows, int32_t topk, int32_t tick,
-                          int32_t *out_hot_idx, int32_t *out_miss_count, int32_t *out_miss_pos,
-                          hipStream_t stream);
-
+// ---- attention launchers; return hipSuccess or the launch error ----
 // Block-table description for attention that resolves top-k token positions itself
 // (the fully resident batch); null = the indices are already KV rows.
 struct PagedMap {
@@ -79,26 +64,6 @@ hipError_t launch_attn128(const void *q, const void *kv, int64_t kv_rows, const 
 hipError_t launch_attn_f32(const float *q, const float *kv, int64_t kv_rows, const int32_t *indices,
                            int32_t num_rows, int32_t num_heads, int32_t d_qk, int32_t d_v,
                            int32_t topk, float scale, float *out, float *lse, hipStream_t stream);
-
-hipError_t launch_finalize(const hs_hot_state &st, const void *host_pool_dev, const void *logits,
-                           int32_t vocab, const int32_t *draft_ids, const void *new_kv,
-                           int32_t rows_per_req, const int32_t *seq_len, const int32_t *block_table,
-                           int32_t bt_stride, int32_t block_size, int32_t tick, int32_t *out_argmax,
-                           int32_t *out_accept_len, int32_t *out_next_token, hipStream_t stream);
-
-// Device -> host row backup; host_cache_dev is the pinned host cache's device address.
-hipError_t launch_backup_rows(const void *dev_cache, int64_t dev_layer_rows, void *host_cache_dev,
-                              int64_t host_layer_rows, int32_t num_layers, int32_t row_bytes,
-                              const int32_t *src_slots, int32_t src_per_layer,
-                              const int32_t *dst_rows, int32_t num_rows, int32_t src_block_size,
-                              int32_t src_block_stride, hipStream_t stream);
-
-// Follower caches from the leader's swap plan; host_pool_dev is the pinned pools' device address.
-hipError_t launch_apply_plan(void *hot_kv, const void *host_pool_dev, int64_t host_rows,
-                             int32_t num_caches, int32_t num_reqs, int32_t capacity,
-                             int32_t row_bytes, const int32_t *wave_rows, int32_t topk,
-                             const int32_t *hot_idx, const int32_t *miss_count,
-                             const int32_t *miss_pos, hipStream_t stream);
 
 // ---- small device helpers ----
 __device__ __forceinline__ int lane_id() { return __lane_id(); }

@@ -17,7 +17,7 @@
 //                   link) and into the hot buffer (overwrite, or install into the LRU
 //                   victim with the kept hits pinned).
 
-#include "common.h"
+#include "ops.h"
 
 namespace hs {
 namespace {

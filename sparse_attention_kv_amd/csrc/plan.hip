@@ -9,7 +9,7 @@
 // Grid (request, kSlices): the slices of a request split its (cache, miss, 16-byte chunk)
 // work; each thread keeps kUnroll host-link loads in flight before it stores to HBM.
 
-#include "common.h"
+#include "ops.h"
 
 namespace hs {
 namespace {

@@ -11,7 +11,7 @@
 // block-table row of a request is small (<= 8 KB) and stays in L2.
 // Output keeps -1 in place (no compaction); the valid count is a block reduction.
 
-#include "common.h"
+#include "ops.h"
 
 namespace hs {
 namespace {

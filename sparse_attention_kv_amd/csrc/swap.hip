@@ -21,7 +21,7 @@
 //      loads (the host link is the bound; many independent loads per thread are kept
 //      in flight).
 
-#include "common.h"
+#include "ops.h"
 
 namespace hs {
 namespace {

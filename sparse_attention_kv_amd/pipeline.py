@@ -32,7 +32,8 @@ from typing import Optional, Sequence
 import numpy as np
 import torch
 
-from . import (HotState, hs_attn_workspace_bytes, hs_backup_rows, hs_finalize_accepted,
+from . import (HotState, hs_append_accepted, hs_attn_workspace_bytes, hs_backup_rows,
+               hs_finalize_accepted,
                hs_resolve_topk, hs_sparse_decode_attn, hs_sparse_decode_attn_mixed,
                hs_sparse_decode_attn_paged, hs_swap_in)
 
@@ -162,6 +163,11 @@ class DecodeStep:
                                  finalize["new_kv"], R, finalize["seq_len"], block_table,
                                  block_size, tick0 + R, b.argmax, b.accept_len, b.next_token,
                                  stream=main)
+            d = finalize.get("dflash")
+            if d is not None:  # P2 ⑤: the draft model's context KV takes the accepted prefix
+                hs_append_accepted(d["ctx_cache"], d["ctx_block_table"], d["ctx_len"],
+                                   d["ctx_rows"], b.accept_len, d["block_size"], d["block_size"],
+                                   R, stream=main)
 
     # -- mixed batch: per-request residency ---------------------------------------------
     def run_mixed(self, state: HotState, topk_pos, req_id_resident, req_id_swap, row_sel,

@@ -113,6 +113,20 @@ def _pipeline_case(name, sample_rows_per_wave=6):
         snap = (locs, w.kv_pool[torch.from_numpy(locs).long()].clone())
         fin = dict(logits=w.logits.to(dev()), draft_ids=to_dev(w.draft_ids),
                    new_kv=w.new_kv.to(dev()), seq_len=g["seq_len"])
+        # the draft model's context cache takes the accepted prefix too (its own rows)
+        crng = np.random.default_rng(77)
+        cbs, cpages = 16, 8
+        ctx = dict(bt=crng.permutation(B * cpages).reshape(B, cpages).astype(np.int32),
+                   len=crng.integers(0, cpages * cbs - R, size=B).astype(np.int32),
+                   rows=raw(w.new_kv)[crng.permutation(B * R)],
+                   cache=raw(w.new_kv)[crng.integers(0, B * R, size=B * cpages * cbs)])
+        tdt = w.new_kv.dtype
+
+        def _t(a):
+            t = torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a)
+            return (t.view(tdt) if a.dtype == np.uint16 else t).to(dev())
+        fin["dflash"] = dict(ctx_cache=_t(ctx["cache"]), ctx_block_table=to_dev(ctx["bt"]),
+                             ctx_len=to_dev(ctx["len"]), ctx_rows=_t(ctx["rows"]), block_size=cbs)
     step = DecodeStep(num_reqs=B, rows_per_req=R, topk=s.topk, num_heads=s.num_heads, d_qk=s.d_qk,
                       d_v=s.d_v, dtype=w.q.dtype, capacity=s.capacity, finalize=s.finalize,
                       want_miss_pos=True, device=dev())
@@ -153,6 +167,13 @@ def _pipeline_case(name, sample_rows_per_wave=6):
                                  s.block_size, R, s.tick0 + R)
         locs, _ = snap
         assert np.array_equal(raw(gpu_fin_rows), pool[locs]), "host rows after finalize"
+        d = fin["dflash"]
+        ref_cache, ref_len = oracle.append_accepted(ctx["cache"], ctx["bt"], ctx["len"], ctx["rows"],
+                                                    acc, R, cbs, cbs)
+        got_cache = d["ctx_cache"].cpu()
+        got_cache = raw(got_cache) if got_cache.dtype == torch.bfloat16 else got_cache.numpy()
+        assert np.array_equal(got_cache, ref_cache), "draft-model context cache"
+        assert np.array_equal(d["ctx_len"].cpu().numpy(), ref_len), "draft-model context length"
         log(f"finalize {name}: accept-length histogram {np.bincount(acc, minlength=R).tolist()}")
     _compare_state(ost, gst, f"{name} after step")
     check_state_invariants(ost, pool)

@@ -170,3 +170,20 @@ def test_apply_plan_validation():
                dict(topk=0), dict(hot=None), dict(pool=None), dict(rows=None), dict(idx=None),
                dict(mc=None), dict(mp=None), dict(host_rows=1 << 31), dict(hot=P + 4)):
         assert call(**kw) == bad, kw
+
+
+def test_append_validation():
+    hs, lib = _lib()
+    f = lib.hs_append_accepted
+    P = 4096
+    ok = dict(cache=P, rows=100, rb=1152, bt=P, bts=4, bs=16, ps=16, ln=P, new=P, acc=P, B=2, R=3)
+
+    def call(**kw):
+        a = {**ok, **kw}
+        return f(a["cache"], a["rows"], a["rb"], a["bt"], a["bts"], a["bs"], a["ps"], a["ln"],
+                 a["new"], a["acc"], a["B"], a["R"], None)
+
+    for kw in (dict(rows=0), dict(rb=8), dict(bts=0), dict(bs=0), dict(ps=0), dict(B=0), dict(R=0),
+               dict(cache=None), dict(bt=None), dict(ln=None), dict(new=None), dict(acc=None),
+               dict(rows=1 << 31), dict(new=P + 8)):
+        assert call(**kw) == hs.HS_ERR_INVALID_ARG, kw
