@@ -8,19 +8,30 @@
  *   hs_swap_in            hit/miss split against the per-request hot buffer, LRU
  *                         victim choice, copy of the misses from the pinned host pool
  *   hs_sparse_decode_attn attention over only the selected latent KV rows
+ *                         (_paged: positions resolved in the same call; _mixed: each
+ *                         row reads one of two caches)
  *   hs_finalize_accepted  greedy acceptance of the draft rows, then keep exactly the
  *                         target-verified prefix's KV (host pool + hot buffer)
  *
+ * and around it:
+ *
+ *   hs_apply_plan         follower caches (other layers) take the leader's swap plan
+ *   hs_backup_rows        device -> pinned host copy of new KV rows (staging, spills)
+ *   hs_append_accepted    the draft model's context cache takes the accepted prefix
+ *
  * Sources (web pages describing the method):
  *   P1  Notion page "hiSparse-MTP" -- summary (six-stage main line ending in accepted-KV
- *       finalize) and "1. 启动阶段" (startup: the coordinator's device buffer, host
- *       pool, LRU slots and async stream; the core-state maps).
+ *       finalize), "1. 启动阶段" (startup: the coordinator's device buffer, host
+ *       pool, LRU slots and async stream; the core-state maps) and "3. HiSparse staging"
+ *       (prefill KV backed up to the host pool, readiness by event).
  *   P2  blog post "投机解码的 KV 流转：prefill 阶段 DFlash 也要吃下整个 prompt" --
- *       worked example, sections ④ (target verify, greedy acceptance, kept KV) and ⑥.
+ *       worked example, sections ④ (target verify, greedy acceptance, kept KV), ⑤ (the
+ *       draft model's context KV takes the accepted prefix) and ⑥.
  *   P3  CSDN post "vllm 分析（十二）——Hisparse下篇" -- HiSparseCacheHandle.resolve_topk
  *       listing (fully-resident conversion vs. swap-in), HiSparseHotSpec (fixed hot
  *       blocks per request), "数据 back up" (block-row address arithmetic, pinned host
- *       pool), build_offload_command (fully-resident batch predicate).
+ *       pool, the worker's backup transfers), reclaim_resident_blocks and
+ *       build_offload_command (per-batch residency).
  *
  * Conventions for every call:
  *   - All pointers are caller-owned; the library allocates nothing and keeps no state.

@@ -179,6 +179,8 @@ class DecodeStep:
         the other kind's rows set to -1, ``row_sel`` is 1 on rows that read the hot buffer
         (see ResidencyTracker.row_inputs)."""
         b, B, R = self.buf, self.B, self.R
+        if b.slots_res is None:
+            raise ValueError("run_mixed needs a DecodeStep built with capacity > 0 and mixed=True")
         main = torch.cuda.current_stream()
         copy = self.copy_stream
         serialize = self.capacity < 2 * self.K
