@@ -7,7 +7,8 @@
 // Workgroup = (query row, 128 heads, key split); 4 waves, each owning 32 heads end to end,
 // so every gathered KV tile serves all 128 heads of its row once:
 //   * tiles of 64 selected rows are gathered direct-to-LDS and double buffered; a wave's
-//     18 slot issues for the next tile are spread over its two 32-key blocks;
+//     18 slot issues for the next tile are spread over the S^T phases of its two 32-key
+//     blocks, one every other k-step pair;
 //   * per 32-key block: S^T (32 keys x the wave's 32 heads) = K Q^T with
 //     v_mfma_f32_32x32x16_bf16, Q resident in 144 VGPRs, two accumulator chains;
 //   * a lane holds 16 scores of one head: the head maximum takes one cross-half step; the
@@ -273,7 +274,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn128_kernel(
             mfma_s(sa, kf[bb][0], qreg[2 * kp]);
             mfma_s(sb, kf[bb][1], qreg[2 * kp + 1]);
           }
-          if (more && kp < 9) dma16(gsrc + 128 * kp, gdst + 1024 * kp);
+          // one slot every other k-step pair: a wave that waits to issue a DMA stalls its
+          // MFMAs too, so the issues are spread over the whole S^T phase
+          if (more && (kp & 1) == 0) dma16(gsrc + 128 * (kp >> 1), gdst + 1024 * (kp >> 1));
           __builtin_amdgcn_sched_barrier(0);
         }
         mfma_s_drain(sa, sb);
