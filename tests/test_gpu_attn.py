@@ -218,3 +218,23 @@ def test_attn_deterministic_and_index_order_invariant():
     perm = torch.randperm(idx.shape[1], generator=torch.Generator().manual_seed(0)).to(dev())
     c, _ = _attn(g["q"], w.kv_pool, idx[:, perm].contiguous(), s.scale, s.d_v)
     assert_close(out_f64(c), out_f64(a), (1e-2, 1e-2), "permuted indices")
+
+
+# Head counts other than 128 reach the kernels through other planner choices: 32 and 96
+# heads only the 32-head kernel, 192 the 64-head one from 32 (row, 64-head) groups, 256
+# the 128-head one from 256 (row, 128-head) groups.  The oracle checks sampled rows.
+@pytest.mark.parametrize("H,rows", [(32, 5), (96, 7), (96, 40), (192, 3), (192, 16), (256, 128)])
+def test_attn_head_counts(H, rows):
+    rng = np.random.default_rng(H * 1000 + rows)
+    kv_rows, topk = 5000, 900
+    q = _rand_bf16((rows, H, 576), H + rows)
+    kv = _rand_bf16((kv_rows, 576), H + rows + 1)
+    idx = np.stack([rng.choice(kv_rows, topk, replace=False) for _ in range(rows)]).astype(np.int32)
+    idx[0, rng.random(topk) < 0.25] = -1
+    log(f"attn head count H={H} rows={rows}")
+    out, lse = _attn(q, kv, to_dev(idx), 1 / 24, 512)
+    sample = sorted(set([0, 1, rows // 2, rows - 1]))
+    ref, rlse = oracle.sparse_decode_attn(raw(q.cpu()[sample]), raw(kv.cpu()), idx[sample], 1 / 24, 512)
+    assert_close(out_f64(out[sample]), ref, BF16_TOL, f"H={H} rows={rows}")
+    g = lse[sample].cpu().double().numpy()
+    assert_close(g, rlse, LSE_TOL, f"H={H} rows={rows} lse")
