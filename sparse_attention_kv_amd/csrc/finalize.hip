@@ -22,8 +22,8 @@
 namespace hs {
 namespace {
 
-constexpr int kArgThreads = 256;
-constexpr int kArgUnroll = 8;  // 16-byte loads in flight per thread
+constexpr int kArgThreads = 512;
+constexpr int kArgUnroll = 4;  // 16-byte loads per thread and pass (more measured slower)
 constexpr int kFinThreads = 256;
 constexpr int kMaxRowsPerReq = 64;
 constexpr int kKeysPerThread = 16;  // victim keys held in registers up to 4096 slots
@@ -50,13 +50,15 @@ __global__ __launch_bounds__(kArgThreads) void argmax_kernel(const uint16_t *__r
   float bv = -INFINITY;
   int bi = 0x7fffffff;
   if ((vocab & 7) == 0) {
-    const int chunks = vocab >> 3;
+    const int chunks = vocab >> 3;  // >= 1: the host rejects vocab <= 0
     for (int c0 = tid; c0 < chunks; c0 += kArgThreads * kArgUnroll) {
+      // Every load of the pass is issued before any is used: chunks past the end re-load
+      // the last chunk (no branch around a load) and are skipped below.
       i32x4 raw[kArgUnroll];
 #pragma unroll
       for (int k = 0; k < kArgUnroll; ++k) {
-        const int c = c0 + k * kArgThreads;
-        raw[k] = c < chunks ? *reinterpret_cast<const i32x4 *>(lr + 8 * c) : i32x4{0, 0, 0, 0};
+        const int c = min(c0 + k * kArgThreads, chunks - 1);
+        raw[k] = *reinterpret_cast<const i32x4 *>(lr + 8 * c);
       }
 #pragma unroll
       for (int k = 0; k < kArgUnroll; ++k) {
@@ -130,9 +132,13 @@ __global__ __launch_bounds__(kFinThreads) void finalize_kernel(
     const int32_t *__restrict__ argmax, int32_t *__restrict__ out_accept_len,
     int32_t *__restrict__ out_next_token) {
   __shared__ int s_L;
-  __shared__ int s_loc[kMaxRowsPerReq];
+  __shared__ int s_loc[kMaxRowsPerReq];    // host row of each verify row, -1 none
+  __shared__ int s_hit[kMaxRowsPerReq];    // slot within the request holding the row, -1 none
   __shared__ int s_slot[kMaxRowsPerReq];   // slot within the request for kept rows, -1 none
+  __shared__ int s_owner[kMaxRowsPerReq];  // host row the slot of a missed kept row held
   __shared__ int s_miss[kMaxRowsPerReq];   // kept rows that must be installed
+  __shared__ int s_vic[kMaxRowsPerReq];    // victims in LRU order
+  __shared__ int s_vown[kMaxRowsPerReq];   // host row each victim held
   __shared__ int s_nmiss;
   __shared__ uint64_t s_red[kFinThreads / 64];
 
@@ -140,12 +146,58 @@ __global__ __launch_bounds__(kFinThreads) void finalize_kernel(
   const int tid = threadIdx.x;
   const int R = rows_per_req;
   const int64_t slot_base = (int64_t)b * capacity;
+  auto slot_key = [&](int sl, int stamp) -> uint64_t {
+    return (static_cast<uint64_t>(static_cast<uint32_t>(stamp) ^ 0x80000000u) << 32) |
+           static_cast<uint32_t>(sl);
+  };
+
+  // Loads first, uses after: the acceptance inputs, the verify rows' block-table entries,
+  // then (up to 4096 slots) the request's (stamp, slot) keys and slot owners, which depend
+  // on nothing here.  Loads complete in issue order, so the key loads go last and do not
+  // delay the reads the acceptance length and host rows wait for.  This kernel's own slot
+  // updates are applied to the register copies as it makes them.
+  // (Row indices are clamped into range so that no load sits behind a branch; the
+  // clamped lanes' values are masked when used.)
+  const int draft_next = draft_ids[(int64_t)min(tid + 1, R - 1) * num_reqs + b];
+  const int am_row = argmax[(int64_t)min(tid, R - 1) * num_reqs + b];
+  // host row of position seq_len - R + tid (same block-table mapping as resolve_topk)
+  const int pos = seq_len[b] - R + tid;
+  const int pi = pos >= 0 ? pos / block_size : 0;
+  const int page_raw = block_table[(int64_t)b * bt_stride + min(pi, bt_stride - 1)];
+  // masked with an OR, not a select (a select on a load's value compiles to a branch
+  // around the load)
+  const int page = page_raw | -static_cast<int>(!(tid < R && pos >= 0 && pi < bt_stride));
+  // this thread's first chunk of the verify rows' new KV (chunk tid of rows 0 .. R-1)
+  const int chunks = row_bytes >> 4;
+  const int c_first = min(tid, R * chunks - 1);
+  const int r_first = c_first / chunks;
+  const i32x4 kv_first = *reinterpret_cast<const i32x4 *>(
+      new_kv + ((int64_t)r_first * num_reqs + b) * row_bytes + (c_first - r_first * chunks) * 16);
+  const bool in_regs = capacity <= kFinThreads * kKeysPerThread;
+  uint64_t keys[kKeysPerThread];
+  int owner[kKeysPerThread];
+  if (in_regs) {
+    // slots past the capacity re-read the last slot (no branch around a load: every load
+    // is issued before the first wait) and are masked after
+    int stamp[kKeysPerThread];
+#pragma unroll
+    for (int i = 0; i < kKeysPerThread; ++i) {
+      const int64_t g = slot_base + min(tid + i * kFinThreads, capacity - 1);
+      stamp[i] = slot_stamp[g];
+      owner[i] = slot_loc[g];
+    }
+#pragma unroll
+    for (int i = 0; i < kKeysPerThread; ++i) {
+      const int sl = tid + i * kFinThreads;
+      keys[i] = sl < capacity ? slot_key(sl, stamp[i]) : ~0ull;
+      owner[i] = sl < capacity ? owner[i] : -1;
+    }
+  }
 
   // Acceptance length, wave-parallel (R <= 64): lane r checks draft r+1 against the argmax
   // of row r; L is the number of leading matches.
   if (tid < 64) {
-    const bool match = tid < R - 1 && draft_ids[(int64_t)(tid + 1) * num_reqs + b] ==
-                                          argmax[(int64_t)tid * num_reqs + b];
+    const bool match = tid < R - 1 && draft_next == am_row;
     const uint64_t mism = ~__builtin_amdgcn_ballot_w64(match);
     const int L = min(static_cast<int>(__builtin_ctzll(mism)), R - 1);
     if (tid == 0) {
@@ -155,60 +207,62 @@ __global__ __launch_bounds__(kFinThreads) void finalize_kernel(
     }
   }
   if (tid < R) {
-    // host row of position seq_len - R + tid (same block-table mapping as resolve_topk)
-    const int pos = seq_len[b] - R + tid;
     int loc = -1;
-    if (pos >= 0) {
-      const int pi = pos / block_size;
-      if (pi < bt_stride) {
-        const int page = block_table[(int64_t)b * bt_stride + pi];
-        if (page >= 0) {
-          const int64_t r = (int64_t)page * block_size + (pos - pi * block_size);
-          loc = r < host_rows ? (int)r : -1;
-        }
-      }
+    if (page >= 0) {
+      const int64_t r = (int64_t)page * block_size + (pos - pi * block_size);
+      loc = r < host_rows ? (int)r : -1;
     }
     s_loc[tid] = loc;
-    s_slot[tid] = -1;
   }
   __syncthreads();
   const int L = s_L;
-  const int chunks = row_bytes >> 4;
+
+  // The slot each verify row occupies, looked up once (the rows' host rows are distinct,
+  // so emptying a dropped row's slot cannot change a kept row's lookup).
+  if (tid < R) {
+    const int loc = s_loc[tid];
+    const int64_t g = loc >= 0 ? loc_to_hot[loc] : -1;
+    s_hit[tid] = g >= slot_base && g < slot_base + capacity ? (int)(g - slot_base) : -1;
+    s_slot[tid] = -1;
+  }
 
   // kept rows' new KV -> their host-pool rows (device stores over the host link); issued
-  // first so the link transfer overlaps the slot bookkeeping below
+  // early so the link transfer overlaps the slot bookkeeping below
   for (int c = tid; c < (L + 1) * chunks; c += kFinThreads) {
     const int r = c / chunks;
     const int part = c - r * chunks;
     const int loc = s_loc[r];
     if (loc < 0) continue;
-    const i32x4 v = *reinterpret_cast<const i32x4 *>(new_kv + ((int64_t)r * num_reqs + b) * row_bytes + part * 16);
+    const i32x4 v = c == tid ? kv_first : *reinterpret_cast<const i32x4 *>(
+        new_kv + ((int64_t)r * num_reqs + b) * row_bytes + part * 16);
     *reinterpret_cast<i32x4 *>(host_pool + (int64_t)loc * row_bytes + part * 16) = v;
   }
+  __syncthreads();
 
   // dropped rows: empty the slot that holds them (host rows untouched)
-  if (tid < R && tid > L) {
-    const int loc = s_loc[tid];
-    if (loc >= 0) {
-      const int g = loc_to_hot[loc];
-      if (g >= slot_base && g < slot_base + capacity) {
-        slot_loc[g] = -1;
-        slot_stamp[g] = -1;
-        loc_to_hot[loc] = -1;
-      }
+  if (tid < R && tid > L && s_hit[tid] >= 0) {
+    const int64_t g = slot_base + s_hit[tid];
+    slot_loc[g] = -1;
+    slot_stamp[g] = -1;
+    loc_to_hot[s_loc[tid]] = -1;
+  }
+  if (in_regs) {
+    for (int r = L + 1; r < R; ++r) {
+      const int sl = s_hit[r];
+#pragma unroll
+      for (int i = 0; i < kKeysPerThread; ++i)
+        if (sl >= 0 && tid + i * kFinThreads == sl) {
+          keys[i] = slot_key(sl, -1);
+          owner[i] = -1;
+        }
     }
   }
-  __syncthreads();
   // kept rows (wave-parallel): hit -> its slot (pinned), miss -> listed in row order
   if (tid < 64) {
     const int r = tid;
-    const int loc = r <= L && r < R ? s_loc[r] : -1;
-    bool miss = false;
-    if (loc >= 0) {
-      const int g = loc_to_hot[loc];
-      if (g >= slot_base && g < slot_base + capacity) s_slot[r] = (int)(g - slot_base);
-      else miss = true;
-    }
+    const bool kept = r <= L && r < R && s_loc[r] >= 0;
+    const bool miss = kept && s_hit[r] < 0;
+    if (kept && !miss) s_slot[r] = s_hit[r];
     const uint64_t mm = __builtin_amdgcn_ballot_w64(miss);
     if (miss) s_miss[__builtin_popcountll(mm & ((1ull << r) - 1))] = r;
     if (tid == 0) s_nmiss = __builtin_popcountll(mm);
@@ -216,21 +270,9 @@ __global__ __launch_bounds__(kFinThreads) void finalize_kernel(
   __syncthreads();
   const int nmiss = s_nmiss;
 
-  // victims: repeatedly the least-recently-used unpinned, unchosen slot (nmiss <= R).  Up
-  // to 4096 slots the (stamp, slot) keys stay in registers: one pass of loads, then nmiss
-  // block minima.  (A candidate always exists when rows_per_req <= capacity, which the
-  // host checks.)
-  auto slot_key = [&](int sl) -> uint64_t {
-    return (static_cast<uint64_t>(static_cast<uint32_t>(slot_stamp[slot_base + sl]) ^ 0x80000000u) << 32) |
-           static_cast<uint32_t>(sl);
-  };
-  if (nmiss > 0 && capacity <= kFinThreads * kKeysPerThread) {
-    uint64_t keys[kKeysPerThread];
-#pragma unroll
-    for (int i = 0; i < kKeysPerThread; ++i) {
-      const int sl = tid + i * kFinThreads;
-      keys[i] = sl < capacity ? slot_key(sl) : ~0ull;
-    }
+  // victims: repeatedly the least-recently-used unpinned, unchosen slot (nmiss <= R).  (A
+  // candidate always exists when rows_per_req <= capacity, which the host checks.)
+  if (nmiss > 0 && in_regs) {
     for (int r = 0; r <= L; ++r) {  // kept hits are pinned
       const int ps = s_slot[r];
 #pragma unroll
@@ -242,43 +284,50 @@ __global__ __launch_bounds__(kFinThreads) void finalize_kernel(
 #pragma unroll
       for (int i = 0; i < kKeysPerThread; ++i) best = keys[i] < best ? keys[i] : best;
       best = block_min_u64(best, s_red);
+      if (tid == 0 && best == ~0ull) s_vic[k] = -1;
 #pragma unroll
       for (int i = 0; i < kKeysPerThread; ++i)
-        if (keys[i] == best) keys[i] = ~0ull;  // chosen: not a candidate again
-      if (tid == 0) s_slot[s_miss[k]] = best == ~0ull ? -1 : static_cast<int>(best & 0xffffffffu);
+        if (keys[i] == best && best != ~0ull) {  // chosen: not a candidate again
+          keys[i] = ~0ull;
+          s_vic[k] = tid + i * kFinThreads;
+          s_vown[k] = owner[i];
+        }
     }
     __syncthreads();
-  } else {
+  } else if (nmiss > 0) {
     for (int k = 0; k < nmiss; ++k) {
       uint64_t best = ~0ull;
       for (int sl = tid; sl < capacity; sl += kFinThreads) {
         bool taken = false;
         for (int r = 0; r <= L; ++r) taken |= s_slot[r] == sl;
+        for (int j = 0; j < k; ++j) taken |= s_vic[j] == sl;
         if (taken) continue;
-        const uint64_t key = slot_key(sl);
+        const uint64_t key = slot_key(sl, slot_stamp[slot_base + sl]);
         best = key < best ? key : best;
       }
       best = block_min_u64(best, s_red);
-      if (tid == 0) s_slot[s_miss[k]] = best == ~0ull ? -1 : static_cast<int>(best & 0xffffffffu);
+      if (tid == 0) {
+        const int v = best == ~0ull ? -1 : static_cast<int>(best & 0xffffffffu);
+        s_vic[k] = v;
+        s_vown[k] = v >= 0 ? slot_loc[slot_base + v] : -1;
+      }
       __syncthreads();
     }
   }
   // Victims were chosen in LRU order; pair them with the misses in ascending slot order:
-  // miss k takes the victim of rank k (victims are distinct slots).  One wave; every lane
-  // reads all victims before any lane writes.
-  if (tid < 64 && nmiss > 1) {
-    const int v = tid < nmiss ? s_slot[s_miss[tid]] : 0x7fffffff;
+  // miss k takes the victim of rank k (victims are distinct slots).
+  if (tid < nmiss) {
+    const int v = s_vic[tid];
     int rank = 0;
-    for (int j = 0; j < nmiss; ++j) rank += s_slot[s_miss[j]] < v;
-    __builtin_amdgcn_wave_barrier();
-    if (tid < nmiss) s_slot[s_miss[rank]] = v;
+    for (int j = 0; j < nmiss; ++j) rank += s_vic[j] < v;
+    s_slot[s_miss[rank]] = v;
+    s_owner[s_miss[rank]] = s_vown[tid];
   }
   __syncthreads();
   if (tid < nmiss && s_slot[s_miss[tid]] >= 0) {
     const int r = s_miss[tid];
-    const int v = s_slot[r];
-    const int64_t g = slot_base + v;
-    const int old = slot_loc[g];
+    const int64_t g = slot_base + s_slot[r];
+    const int old = s_owner[r];
     if (old >= 0 && old < host_rows) loc_to_hot[old] = -1;
     slot_loc[g] = s_loc[r];
     loc_to_hot[s_loc[r]] = (int32_t)g;
@@ -289,7 +338,8 @@ __global__ __launch_bounds__(kFinThreads) void finalize_kernel(
     const int r = c / chunks;
     const int part = c - r * chunks;
     if (s_loc[r] < 0 || s_slot[r] < 0) continue;
-    const i32x4 v = *reinterpret_cast<const i32x4 *>(new_kv + ((int64_t)r * num_reqs + b) * row_bytes + part * 16);
+    const i32x4 v = c == tid ? kv_first : *reinterpret_cast<const i32x4 *>(
+        new_kv + ((int64_t)r * num_reqs + b) * row_bytes + part * 16);
     *reinterpret_cast<i32x4 *>(hot_kv + (slot_base + s_slot[r]) * row_bytes + part * 16) = v;
   }
 }

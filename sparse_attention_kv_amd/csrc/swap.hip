@@ -244,23 +244,23 @@ __global__ __launch_bounds__(kThreads) void swap_in_kernel(
   const int total = need * chunks;
   constexpr int kUnroll = 8;
   for (int base = 0; base < total; base += kThreads * kUnroll) {
+    // All kUnroll loads are issued before the first store: chunks past the end re-read the
+    // last chunk (no branch around a load, which would make each load wait for the one
+    // before it) and are not stored.
     i32x4 v[kUnroll];
     int64_t dst[kUnroll];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-      const int c = base + u * kThreads + tid;
-      dst[u] = -1;
-      if (c < total) {
-        const int mi = c / chunks;
-        const int part = c - mi * chunks;
-        const int64_t src = (int64_t)sm.miss_row[mi] * row_bytes + part * 16;
-        v[u] = *reinterpret_cast<const i32x4 *>(host_pool + src);
-        dst[u] = (slot_base + sm.victim[mi]) * row_bytes + part * 16;
-      }
+      const int c = min(base + u * kThreads + tid, total - 1);
+      const int mi = c / chunks;
+      const int part = c - mi * chunks;
+      const int64_t src = (int64_t)sm.miss_row[mi] * row_bytes + part * 16;
+      v[u] = *reinterpret_cast<const i32x4 *>(host_pool + src);
+      dst[u] = (slot_base + sm.victim[mi]) * row_bytes + part * 16;
     }
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u)
-      if (dst[u] >= 0) *reinterpret_cast<i32x4 *>(hot_kv + dst[u]) = v[u];
+      if (base + u * kThreads + tid < total) *reinterpret_cast<i32x4 *>(hot_kv + dst[u]) = v[u];
   }
 }
 

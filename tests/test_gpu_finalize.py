@@ -113,6 +113,69 @@ def test_finalize_random_requests(vocab):
     log(f"accept lengths {acc.tolist()}")
 
 
+
+@pytest.mark.parametrize("vocab", [129280, 129281, 8, 9])
+def test_argmax_special_values(vocab):
+    """Argmax rows with NaN, -inf, all-NaN and all -inf rows, the maximum in the first or
+    the last element, and ties between the first and a later pass of the kernel's loads:
+    the lowest index of the maximum, NaN never winning (an all-NaN row gives 0)."""
+    B, R, cap, bs, width = 4, 3, 16, 8, 4
+    rows = B * R
+    gen = torch.Generator().manual_seed(vocab)
+    logits = torch.randn(rows, vocab, generator=gen).to(torch.bfloat16)
+    nan, inf = float("nan"), float("inf")
+    logits[0, :] = -inf                                   # all -inf: index 0
+    logits[1, :] = nan                                    # all NaN: index 0
+    logits[2, 0] = nan; logits[2, vocab - 1] = 50.0       # maximum in the last element
+    logits[3, 0] = 50.0; logits[3, 1:] = nan              # maximum first, NaN after
+    logits[4, :] = -inf; logits[4, vocab // 2] = nan      # NaN among -inf: index 0
+    if vocab > 9000:                                      # equal maxima 8704 apart, and at
+        logits[5, 8704 + 3] = 40.0; logits[5, 3] = 40.0  # the start of a later pass
+        logits[6, vocab - 2] = 40.0; logits[6, 4096 * 8 + 1] = 40.0
+    logits[7, :] = 0.0; logits[7, 5:] = -0.0              # +0 and -0 compare equal: index 0
+    seq = np.full(B, width * bs - 2, np.int32)
+    bt = np.arange(B * width, dtype=np.int32).reshape(B, width)
+    rng = np.random.default_rng(vocab)
+    pool = rng.standard_normal((B * width * bs, 8)).astype(np.float32)
+    init_pos = np.full((B, cap), -1, np.int32)
+    init_stamp = np.full((B, cap), -1, np.int32)
+    draft = rng.integers(0, vocab, size=rows).astype(np.int32)
+    new_kv = rng.standard_normal((rows, 8)).astype(np.float32)
+    _run_finalize(B, R, cap, seq, bt, bs, pool, init_pos, init_stamp, logits, draft, new_kv,
+                  tick=7)
+
+
+def test_finalize_capacity_beyond_register_keys():
+    """More than 4096 hot slots per request: the victim search reads the stamps from
+    memory instead of registers; nearly full buffers so every miss evicts."""
+    rng = np.random.default_rng(4099)
+    B, R, cap, bs, width = 3, 4, 4500, 64, 80
+    bt = rng.permutation(B * width).astype(np.int32).reshape(B, width)
+    seq = rng.integers(4600, width * bs, size=B).astype(np.int32)
+    pool = rng.standard_normal((B * width * bs, 8)).astype(np.float32)
+    init_pos = np.full((B, cap), -1, np.int32)
+    init_stamp = np.full((B, cap), -1, np.int32)
+    for b in range(B):
+        pos = rng.choice(int(seq[b]) - R, cap, replace=False)   # full; no verify row resident
+        init_pos[b] = pos
+        init_stamp[b] = rng.integers(0, 50, size=cap)
+        if b == 1:                                               # two verify rows resident
+            init_pos[b, 17] = seq[b] - R
+            init_pos[b, 4400] = seq[b] - 1
+    vocab = 1000
+    gen = torch.Generator().manual_seed(1)
+    logits = torch.randn(B * R, vocab, generator=gen).to(torch.bfloat16)
+    plant = rng.integers(0, vocab, size=B * R)
+    logits[torch.arange(B * R), torch.from_numpy(plant)] = 9.0
+    draft = rng.integers(0, vocab, size=B * R).astype(np.int32)
+    for b in range(B):                                           # accept lengths 3, 1, 2
+        for r in range(1, [4, 2, 3][b]):
+            draft[r * B + b] = plant[(r - 1) * B + b]
+    new_kv = rng.standard_normal((B * R, 8)).astype(np.float32)
+    acc, *_ = _run_finalize(B, R, cap, seq, bt, bs, pool, init_pos, init_stamp, logits, draft,
+                            new_kv, tick=60)
+    assert acc.tolist() == [3, 1, 2]
+
 def test_attention_identical_on_resident_and_swap_paths():
     """Same rows, same index order: the paged pool and the hot buffer give equal bits."""
     import sparse_attention_kv_amd as hs
