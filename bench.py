@@ -116,7 +116,8 @@ def measure_swap(dev, reps=5):
     """Swap path on the 32-request MTP workload (4 rows per request, top-k 2048, 4096 hot
     slots per request, 1.21 GB pinned host pool): host-link reference rate, swap-in
     kernel rates and the whole step.  Hot state is restored from a device snapshot before
-    every repetition (not timed)."""
+    every repetition (not timed).  Each timed region starts behind a short spin kernel, so
+    it measures device time, not the host-side marshalling of the first call."""
     import numpy as np
     import torch
 
@@ -174,6 +175,7 @@ def measure_swap(dev, reps=5):
     for rep in range(reps + 2):
         restore()
         torch.cuda.synchronize()
+        gpu_busy()
         e0.record(main)
         run()
         main.wait_stream(copy)
@@ -201,6 +203,7 @@ def measure_swap(dev, reps=5):
     for rep in range(reps + 2):
         restore()
         torch.cuda.synchronize()
+        gpu_busy()
         e0.record(main)
         mstep.run_mixed(st, topk_pos, req_res, req_swap, sel, lim, res_bt, bt, s.block_size, q,
                         dev_pool, s.scale, s.tick0)
@@ -225,6 +228,7 @@ def measure_swap(dev, reps=5):
         for r in range(s.rows_per_req):
             lo, hi = r * s.num_reqs, (r + 1) * s.num_reqs
             a, z = ev(), ev()
+            gpu_busy()
             a.record(main)
             hs.hs_swap_in(st, b.slots[lo:hi], s.tick0 + r, b.hot_idx[lo:hi], b.miss_count[r])
             z.record(main)
@@ -254,6 +258,7 @@ def measure_swap(dev, reps=5):
     for r in range(s.rows_per_req):
         lo, hi = r * s.num_reqs, (r + 1) * s.num_reqs
         a, m, z = ev(), ev(), ev()
+        gpu_busy()
         a.record(main)
         hs.hs_swap_in(st, b.slots[lo:hi], s.tick0 + r, b.hot_idx[lo:hi], b.miss_count[r], mpos)
         m.record(main)
@@ -271,6 +276,7 @@ def measure_swap(dev, reps=5):
     st.slot_stamp.fill_(-1)
     st.loc_to_hot.fill_(-1)
     a, z = ev(), ev()
+    gpu_busy()
     a.record(main)
     hs.hs_swap_in(st, b.slots[0:s.num_reqs], s.tick0, b.hot_idx[0:s.num_reqs], b.miss_count[0])
     z.record(main)
