@@ -307,6 +307,57 @@ def gpu_busy(us=100.0):
     torch.cuda._sleep(int(us * 2000))  # spin kernel counting shader clocks (~2 GHz)
 
 
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+
+def measure_attn_sweep(dev, sizes=(32, 64, 128, 256), reps=50):
+    """The attention op alone at the batch sizes of the other workloads: one swap wave of
+    the MTP workload (32 rows), of the long-context workload (64), of the mixed workload
+    (128), and the long-context workload's 256 rows at once.  Top-k 2048 distinct rows per
+    query row, drawn uniformly from a resident pool of 1M bf16 576-wide latent rows
+    (1.15 GB, N(0,1)); 128 heads, value = first 512 dims, scale 1/sqrt(576).  Each size is
+    timed over back-to-back calls; the kernel (32-, 64- or 128-head workgroups) is the
+    library planner's choice."""
+    import torch
+
+    import sparse_attention_kv_amd as hs
+    H, D, DV, K, N = 128, 576, 512, 2048, 1 << 20
+    g = torch.Generator(device=dev).manual_seed(20261202)
+    kv = torch.randn((N, D), generator=g, device=dev).to(torch.bfloat16)
+    main = torch.cuda.current_stream()
+    out_rows = []
+    for rows in sizes:
+        q = torch.randn((rows, H, D), generator=g, device=dev).to(torch.bfloat16)
+        idx = torch.stack([torch.randperm(N, generator=g, device=dev)[:K] for _ in range(rows)])
+        idx = idx.to(torch.int32).contiguous()
+        out = torch.empty((rows, H, DV), dtype=torch.bfloat16, device=dev)
+        lse = torch.empty((rows, H), dtype=torch.float32, device=dev)
+        wsb = hs.hs_attn_workspace_bytes(rows, H, D, DV, K, torch.bfloat16)
+        ws = torch.empty((max(wsb, 16),), dtype=torch.uint8, device=dev) if wsb else None
+        for _ in range(5):
+            hs.hs_sparse_decode_attn(q, kv, idx, D ** -0.5, DV, out, lse, ws)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(main)
+        for _ in range(reps):
+            hs.hs_sparse_decode_attn(q, kv, idx, D ** -0.5, DV, out, lse, ws)
+        e1.record(main)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / reps
+        alg = attn_alg_bytes([K] * rows, H, D, DV, K)
+        flops = rows * K * 2 * H * (D + DV)
+        out_rows.append({"rows": rows, "us": us, "rows_per_s": rows / (us / 1e6),
+                         "GBps": alg / (us / 1e6) / 1e9,
+                         "hbm_frac": alg / (us / 1e6) / 1e9 / HBM_PEAK_GBS,
+                         "TFLOPs": flops / (us / 1e6) / 1e12,
+                         "mfma_frac": flops / (us / 1e6) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+                         "split_workspace_bytes": wsb})
+        del q, idx, out, lse, ws
+    del kv
+    return {"workload": "attention op alone, top-k 2048 distinct rows of a 1M-row resident "
+                        "pool, 128 heads x 576/512 bf16", "sizes": out_rows}
+
+
 def measure_finalize(dev, reps=10):
     """Greedy accept + accepted-prefix finalize on the mixed workload's verify shape: 128
     requests x 3 rows, logits [384, 129280] bf16 (99.3 MB), 4096 hot slots per request.
@@ -457,6 +508,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--no-swap", action="store_true", help="skip the swap-path measurement")
+    ap.add_argument("--no-sweep", action="store_true",
+                    help="skip the attention sweep over larger batches")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
@@ -589,6 +642,9 @@ def main():
                      "alg_bytes_per_launch": alg,
                      "launch_us": attn_t * 1e3},
     }
+    if not args.no_sweep:
+        log("attention sweep")
+        res["attn_sweep"] = measure_attn_sweep(dev)
     if not args.no_swap:
         log("swap path")
         res["swap_in"] = measure_swap(dev)
