@@ -220,15 +220,16 @@ __global__ __launch_bounds__(kThreads, 1) void attn128_kernel(
   };
 
   // The inner loop touches O only through MFMA.  The first block sets the reference (O is
-  // still zero); a later block that needs a new one leaves the loop, O is rescaled outside,
-  // and the loop resumes.  That rare path re-reads Q afterwards, so Q's registers are free
-  // while it runs.
+  // still zero); a later block that needs a new one jumps out of the loop, O is rescaled
+  // outside, and the loop resumes.  That rare path re-reads Q afterwards, so Q's registers
+  // are free while it runs.  It is entered by a jump of its own, not through the loop's
+  // normal exit: the compiler puts the rare path's register spills on the edge into it, and
+  // on a shared exit block they ran once per launch (≈764 B per lane, 50 MB at 256 rows).
   const int nblocks = 2 * ntiles;
   int b = 0;
   float s[16];
   float alpha = 1.f;
-  while (b < nblocks) {
-    bool renorm = false;
+  for (;;) {
     for (; b < nblocks; ++b) {
       const int t = b >> 1, kb = b & 1;
       const uint8_t *cur = s_kv + (t & 1) * kTileBytes;
@@ -297,10 +298,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn128_kernel(
         alpha = over ? __builtin_amdgcn_exp2f(m_ref - mx) : 1.f;
         m_ref = over ? mx : m_ref;
         l_run *= alpha;
-        if (b > 0) {
-          renorm = true;
-          break;
-        }
+        if (b > 0) goto rare;
       }
       float p[16];
 #pragma unroll
@@ -310,7 +308,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn128_kernel(
       }
       pv_block(cur, kb, p);
     }
-    if (!renorm) break;
+    break;  // every block done
+  rare:
     // ---- rare path: rescale O by this lane's head factor, then this block's P V ----
 #pragma unroll
     for (int nb = 0; nb < kNB; ++nb) {

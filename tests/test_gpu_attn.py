@@ -206,6 +206,41 @@ def test_attn_bf16_128head_path_zero_query_and_large_scores():
     _check_sampled(q, kv, to_dev(idx), 1 / 24, 512, "128-head zero query / large scores", _SAMPLE128)
 
 
+
+@pytest.mark.parametrize("rows", [8, 128, 256])
+def test_attn_reference_moves_at_later_keys(rows):
+    """Forces every kernel's rare path (8 rows: 32-head, 128: 64-head, 256: 128-head).  In
+    the special rows all heads share one query direction, and keys along it are planted at
+    later positions with scores (log2 domain) near 100, 200, 300 and 400, each beyond the
+    reference slack, so the reference moves and O is rescaled after the first block, more
+    than once, and last at the final block."""
+    H, kv_rows, topk = 128, 9000, 2048
+    rng = np.random.default_rng(4400 + rows)
+    q = _rand_bf16((rows, H, 576), 4500 + rows).cpu()
+    kv = _rand_bf16((kv_rows, 576), 4600 + rows).cpu()
+    idx = np.stack([rng.choice(kv_rows - 64, topk, replace=False) for _ in range(rows)]).astype(np.int32)
+    special = [0, 1, rows // 2, rows - 1]
+    for j, r in enumerate(special):
+        base = torch.randn((576,), generator=torch.Generator().manual_seed(4700 + j))
+        q[r] = (base[None, :] + 0.1 * torch.randn((H, 576), generator=torch.Generator().manual_seed(4800 + j))).to(torch.bfloat16)
+        # |base|^2 ~ 576: score(c * base) ~ c * 24 (natural) ~ c * 34.6 (log2)
+        for c, pos in zip((3.0, 6.0, 9.0, 12.0), (40 + j, 300 + 7 * j, 1100 + j, topk - 1 - j)):
+            row = kv_rows - 64 + 16 * j + int(c)
+            kv[row] = (c * base).to(torch.bfloat16)
+            idx[r, pos] = row
+        # the condition the test is for: each planted key's score exceeds the maximum over
+        # the row's first 32 keys by more than the kernels' 64 (log2) slack, in every head
+        qf, kf = raw(q[r]).astype(np.uint32), raw(kv).astype(np.uint32)
+        qv = (qf << 16).view(np.float32).astype(np.float64)
+        kvv = (kf << 16).view(np.float32).astype(np.float64)
+        s2 = (qv @ kvv[idx[r]].T) / 24 * np.log2(np.e)          # [H, topk], log2 domain
+        first = s2[:, :32].max(axis=1)
+        for pos in (300 + 7 * j, 1100 + j, topk - 1 - j):
+            assert (s2[:, pos] > first + 64).all() and (s2[:, pos] >= s2[:, :pos].max(axis=1) + 64).all()
+    sample = sorted(set(special + [2, rows // 3]))
+    _check_sampled(q.to(dev()), kv.to(dev()), to_dev(idx), 1 / 24, 512,
+                   f"reference moves, {rows} rows", sample)
+
 def test_attn_deterministic_and_index_order_invariant():
     s, w = make("resident", num_reqs=4)
     g = gpu_inputs(s, w)
