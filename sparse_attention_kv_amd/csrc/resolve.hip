@@ -7,7 +7,8 @@
 //
 // One 1024-thread workgroup per query row.  Consecutive lanes read consecutive int32
 // positions (coalesced); a thread's position loads, then its block-table loads, are all
-// issued before any result is used, so a row costs about two memory round trips.  The
+// issued before any result is used (none behind a branch), so a row costs about two memory
+// round trips.  The
 // block-table row of a request is small (<= 8 KB) and stays in L2.
 // Output keeps -1 in place (no compaction); the valid count is a block reduction.
 
@@ -37,16 +38,20 @@ __global__ __launch_bounds__(kThreads) void resolve_topk_kernel(
   int count = 0;
   for (int base = 0; base < topk; base += kThreads * kPer) {
     int t[kPer], page_idx[kPer], page[kPer];
+    // No load sits behind a branch (the compiler would wait for each before the next):
+    // indices are clamped into range and the results masked afterwards.
 #pragma unroll
     for (int k = 0; k < kPer; ++k) {
       const int j = base + k * kThreads + threadIdx.x;
-      t[k] = j < topk ? in[j] : -1;
+      const int tj = in[min(j, topk - 1)];
+      t[k] = j < topk ? tj : -1;
     }
 #pragma unroll
     for (int k = 0; k < kPer; ++k) {
       const bool ok = req_ok && t[k] >= 0 && t[k] < lim;
-      page_idx[k] = ok ? t[k] / block_size : bt_stride;
-      page[k] = page_idx[k] < bt_stride ? bt[page_idx[k]] : -1;
+      page_idx[k] = ok ? t[k] / block_size : 0;
+      const int raw = bt[min(page_idx[k], bt_stride - 1)];
+      page[k] = raw | -static_cast<int>(!(ok && page_idx[k] < bt_stride));  // OR, not a select
     }
 #pragma unroll
     for (int k = 0; k < kPer; ++k) {
