@@ -32,28 +32,32 @@ __global__ __launch_bounds__(kThreads) void backup_rows_kernel(
   const int64_t stride = (int64_t)gridDim.x * kThreads * kUnroll;
   for (int64_t base = (int64_t)blockIdx.x * kThreads * kUnroll + threadIdx.x; base < total_chunks;
        base += stride) {
+    // Two phases, every load of a phase issued before any result is used and none behind a
+    // branch (the compiler would wait for each before the next): the entries' slot and row
+    // indices, then the rows' chunks.  Out-of-range positions are clamped and not stored.
+    int src[kUnroll], drow[kUnroll], layer[kUnroll], part[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int64_t c = min(base + (int64_t)u * kThreads, total_chunks - 1);
+      const int64_t r = c / chunks;  // (layer, entry) pair
+      part[u] = (int)(c - r * chunks);
+      layer[u] = (int)(r / num_rows);
+      const int i = (int)(r - (int64_t)layer[u] * num_rows);
+      src[u] = src_slots[(src_per_layer ? (int64_t)layer[u] * num_rows : 0) + i];
+      drow[u] = dst_rows[i];
+    }
     i32x4 v[kUnroll];
     int64_t dst[kUnroll];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-      const int64_t c = base + (int64_t)u * kThreads;
-      dst[u] = -1;
-      if (c < total_chunks) {
-        const int64_t r = c / chunks;  // (layer, entry) pair
-        const int part = (int)(c - r * chunks);
-        const int layer = (int)(r / num_rows);
-        const int i = (int)(r - (int64_t)layer * num_rows);
-        const int s = src_slots[(src_per_layer ? (int64_t)layer * num_rows : 0) + i];
-        const int d = dst_rows[i];
-        if (s >= 0 && d >= 0 && d < host_layer_rows) {
-          const int64_t p = (int64_t)(s / src_block_size) * src_block_stride + s % src_block_size;
-          if (p < dev_layer_rows) {
-            v[u] = *reinterpret_cast<const i32x4 *>(
-                dev_cache + ((int64_t)layer * dev_layer_rows + p) * row_bytes + part * 16);
-            dst[u] = ((int64_t)layer * host_layer_rows + d) * row_bytes + part * 16;
-          }
-        }
-      }
+      const int sl = src[u], d = drow[u];
+      bool ok = base + (int64_t)u * kThreads < total_chunks && sl >= 0 && d >= 0 &&
+                d < host_layer_rows;
+      const int64_t p = ok ? (int64_t)(sl / src_block_size) * src_block_stride + sl % src_block_size : 0;
+      ok = ok && p < dev_layer_rows;
+      v[u] = *reinterpret_cast<const i32x4 *>(
+          dev_cache + ((int64_t)layer[u] * dev_layer_rows + (ok ? p : 0)) * row_bytes + part[u] * 16);
+      dst[u] = ok ? ((int64_t)layer[u] * host_layer_rows + d) * row_bytes + part[u] * 16 : -1;
     }
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u)

@@ -7,7 +7,7 @@
 // assignment) needs only those rows copied from its own host pool into its own hot buffer.
 //
 // Grid (request, kSlices): the slices of a request split its (cache, miss, 16-byte chunk)
-// work; each thread keeps kUnroll host-link loads in flight before it stores to HBM.
+// work; each thread issues its kUnroll host-link loads together before it stores to HBM.
 
 #include "ops.h"
 
@@ -15,7 +15,7 @@ namespace hs {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kUnroll = 8;
+constexpr int kUnroll = 2;  // more in flight measured slower (the host link saturates)
 constexpr int kSlices = 8;
 
 __global__ __launch_bounds__(kThreads) void apply_plan_kernel(
@@ -33,28 +33,36 @@ __global__ __launch_bounds__(kThreads) void apply_plan_kernel(
   const int64_t stride = (int64_t)kSlices * kThreads * kUnroll;
   for (int64_t base = (int64_t)blockIdx.y * kThreads * kUnroll + threadIdx.x; base < total;
        base += stride) {
+    // Three phases, every load of a phase issued before any result is used and none behind
+    // a branch (the compiler would wait for each before the next): the missed entries, their
+    // host rows and hot indices, then the rows' chunks.  Out-of-range positions are clamped
+    // and not stored.
+    int cache[kUnroll], part[kUnroll], e[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int64_t f = min(base + (int64_t)u * kThreads, total - 1);
+      cache[u] = (int)(f / per_cache);
+      const int64_t rem = f - (int64_t)cache[u] * per_cache;
+      const int m = (int)(rem / chunks);
+      part[u] = (int)(rem - (int64_t)m * chunks);
+      e[u] = miss_pos[base_row + m];
+    }
+    int row[kUnroll], g[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int ec = min(max(e[u], 0), topk - 1);
+      row[u] = wave_rows[base_row + ec];
+      g[u] = hot_idx[base_row + ec];
+    }
     i32x4 v[kUnroll];
     int64_t dst[kUnroll];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-      const int64_t f = base + (int64_t)u * kThreads;
-      dst[u] = -1;
-      if (f < total) {
-        const int c = (int)(f / per_cache);
-        const int64_t rem = f - (int64_t)c * per_cache;
-        const int m = (int)(rem / chunks);
-        const int part = (int)(rem - (int64_t)m * chunks);
-        const int e = miss_pos[base_row + m];
-        if (e >= 0 && e < topk) {
-          const int row = wave_rows[base_row + e];
-          const int g = hot_idx[base_row + e];
-          if (row >= 0 && row < host_rows && g >= 0 && g < hot_rows) {
-            v[u] = *reinterpret_cast<const i32x4 *>(
-                host_pool + ((int64_t)c * host_rows + row) * row_bytes + part * 16);
-            dst[u] = ((int64_t)c * hot_rows + g) * row_bytes + part * 16;
-          }
-        }
-      }
+      const bool ok = base + (int64_t)u * kThreads < total && e[u] >= 0 && e[u] < topk &&
+                      row[u] >= 0 && row[u] < host_rows && g[u] >= 0 && g[u] < hot_rows;
+      v[u] = *reinterpret_cast<const i32x4 *>(
+          host_pool + ((int64_t)cache[u] * host_rows + (ok ? row[u] : 0)) * row_bytes + part[u] * 16);
+      dst[u] = ok ? ((int64_t)cache[u] * hot_rows + g[u]) * row_bytes + part[u] * 16 : -1;
     }
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u)
