@@ -83,11 +83,13 @@ def stored_traffic(workload):
         return None
 
 
-def cpu_baseline(w, s, budget_s=12.0):
-    """The oracle (numpy, float64) over the same rows, repeated for ~budget_s seconds."""
+def cpu_baseline(w, s, budget_s=12.0, one_thread_s=6.0):
+    """The oracle (numpy, float64) over the same rows, repeated for ~budget_s seconds with
+    numpy's own thread pool (all host cores), then for ~one_thread_s seconds limited to one
+    thread.  The resolve and attention stages are timed separately."""
     import numpy as np
     import oracle
-    from threadpoolctl import threadpool_info
+    from threadpoolctl import threadpool_info, threadpool_limits
 
     def raw(t):
         import torch
@@ -95,21 +97,36 @@ def cpu_baseline(w, s, budget_s=12.0):
         return t.view(torch.int16).numpy().view(np.uint16) if t.dtype == torch.bfloat16 else t.numpy()
 
     q, kv = raw(w.q), raw(w.kv_pool)
-    t0 = time.perf_counter()
-    reps = rows = 0
-    while True:
-        slots, _ = oracle.resolve_topk(w.topk_pos, w.req_id, w.causal_limit, w.block_table,
-                                       s.block_size, s.block_size, s.num_reqs)
-        oracle.sparse_decode_attn(q, kv, slots, s.scale, s.d_v)
-        reps += 1
-        rows += s.rows
-        if time.perf_counter() - t0 >= budget_s:
-            break
-    dt = time.perf_counter() - t0
+
+    def run(budget):
+        t_res = t_att = 0.0
+        reps = 0
+        t0 = time.perf_counter()
+        while True:
+            a = time.perf_counter()
+            slots, _ = oracle.resolve_topk(w.topk_pos, w.req_id, w.causal_limit, w.block_table,
+                                           s.block_size, s.block_size, s.num_reqs)
+            m = time.perf_counter()
+            oracle.sparse_decode_attn(q, kv, slots, s.scale, s.d_v)
+            z = time.perf_counter()
+            t_res += m - a
+            t_att += z - m
+            reps += 1
+            if z - t0 >= budget:
+                break
+        return reps, time.perf_counter() - t0, t_res / reps, t_att / reps
+
+    reps, dt, res_s, att_s = run(budget_s)
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-    return {"value": rows / dt, "unit": "rows/s", "cores": int(threads), "kind": "oracle",
+    with threadpool_limits(limits=1):
+        reps1, dt1, res1, att1 = run(one_thread_s)
+    return {"value": reps * s.rows / dt, "unit": "rows/s", "cores": int(threads), "kind": "oracle",
             "sample": f"full {s.name} step ({s.rows} rows: resolve_topk + float64 attention) "
-                      f"x {reps} repetitions, {dt:.1f} s on {os.cpu_count()} visible host CPUs"}
+                      f"x {reps} repetitions, {dt:.1f} s on {os.cpu_count()} visible host CPUs",
+            "stage_ms": {"resolve": res_s * 1e3, "attention": att_s * 1e3},
+            "one_thread": {"value": reps1 * s.rows / dt1, "unit": "rows/s",
+                           "stage_ms": {"resolve": res1 * 1e3, "attention": att1 * 1e3},
+                           "sample": f"{reps1} repetitions, {dt1:.1f} s"}}
 
 
 def measure_swap(dev, reps=5):
