@@ -456,6 +456,82 @@ def measure_finalize(dev, reps=10):
     }
 
 
+def measure_config_steps(dev, reps=3):
+    """Whole steps of the long-context workload (64 requests x 4 rows, seq_len 131072, reuse
+    0.5, 9.66 GB pinned host pool) and the mixed + finalize workload (128 requests x 3 rows,
+    seq_len log-uniform in [1024, 131072], reuse 0.6, logits [384, 129280]): resolve, then
+    per wave swap-in on the copy stream under attention on the main stream, and for the
+    mixed workload greedy accept + finalize.  Hot state restored before every repetition;
+    each timed region starts behind a spin kernel (device time)."""
+    import numpy as np
+    import torch
+
+    import sparse_attention_kv_amd as hs
+    from sparse_attention_kv_amd.pipeline import DecodeStep, build_hot_state
+    from workloads import generate, spec
+
+    main = torch.cuda.current_stream()
+    n = 256 << 20
+    src = torch.empty(n, dtype=torch.uint8, pin_memory=True)
+    dst = torch.empty(n, dtype=torch.uint8, device=dev)
+    dst.copy_(src, non_blocking=True)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(main)
+    for _ in range(4):
+        dst.copy_(src, non_blocking=True)
+    e1.record(main)
+    torch.cuda.synchronize()
+    b_host = 4 * n / (e0.elapsed_time(e1) / 1e3) / 1e9
+    del src, dst
+    out = {"B_host_GBps": b_host}
+    for name in ("long", "mixed_finalize"):
+        s = spec(name)
+        log(f"generate {s.name} (pinned host pool)")
+        w = generate(s, big_device="cuda", pin_host_pool=True)
+
+        def d(a):
+            return torch.as_tensor(np.ascontiguousarray(a)).to(device=dev, dtype=torch.int32)
+
+        topk_pos, req_id, lim, bt, seq = (d(w.topk_pos), d(w.req_id), d(w.causal_limit),
+                                          d(w.block_table), d(w.seq_len))
+        st = build_hot_state(torch.from_numpy(w.init_pos), torch.from_numpy(w.init_stamp), seq,
+                             bt, s.block_size, w.kv_pool, dev)
+        snap = [t.clone() for t in (st.slot_loc, st.slot_stamp, st.loc_to_hot)]
+        step = DecodeStep(num_reqs=s.num_reqs, rows_per_req=s.rows_per_req, topk=s.topk,
+                          num_heads=s.num_heads, d_qk=s.d_qk, d_v=s.d_v, dtype=torch.bfloat16,
+                          capacity=s.capacity, finalize=s.finalize, device=dev)
+        q = w.q.to(dev)
+        fin = None
+        if s.finalize:
+            fin = dict(logits=w.logits.to(dev), draft_ids=d(w.draft_ids), new_kv=w.new_kv.to(dev),
+                       seq_len=seq)
+        times = []
+        for rep in range(reps + 1):
+            for t, c in zip((st.slot_loc, st.slot_stamp, st.loc_to_hot), snap):
+                t.copy_(c)
+            torch.cuda.synchronize()
+            gpu_busy()
+            e0.record(main)
+            step.run_swap(st, topk_pos, req_id, lim, bt, s.block_size, q, s.scale, s.tick0,
+                          finalize=fin)
+            main.wait_stream(step.copy_stream)
+            e1.record(main)
+            torch.cuda.synchronize()
+            if rep >= 1:
+                times.append(e0.elapsed_time(e1))
+        ms = float(np.median(times))
+        miss_bytes = int(step.buf.miss_count.sum().item()) * s.d_qk * 2
+        out[name] = {"workload": s.name, "rows_per_step": s.rows, "waves": s.rows_per_req,
+                     "step_ms": ms, "rows_per_s": s.rows / (ms / 1e3), "miss_bytes": miss_bytes,
+                     "miss_GBps": miss_bytes / (ms / 1e3) / 1e9,
+                     "frac_of_B_host": miss_bytes / (ms / 1e3) / 1e9 / b_host,
+                     "finalize": bool(s.finalize)}
+        del w, st, step, q, fin, snap
+        torch.cuda.empty_cache()
+    return out
+
+
 def measure_backup(dev, reps=5):
     """Device -> host backup of prefill KV (staging): 8 requests x 4096 prompt tokens in
     pages of 64 rows, 4 layers of 576 bf16 latent rows -> 512 page transfers, 131072 rows,
@@ -525,6 +601,9 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--no-swap", action="store_true", help="skip the swap-path measurement")
+    ap.add_argument("--configs", action="store_true",
+                    help="also time whole steps of the long-context and mixed workloads "
+                         "(9.66 GB pinned host pool; not in the default run)")
     ap.add_argument("--no-sweep", action="store_true",
                     help="skip the attention sweep over larger batches")
     args = ap.parse_args()
@@ -669,6 +748,9 @@ def main():
         res["finalize"] = measure_finalize(dev)
         log("backup")
         res["backup"] = measure_backup(dev)
+    if args.configs:
+        log("whole steps of the long-context and mixed workloads")
+        res["config_steps"] = measure_config_steps(dev)
     if not args.no_cpu:
         log("cpu baseline (oracle)")
         res["cpu_baseline"] = cpu_baseline(w, s)
