@@ -456,6 +456,50 @@ def measure_finalize(dev, reps=10):
     }
 
 
+def measure_resolve(dev, reps=100):
+    """hs_resolve_topk alone, back-to-back calls, at the batch shapes of the resident (8
+    rows), MTP swap (128 rows) and long-context (256 rows, 2048-page tables) workloads;
+    a spin kernel ahead of the timed calls covers their host-side marshalling, so the time
+    is the device's.  Algorithmic bytes per call: the positions read and the rows written (4 B each per
+    entry), plus request id, causal limit and valid count per row; block-table lines are
+    not counted."""
+    import numpy as np
+    import torch
+
+    import sparse_attention_kv_amd as hs
+    from workloads import generate, spec
+
+    main = torch.cuda.current_stream()
+    out = []
+    for name in ("resident", "mtp_swap", "long"):
+        s = spec(name)
+        w = generate(s, tensors=False)
+
+        def d(a):
+            return torch.as_tensor(np.ascontiguousarray(a)).to(device=dev, dtype=torch.int32)
+
+        topk_pos, req_id, lim, bt = d(w.topk_pos), d(w.req_id), d(w.causal_limit), d(w.block_table)
+        rows = topk_pos.shape[0]
+        slots = torch.empty_like(topk_pos)
+        valid = torch.empty((rows,), dtype=torch.int32, device=dev)
+        for _ in range(5):
+            hs.hs_resolve_topk(topk_pos, req_id, lim, bt, s.block_size, s.block_size, slots, valid)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        gpu_busy(reps * 25.0)  # covers the marshalling of every call: device time only
+        e0.record(main)
+        for _ in range(reps):
+            hs.hs_resolve_topk(topk_pos, req_id, lim, bt, s.block_size, s.block_size, slots, valid)
+        e1.record(main)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / reps
+        alg = rows * s.topk * 8 + rows * 12
+        out.append({"workload": s.name, "rows": rows, "topk": s.topk, "us": us,
+                    "GBps": alg / (us / 1e6) / 1e9,
+                    "hbm_frac": alg / (us / 1e6) / 1e9 / HBM_PEAK_GBS})
+    return out
+
+
 def measure_config_steps(dev, reps=3):
     """Whole steps of the long-context workload (64 requests x 4 rows, seq_len 131072, reuse
     0.5, 9.66 GB pinned host pool) and the mixed + finalize workload (128 requests x 3 rows,
@@ -738,6 +782,8 @@ def main():
                      "alg_bytes_per_launch": alg,
                      "launch_us": attn_t * 1e3},
     }
+    log("resolve")
+    res["resolve"] = measure_resolve(dev)
     if not args.no_sweep:
         log("attention sweep")
         res["attn_sweep"] = measure_attn_sweep(dev)
