@@ -38,8 +38,24 @@ def _compare_state(ost, gst, what, with_kv=True):
 
 @pytest.mark.parametrize("name", ["tiny", "mtp_swap", "long", "mixed_finalize"])
 def test_swap_waves_bit_exact(name):
+    _swap_waves(name)
+
+
+@pytest.mark.parametrize("over", [
+    # the library's limits: 16384 slots (16 per thread), top-k 4096 (4 entries per thread)
+    dict(num_reqs=3, capacity=16384, topk=4096, seq_rule=("const", 30000)),
+    # sizes that are no multiple of the workgroup: 5 slots and 3 entries per thread, the
+    # last threads partly empty
+    dict(num_reqs=5, capacity=5000, topk=3000, seq_rule=("uniform", 6000, 9000)),
+], ids=["max_capacity_and_topk", "ragged_capacity_and_topk"])
+def test_swap_waves_bit_exact_at_size_limits(over):
+    """Full hot buffers, so every miss evicts an LRU victim."""
+    _swap_waves("mtp_swap", **over)
+
+
+def _swap_waves(name, **over):
     import sparse_attention_kv_amd as hs
-    s, w = make(name)
+    s, w = make(name, **over)
     g = gpu_inputs(s, w)
     ost, gst, pool = _both_states(s, w, g)
     _compare_state(ost, gst, f"{name} initial state")
