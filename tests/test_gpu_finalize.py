@@ -114,6 +114,39 @@ def test_finalize_random_requests(vocab):
 
 
 
+
+@pytest.mark.parametrize("accept", [63, 40, 0])
+def test_finalize_sixty_four_verify_rows(accept):
+    """The most verify rows a request may have (64): the acceptance ballot spans a whole
+    wave, and up to 64 kept rows miss and are installed with the LRU rule."""
+    rng = np.random.default_rng(6400 + accept)
+    B, R, cap, bs, width = 3, 64, 96, 16, 12
+    bt = rng.permutation(B * width).astype(np.int32).reshape(B, width)
+    seq = np.full(B, width * bs - 3, np.int32)
+    pool = rng.standard_normal((B * width * bs, 16)).astype(np.float32)
+    init_pos = np.full((B, cap), -1, np.int32)
+    init_stamp = np.full((B, cap), -1, np.int32)
+    for b in range(B):  # full buffers: committed positions plus a few verify positions
+        pos = rng.choice(int(seq[b]) - R, cap - 5, replace=False)
+        init_pos[b, :cap - 5] = pos
+        init_pos[b, cap - 5:] = seq[b] - R + np.array([0, 3, 17, 40, 63])
+        init_stamp[b] = rng.integers(0, 30, size=cap)
+    vocab = 300
+    gen = torch.Generator().manual_seed(accept)
+    logits = torch.randn(B * R, vocab, generator=gen).to(torch.bfloat16)
+    plant = rng.integers(0, vocab, size=B * R)
+    logits[torch.arange(B * R), torch.from_numpy(plant)] = 9.0
+    draft = rng.integers(0, vocab, size=B * R).astype(np.int32)
+    for b in range(B):
+        for r in range(1, accept + 1):
+            draft[r * B + b] = plant[(r - 1) * B + b]
+        if accept + 1 < R:  # the first rejected draft differs from the argmax
+            draft[(accept + 1) * B + b] = (plant[accept * B + b] + 1) % vocab
+    new_kv = rng.standard_normal((B * R, 16)).astype(np.float32)
+    acc, *_ = _run_finalize(B, R, cap, seq, bt, bs, pool, init_pos, init_stamp, logits, draft,
+                            new_kv, tick=40)
+    assert acc.tolist() == [accept] * B
+
 @pytest.mark.parametrize("vocab", [129280, 129281, 8, 9])
 def test_argmax_special_values(vocab):
     """Argmax rows with NaN, -inf, all-NaN and all -inf rows, the maximum in the first or
