@@ -132,7 +132,7 @@ def test_attn_many_splits_with_empty_leading_splits():
 # 32-head one.  These repeat the ragged / padded / empty cases on the 64-head path.
 @pytest.mark.parametrize("topk", [1, 65, 2047, 4500])
 def test_attn_bf16_64head_path_ragged_topk(topk):
-    rows, H, kv_rows = 16, 128, 6000
+    rows, H, kv_rows = 32, 128, 6000
     rng = np.random.default_rng(100 + topk)
     q = _rand_bf16((rows, H, 576), 200 + topk)
     kv = _rand_bf16((kv_rows, 576), 300 + topk)
@@ -146,7 +146,7 @@ def test_attn_bf16_64head_path_ragged_topk(topk):
 
 
 def test_attn_bf16_64head_path_zero_query_and_large_scores():
-    rows, H, kv_rows, topk = 32, 64, 3000, 300
+    rows, H, kv_rows, topk = 64, 64, 3000, 300
     rng = np.random.default_rng(77)
     q = _rand_bf16((rows, H, 576), 78)
     q[0] = 0  # uniform softmax
@@ -256,9 +256,9 @@ def test_attn_deterministic_and_index_order_invariant():
 
 
 # Head counts other than 128 reach the kernels through other planner choices: 32 and 96
-# heads only the 32-head kernel, 192 the 64-head one from 32 (row, 64-head) groups, 256
+# heads only the 32-head kernel, 192 the 64-head one from 64 (row, 64-head) groups, 256
 # the 128-head one from 256 (row, 128-head) groups.  The oracle checks sampled rows.
-@pytest.mark.parametrize("H,rows", [(32, 5), (96, 7), (96, 40), (192, 3), (192, 16), (256, 128)])
+@pytest.mark.parametrize("H,rows", [(32, 5), (96, 7), (96, 40), (192, 3), (192, 24), (256, 128)])
 def test_attn_head_counts(H, rows):
     rng = np.random.default_rng(H * 1000 + rows)
     kv_rows, topk = 5000, 900
