@@ -247,6 +247,18 @@ hs_status hs_sparse_decode_attn_paged(const void *q, const void *kv_pool, int64_
                                       void *out, float *lse, void *workspace,
                                       size_t workspace_bytes, void *stream);
 
+/*
+ * hs_attn_plan_info -- the launch hs_sparse_decode_attn(_paged, _mixed) makes for these
+ * sizes: *heads_per_wg = 32, 64 or 128 (the bf16 kernel the call runs), or 1 for the fp32
+ * path (one wave per (row, head)); *splits = key splits per row (1: no split, no
+ * workspace).  Either output may be NULL.  For tuning and tests; it launches nothing.
+ * Errors: HS_ERR_INVALID_ARG for non-positive sizes or an unknown dtype;
+ * HS_ERR_UNSUPPORTED for bf16 shapes the attention calls reject.
+ */
+hs_status hs_attn_plan_info(int32_t num_rows, int32_t num_heads, int32_t d_qk, int32_t d_v,
+                            int32_t topk, int32_t dtype, int32_t *heads_per_wg,
+                            int32_t *splits);
+
 /* Device workspace hs_sparse_decode_attn(_paged) needs for these sizes (0 when none). */
 size_t hs_attn_workspace_bytes(int32_t num_rows, int32_t num_heads, int32_t d_qk, int32_t d_v,
                                int32_t topk, int32_t dtype);

@@ -23,7 +23,7 @@ HS_BF16, HS_F32 = 0, 1
 
 EXPORTED = ("hs_resolve_topk", "hs_swap_in", "hs_sparse_decode_attn", "hs_sparse_decode_attn_paged",
             "hs_sparse_decode_attn_mixed",
-            "hs_attn_workspace_bytes", "hs_finalize_accepted", "hs_backup_rows", "hs_apply_plan",
+            "hs_attn_workspace_bytes", "hs_attn_plan_info", "hs_finalize_accepted", "hs_backup_rows", "hs_apply_plan",
             "hs_append_accepted",
             "hs_status_string", "hs_version")
 
@@ -63,6 +63,8 @@ def _load() -> ctypes.CDLL:
                                                 i32, i32, f32, i32, vp, vp, vp, sz, vp]
     lib.hs_sparse_decode_attn_mixed.restype = i32
     lib.hs_attn_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32]
+    lib.hs_attn_plan_info.argtypes = [i32, i32, i32, i32, i32, i32, vp, vp]
+    lib.hs_attn_plan_info.restype = i32
     lib.hs_attn_workspace_bytes.restype = sz
     lib.hs_finalize_accepted.argtypes = [ctypes.POINTER(HsHotState), vp, i32, vp, vp, i32, vp, vp,
                                          i32, i32, i32, vp, vp, vp, vp]
@@ -184,6 +186,17 @@ def hs_swap_in(state: HotState, wave_rows: torch.Tensor, tick: int, out_hot_idx:
 def hs_attn_workspace_bytes(num_rows: int, num_heads: int, d_qk: int, d_v: int, topk: int,
                             dtype: torch.dtype) -> int:
     return int(_lib.hs_attn_workspace_bytes(num_rows, num_heads, d_qk, d_v, topk, _dtype_code(dtype)))
+
+
+def hs_attn_plan_info(num_rows: int, num_heads: int, d_qk: int, d_v: int, topk: int,
+                      dtype: torch.dtype):
+    """(heads per workgroup, key splits) of the attention launch for these sizes: 32, 64 or
+    128 for the bf16 kernels, 1 for the fp32 path (see include/hisparse.h)."""
+    hpw, spl = ctypes.c_int32(0), ctypes.c_int32(0)
+    _check("hs_attn_plan_info", _lib.hs_attn_plan_info(num_rows, num_heads, d_qk, d_v, topk,
+                                                       _dtype_code(dtype), ctypes.byref(hpw),
+                                                       ctypes.byref(spl)))
+    return hpw.value, spl.value
 
 
 def hs_sparse_decode_attn(q: torch.Tensor, kv: torch.Tensor, indices: torch.Tensor, scale: float,

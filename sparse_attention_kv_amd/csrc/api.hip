@@ -154,6 +154,24 @@ hs_status hs_append_accepted(void *ctx_cache, int64_t ctx_rows, int32_t row_byte
                                              static_cast<hipStream_t>(stream)));
 }
 
+hs_status hs_attn_plan_info(int32_t num_rows, int32_t num_heads, int32_t d_qk, int32_t d_v,
+                            int32_t topk, int32_t dtype, int32_t *heads_per_wg,
+                            int32_t *splits) {
+  if (num_rows <= 0 || num_heads <= 0 || d_qk <= 0 || d_v <= 0 || topk <= 0)
+    return HS_ERR_INVALID_ARG;
+  if (dtype == HS_F32) {
+    if (heads_per_wg) *heads_per_wg = 1;
+    if (splits) *splits = 1;
+    return HS_OK;
+  }
+  if (dtype != HS_BF16) return HS_ERR_INVALID_ARG;
+  if (d_qk != 576 || d_v != 512 || num_heads % 32 != 0) return HS_ERR_UNSUPPORTED;
+  const hs::AttnPlan p = hs::plan_attn_bf16(num_rows, num_heads, topk);
+  if (heads_per_wg) *heads_per_wg = p.heads_per_wg;
+  if (splits) *splits = p.splits;
+  return HS_OK;
+}
+
 size_t hs_attn_workspace_bytes(int32_t num_rows, int32_t num_heads, int32_t d_qk, int32_t d_v,
                                int32_t topk, int32_t dtype) {
   if (dtype != HS_BF16 || num_rows <= 0 || topk <= 0 || num_heads <= 0 || num_heads % 32 != 0 ||

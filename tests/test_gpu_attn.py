@@ -57,6 +57,12 @@ def test_attn_resident_full_bf16():
     _check(g["q"], w.kv_pool, to_dev(ref_slots), s.scale, s.d_v, BF16_TOL, "resident full")
 
 
+def _kernel(rows, H, topk):
+    """Heads per workgroup of the bf16 kernel the planner picks for these sizes."""
+    import sparse_attention_kv_amd as hs
+    return hs.hs_attn_plan_info(rows, H, 576, 512, topk, torch.bfloat16)[0]
+
+
 def _rand_bf16(shape, seed):
     gen = torch.Generator(device="cpu").manual_seed(seed)
     return torch.randn(shape, generator=gen).to(torch.bfloat16).to(dev())
@@ -128,11 +134,12 @@ def test_attn_many_splits_with_empty_leading_splits():
     _check(q, kv, to_dev(idx), 1 / 24, 512, BF16_TOL, "many splits")
 
 
-# Shapes with >= 32 (row, 64-head) groups take the 64-head kernel; the cases above take the
+# Shapes with >= 64 (row, 64-head) groups take the 64-head kernel; the cases above take the
 # 32-head one.  These repeat the ragged / padded / empty cases on the 64-head path.
 @pytest.mark.parametrize("topk", [1, 65, 2047, 4500])
 def test_attn_bf16_64head_path_ragged_topk(topk):
     rows, H, kv_rows = 32, 128, 6000
+    assert _kernel(rows, H, topk) == 64
     rng = np.random.default_rng(100 + topk)
     q = _rand_bf16((rows, H, 576), 200 + topk)
     kv = _rand_bf16((kv_rows, 576), 300 + topk)
@@ -147,6 +154,7 @@ def test_attn_bf16_64head_path_ragged_topk(topk):
 
 def test_attn_bf16_64head_path_zero_query_and_large_scores():
     rows, H, kv_rows, topk = 64, 64, 3000, 300
+    assert _kernel(rows, H, topk) == 64
     rng = np.random.default_rng(77)
     q = _rand_bf16((rows, H, 576), 78)
     q[0] = 0  # uniform softmax
@@ -178,6 +186,7 @@ def _check_sampled(q, kv, idx, scale, d_v, what, sample):
 def test_attn_bf16_128head_path_ragged_topk(topk):
     import sparse_attention_kv_amd as hs
     rows, H, kv_rows = 256, 128, 6000
+    assert _kernel(rows, H, topk) == 128
     if topk <= 2048:  # one split holds at most 2048 keys; longer lists always split
         assert hs.hs_attn_workspace_bytes(rows, H, 576, 512, topk, torch.bfloat16) == 0
     rng = np.random.default_rng(500 + topk)
@@ -195,6 +204,7 @@ def test_attn_bf16_128head_path_ragged_topk(topk):
 
 def test_attn_bf16_128head_path_zero_query_and_large_scores():
     rows, H, kv_rows, topk = 256, 128, 3000, 700
+    assert _kernel(rows, H, topk) == 128
     rng = np.random.default_rng(88)
     q = _rand_bf16((rows, H, 576), 89)
     q[0] = 0   # uniform softmax
@@ -215,6 +225,7 @@ def test_attn_reference_moves_at_later_keys(rows):
     reference slack, so the reference moves and O is rescaled after the first block, more
     than once, and last at the final block."""
     H, kv_rows, topk = 128, 9000, 2048
+    assert _kernel(rows, H, topk) == {8: 32, 128: 64, 256: 128}[rows]
     rng = np.random.default_rng(4400 + rows)
     q = _rand_bf16((rows, H, 576), 4500 + rows).cpu()
     kv = _rand_bf16((kv_rows, 576), 4600 + rows).cpu()
@@ -262,6 +273,7 @@ def test_attn_deterministic_and_index_order_invariant():
 def test_attn_head_counts(H, rows):
     rng = np.random.default_rng(H * 1000 + rows)
     kv_rows, topk = 5000, 900
+    assert _kernel(rows, H, topk) == {32: 32, 96: 32, 192: 32 if rows < 16 else 64, 256: 128}[H]
     q = _rand_bf16((rows, H, 576), H + rows)
     kv = _rand_bf16((kv_rows, 576), H + rows + 1)
     idx = np.stack([rng.choice(kv_rows, topk, replace=False) for _ in range(rows)]).astype(np.int32)

@@ -33,11 +33,13 @@ def _mixed(q, kv_a, ia, kv_b, ib, sel, scale=1 / 24):
     return out, lse
 
 
-@pytest.mark.parametrize("rows,topk,sample", [(8, 2048, None), (16, 700, None),
+@pytest.mark.parametrize("rows,topk,sample", [(8, 2048, None), (40, 700, None),
                                               (256, 600, [0, 1, 2, 3, 100, 255])])
 def test_mixed_attention_matches_oracle(rows, topk, sample):
-    """8 rows take the 32-head kernel, 16 the 64-head one, 256 the 128-head one."""
+    """8 rows take the 32-head kernel, 40 the 64-head one, 256 the 128-head one."""
+    import sparse_attention_kv_amd as hs
     H = 128
+    assert hs.hs_attn_plan_info(rows, H, 576, 512, topk, torch.bfloat16)[0] == {8: 32, 40: 64, 256: 128}[rows]
     rng = np.random.default_rng(rows)
     q = _rand_bf16((rows, H, 576), rows)
     kv_a = _rand_bf16((3000, 576), rows + 1)

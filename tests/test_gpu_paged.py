@@ -71,7 +71,10 @@ def test_paged_resident_full_matches_oracle_and_two_calls():
 def test_paged_fail_closed_cases(num_reqs, topk):
     """Positions past the causal limit or negative, an out-of-range request id, unmapped
     pages and a short block-table row select nothing; 40 requests take the 64-head kernel."""
+    import sparse_attention_kv_amd as hs
     s, w = make("resident", num_reqs=num_reqs, topk=topk, seq_rule=("uniform", 900, 1500))
+    assert hs.hs_attn_plan_info(s.rows, s.num_heads, 576, 512, topk, torch.bfloat16)[0] == \
+        (64 if num_reqs == 40 else 32)
     rng = np.random.default_rng(num_reqs * 1000 + topk)
     pos = w.topk_pos.copy()
     lim = w.causal_limit.copy()

@@ -187,3 +187,21 @@ def test_append_validation():
                dict(cache=None), dict(bt=None), dict(ln=None), dict(new=None), dict(acc=None),
                dict(rows=1 << 31), dict(new=P + 8)):
         assert call(**kw) == hs.HS_ERR_INVALID_ARG, kw
+
+
+def test_attn_plan_info():
+    """The launch the attention calls make, without a GPU: kernel by batch, and key splits."""
+    import torch
+    hs, lib = _lib()
+    plan = lambda rows, heads=128, topk=2048: hs.hs_attn_plan_info(rows, heads, 576, 512, topk,
+                                                                   torch.bfloat16)
+    assert plan(8) == (32, 8)        # 32 workgroups of (row, 32 heads) -> 8 key splits
+    assert plan(24)[0] == 32 and plan(32)[0] == 64 and plan(255)[0] == 64 and plan(256)[0] == 128
+    assert plan(128) == (64, 1) and plan(256) == (128, 1)
+    assert plan(8, topk=4500)[1] >= 3  # one split holds at most 2048 keys
+    assert plan(40, heads=96)[0] == 32  # 96 heads: only the 32-head kernel
+    assert hs.hs_attn_plan_info(4, 4, 64, 48, 16, torch.float32) == (1, 1)
+    h, s = ctypes.c_int32(0), ctypes.c_int32(0)
+    assert lib.hs_attn_plan_info(0, 128, 576, 512, 2048, hs.HS_BF16, ctypes.byref(h), ctypes.byref(s)) == hs.HS_ERR_INVALID_ARG
+    assert lib.hs_attn_plan_info(8, 100, 576, 512, 2048, hs.HS_BF16, None, None) == hs.HS_ERR_UNSUPPORTED
+    assert lib.hs_attn_plan_info(8, 128, 576, 512, 2048, 9, None, None) == hs.HS_ERR_INVALID_ARG
