@@ -142,8 +142,13 @@ hs_status hs_resolve_topk(const int32_t *topk_pos, int32_t num_rows, int32_t top
  * with the smallest (stamp, slot); miss m (ascending entry index) takes the m-th victim
  * in ascending slot order, the evicted row's loc_to_hot entry is cleared and the host
  * row is copied bit for bit into hot_kv; every used slot gets stamp `tick`.
- * Entries of one row must be distinct host rows (top-k sets are); with duplicates the
- * resulting state is unspecified but every access stays in bounds.
+ * Repeated host rows within one request (top-k sets have none): each copy of a hit uses
+ * that hit's slot; each copy of a miss is a miss of its own (counted and listed) and takes
+ * its own victim, so every hot index still names a slot that holds its row.  When two
+ * writes to one row's loc_to_hot entry fall in one call (two copies of a miss, or an
+ * install and the eviction of a slot still holding that row), which write lands last is
+ * not defined.  A row's entry, when set, always names a slot holding that row; a copy the
+ * map does not name stays resident until it is evicted.
  * hot_kv is written only by work queued on `stream`; it may run concurrently with
  * attention over an earlier wave when capacity >= 2*topk (victims are then never slots
  * the previous wave used).

@@ -215,6 +215,9 @@ __global__ __launch_bounds__(kThreads) void swap_in_kernel(
     __syncthreads();
 
     // ---- D: install misses into victims ----
+    // A row repeated within the request installs once per copy.  Two writes to one
+    // loc_to_hot entry (two copies, or an install and an eviction of a slot still holding
+    // the row) land in no set order; either way the entry names -1 or a slot with the row.
     for (int i = tid; i < need; i += kThreads) {
       const int v = sm.victim[i];
       const int row = sm.miss_row[i];

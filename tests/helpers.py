@@ -36,3 +36,31 @@ def check_state_invariants(st, host_pool_raw: np.ndarray):
     flat = st.slot_loc.reshape(-1)
     o = np.nonzero(flat >= 0)[0]
     assert np.array_equal(st.hot_kv[o], host_pool_raw[flat[o]])
+
+
+def with_duplicates(wave: np.ndarray) -> np.ndarray:
+    """A copy of a swap wave in which rows repeat within each request: entry 4i+1 repeats entry
+    4i and entry 4i+3 repeats entry 4i (three copies)."""
+    out = wave.copy()
+    n1 = len(out[:, 1::4][0])
+    out[:, 1::4] = wave[:, 0::4][:, :n1]
+    n3 = len(out[:, 3::4][0])
+    out[:, 3::4] = wave[:, 0::4][:, :n3]
+    return out
+
+
+def check_state_weak(st, host_pool_raw: np.ndarray):
+    """What holds after waves that repeat a row within a request: a row may sit in several
+    slots of its request and the map names at most one of them, but a mapped row's slot holds
+    that row, and every occupied slot holds the bytes of the row it names."""
+    B, cap = st.slot_loc.shape
+    flat = st.slot_loc.reshape(-1)
+    mapped = np.nonzero(st.loc_to_hot >= 0)[0]
+    g = st.loc_to_hot[mapped]
+    assert (g < B * cap).all()
+    assert (flat[g] == mapped).all(), "a mapped row's slot holds another row"
+    occ = st.slot_loc >= 0
+    assert (st.slot_stamp[~occ] == -1).all()
+    assert (st.slot_stamp[occ] >= 0).all()
+    o = np.nonzero(flat >= 0)[0]
+    assert np.array_equal(st.hot_kv[o], host_pool_raw[flat[o]])

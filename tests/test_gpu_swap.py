@@ -202,3 +202,73 @@ def test_pipeline_step(name):
 
 def test_pipeline_step_with_finalize_full():
     _pipeline_case("mixed_finalize", sample_rows_per_wave=4)
+
+
+def _racy_rows(before, wave, hot_idx, mc, mp):
+    """Map entries that two writers set in one wave, with the values they write: every miss
+    installs its row (the slot it took), every eviction clears the row its victim held (-1)."""
+    held = before.slot_loc.reshape(-1)
+    writes = {}
+    for b in range(wave.shape[0]):
+        for m in range(mc[b]):
+            j = mp[b, m]
+            g = int(hot_idx[b, j])
+            writes.setdefault(int(wave[b, j]), []).append(g)
+            if held[g] >= 0:
+                writes.setdefault(int(held[g]), []).append(-1)
+    return {r: set(v) for r, v in writes.items() if len(v) >= 2}
+
+
+@pytest.mark.parametrize("name,over", [
+    ("tiny", {}),
+    ("mtp_swap", {"num_reqs": 3, "seq_rule": ("const", 6000), "capacity": 1024, "topk": 256}),
+], ids=["tiny", "mtp_small"])
+def test_swap_duplicate_rows_in_a_request(name, over):
+    """Rows repeated within a request (top-k sets never do this; the call still defines it).
+    Hot indices, miss lists, slot_loc, stamps and the hot rows match the oracle bit for bit.
+    A map entry that two writers set in the same wave (two copies of a miss, or a miss and the
+    eviction of a slot that held the same row) has no defined order: the device must hold one
+    of the written values, and the oracle then takes the device's map so that the next wave
+    starts from the same state."""
+    import sparse_attention_kv_amd as hs
+    from tests.helpers import check_state_weak, with_duplicates
+    s, w = make(name, **over)
+    g = gpu_inputs(s, w)
+    ost, gst, pool = _both_states(s, w, g)
+    slots, _ = oracle_resolve(s, w)
+    B, K = s.num_reqs, s.topk
+    racy_total = install_vs_evict = 0
+    # wave 0 comes back after every other wave: rows then sit in slots the map no longer
+    # names, and evicting such a slot can race with installing its row again
+    sched = [r for k in range(s.rows_per_req) for r in (k, 0)]
+    for t, r in enumerate(sched):
+        wave = with_duplicates(slots[r * B:(r + 1) * B])
+        before = ost.copy()
+        hot = torch.full((B, K), 7, dtype=torch.int32, device=dev())
+        mc = torch.full((B,), 7, dtype=torch.int32, device=dev())
+        mp = torch.full((B, K), 7, dtype=torch.int32, device=dev())
+        log(f"swap duplicates {name} call {t} (wave {r})")
+        hs.hs_swap_in(gst, to_dev(wave), s.tick0 + t, hot, mc, mp)
+        torch.cuda.synchronize()
+        oh, omc, omp = oracle.swap_in(ost, wave, s.tick0 + t, pool)
+        assert np.array_equal(hot.cpu().numpy(), oh), f"{name} call {t} hot_idx"
+        assert np.array_equal(mc.cpu().numpy(), omc), f"{name} call {t} miss_count"
+        assert np.array_equal(mp.cpu().numpy(), omp), f"{name} call {t} miss_pos"
+        assert np.array_equal(gst.slot_loc.cpu().numpy(), ost.slot_loc), f"{name} call {t} slot_loc"
+        assert np.array_equal(gst.slot_stamp.cpu().numpy(), ost.slot_stamp), f"{name} call {t} stamps"
+        racy = _racy_rows(before, wave, oh, omc, omp)
+        racy_total += len(racy)
+        install_vs_evict += sum(1 for v in racy.values() if -1 in v and len(v) > 1)
+        gl = gst.loc_to_hot.cpu().numpy()
+        for row in np.nonzero(gl != ost.loc_to_hot)[0]:
+            assert int(row) in racy, f"{name} call {t} loc_to_hot[{row}] differs outside a race"
+            assert int(gl[row]) in racy[int(row)], f"{name} call {t} loc_to_hot[{row}] = {gl[row]}"
+        ost.loc_to_hot[:] = gl
+        occ = np.nonzero(ost.slot_loc.reshape(-1) >= 0)[0]
+        assert np.array_equal(raw(gst.hot_kv.cpu())[occ], ost.hot_kv[occ]), f"{name} call {t} hot_kv"
+        check_state_weak(ost, pool)
+    log(f"swap duplicates {name}: {racy_total} map entries with two writers, "
+        f"{install_vs_evict} of them an install against an eviction")
+    assert racy_total > 0
+    if name == "tiny":
+        assert install_vs_evict > 0

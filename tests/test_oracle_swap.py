@@ -6,7 +6,7 @@ import numpy as np
 import pytest
 
 from oracle import HotState, build_hot_state, resolve_topk, swap_in
-from tests.helpers import check_state_invariants, raw
+from tests.helpers import check_state_invariants, check_state_weak, raw, with_duplicates
 from workloads import generate, spec
 
 
@@ -145,3 +145,56 @@ def test_swap_pairs_misses_with_victims_in_slot_order():
     assert st.slot_loc[0].tolist() == [10, 60, 70, 13]
     assert st.slot_stamp[0].tolist() == [5, 20, 20, 20]
     assert st.loc_to_hot[11] == -1 and st.loc_to_hot[12] == -1
+
+
+DUP_CASE = ("mtp_swap", {"num_reqs": 3, "seq_rule": ("const", 6000), "capacity": 1024, "topk": 256})
+
+
+def test_swap_duplicate_rows_in_a_request():
+    """Top-k sets never repeat a row, but the call defines what a repeat does: copies of a hit
+    share its slot; every copy of a miss is a miss of its own and takes its own victim under
+    the pairing rule, so each entry's hot index names a slot holding its row.  From a state
+    without repeats the map names the slot of the last copy; later waves keep the weaker
+    invariants (a row may sit in several slots, the map names one of them or none)."""
+    _duplicate_waves(*DUP_CASE)
+
+
+def test_swap_duplicate_rows_evicting_stale_copies():
+    """A small buffer: copies the map no longer names get evicted while their row is installed
+    again in the same wave."""
+    _duplicate_waves("tiny", {})
+
+
+def _duplicate_waves(name, over):
+    s, w, pool, st, slots = _setup(name, **over)
+    B = s.num_reqs
+    seen_hit_dup = seen_miss_dup = 0
+    # wave 0 comes back after every other wave, so rows return while stale copies remain
+    sched = [r for k in range(s.rows_per_req) for r in (k, 0)]
+    for t, r in enumerate(sched):
+        wave = with_duplicates(slots[r * B:(r + 1) * B])
+        before = st.copy()
+        hot_idx, mc, mp = swap_in(st, wave, s.tick0 + t, pool)
+        check_state_weak(st, pool)
+        valid = wave >= 0
+        assert (st.slot_loc.reshape(-1)[hot_idx[valid]] == wave[valid]).all()
+        assert np.array_equal(st.hot_kv[hot_idx[valid]], pool[wave[valid]])
+        was_hit = valid & (before.loc_to_hot[np.where(valid, wave, 0)] >= 0)
+        assert np.array_equal(mc, (valid & ~was_hit).sum(1))
+        for b in range(B):
+            miss_slots = hot_idx[b, valid[b] & ~was_hit[b]]
+            assert len(np.unique(miss_slots)) == len(miss_slots), "two misses share a victim"
+            assert not np.isin(miss_slots, hot_idx[b, was_hit[b]]).any()
+            for row in np.unique(wave[b, valid[b]]):
+                js = np.nonzero(wave[b] == row)[0]
+                if len(js) < 2:
+                    continue
+                if was_hit[b, js[0]]:
+                    seen_hit_dup += 1
+                    assert (hot_idx[b, js] == before.loc_to_hot[row]).all()
+                else:
+                    seen_miss_dup += 1
+                    assert len(np.unique(hot_idx[b, js])) == len(js)
+                    if t == 0:
+                        assert st.loc_to_hot[row] == hot_idx[b, js[-1]]
+    assert seen_hit_dup > 0 and seen_miss_dup > 0
