@@ -222,10 +222,16 @@ __global__ __launch_bounds__(kThreads, 1) void attn128_kernel(
   // The inner loop touches O only through MFMA.  The first block sets the reference (O is
   // still zero); a later block that needs a new one jumps out of the loop, O is rescaled
   // outside, and the loop resumes.  That rare path re-reads Q afterwards, so Q's registers
-  // are free while it runs.  It is entered by a jump of its own, not through the loop's
-  // normal exit: the compiler puts the rare path's register spills on the edge into it, and
-  // on a shared exit block they ran once per launch (≈764 B per lane, 50 MB at 256 rows).
+  // are free while it runs.  No load may still be in flight where control enters the loop
+  // head (prologue, rare path): the compiler would then wait for it inside the loop, and
+  // that wait also counts the tile DMAs it cannot see, stalling each block on the gather
+  // it has just issued.  Hence the explicit waits before the loop and at the rare path's
+  // end, and the rescale one block of 16 at a time (all 256 at once spills, and the reloads
+  // would be such loads).
   const int nblocks = 2 * ntiles;
+  // Q and tile 0 have landed before the loop (its first block would wait here anyway), so
+  // no load of the prologue is still counted at the loop head.
+  wait_vmem();
   int b = 0;
   float s[16];
   float alpha = 1.f;
@@ -314,10 +320,13 @@ __global__ __launch_bounds__(kThreads, 1) void attn128_kernel(
 #pragma unroll
     for (int nb = 0; nb < kNB; ++nb) {
       f32x16 tmp = oacc[nb];
+      asm volatile("" : "+v"(tmp));
 #pragma unroll
       for (int i = 0; i < 16; ++i) tmp[i] *= alpha;
+      asm volatile("" : "+v"(tmp));
       oacc[nb] = tmp;
       asm volatile("" : "+a"(oacc[nb]));
+      __builtin_amdgcn_sched_barrier(0);
     }
     {
       float p[16];
@@ -329,6 +338,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn128_kernel(
       pv_block(s_kv + ((b >> 1) & 1) * kTileBytes, b & 1, p);
     }
     load_q();
+    wait_vmem();
     ++b;
   }
 
