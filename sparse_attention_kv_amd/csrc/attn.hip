@@ -308,8 +308,7 @@ __global__ __launch_bounds__(kThreads8, 1) void attn_bf16_kernel(
         *reinterpret_cast<bf16x4 *>(s_p + h * kPStride + (16 * kq + 4 * (l >> 4)) * 2) = pk;
       }
       // publish this wave's per-head maxima and whether it needs a new reference
-      mw = vmax(mw, __shfl_xor(mw, 16, 64));
-      mw = vmax(mw, __shfl_xor(mw, 32, 64));
+      mw = xor32_max(xor16_max(mw));
       if (l < 16) s_red[kq][h] = mw;
       if (l == 0) s_flag[w] = any_over;
       lds_barrier();
@@ -357,8 +356,7 @@ __global__ __launch_bounds__(kThreads8, 1) void attn_bf16_kernel(
   // ---- epilogue: total softmax sums, normalise, write ----
   {
     float lr = l_run;
-    lr += __shfl_xor(lr, 16, 64);
-    lr += __shfl_xor(lr, 32, 64);
+    lr = xor32_sum(xor16_sum(lr));
     const int h = 16 * hh + (l & 15);
     if (l < 16) s_red[kq][h] = lr;
     if (kq == 0 && l < 16) s_fm[h] = m_ref;

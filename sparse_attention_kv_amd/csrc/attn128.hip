@@ -298,7 +298,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn128_kernel(
         s[i] = v;
         mx = vmax(mx, v);
       }
-      mx = vmax(mx, __shfl_xor(mx, 32, 64));
+      mx = xor32_max(mx);
       const bool over = mx > m_ref + kRescaleSlack;
       if (__builtin_amdgcn_ballot_w64(over) != 0) {
         alpha = over ? __builtin_amdgcn_exp2f(m_ref - mx) : 1.f;
@@ -343,7 +343,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn128_kernel(
   }
 
   // ---- epilogue: head sums, normalise, stage O^T -> LDS rows, whole-row stores ----
-  const float lt = l_run + __shfl_xor(l_run, 32, 64);
+  const float lt = xor32_sum(l_run);
   const float inv = lt > 0.f ? __builtin_amdgcn_rcpf(lt) : 0.f;
   lds_barrier();  // every wave is done with the tile buffers
   uint8_t *stg = s_kv + w * kHW * kOStride;

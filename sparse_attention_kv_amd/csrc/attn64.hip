@@ -265,8 +265,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn64_kernel(
           s[4 * kb + r] = v;
           mx = vmax(mx, v);
         }
-      mx = vmax(mx, __shfl_xor(mx, 16, 64));
-      mx = vmax(mx, __shfl_xor(mx, 32, 64));
+      mx = xor32_max(xor16_max(mx));
       const bool over = mx > m_ref + kRescaleSlack;
       if (__builtin_amdgcn_ballot_w64(over) != 0) {
         // new reference for the heads whose maximum moved up (rare after the first tile)
@@ -300,8 +299,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn64_kernel(
 
   // ---- epilogue: head sums, normalise, stage O^T -> LDS rows, whole-row stores ----
   float lt = l_run;
-  lt += __shfl_xor(lt, 16, 64);
-  lt += __shfl_xor(lt, 32, 64);
+  lt = xor32_sum(xor16_sum(lt));
   const float inv = lt > 0.f ? __builtin_amdgcn_rcpf(lt) : 0.f;
   lds_barrier();  // every wave is done with the tile buffers
   uint8_t *stg = s_kv0 + w * kHW * kOStride;

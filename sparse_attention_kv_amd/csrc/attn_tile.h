@@ -57,6 +57,28 @@ constexpr int vmcnt_imm(int n) { return ((n >> 4) & 3) << 14 | 0x3f70 | (n & 15)
 // v_max_f32 (inputs here are finite or -inf)
 __device__ __forceinline__ float vmax(float a, float b) { return __builtin_fmaxf(a, b); }
 
+// Maximum and sum of a lane's value and that of lane l ^ 32 (l ^ 16), in every lane, with
+// one VALU lane swap instead of an LDS permute: the gfx950 permlane swaps return the lane's
+// own value in one result and its partner's in the other (which one depends on the half),
+// so combining the two results is the same for every lane.  a + b = b + a exactly, so the
+// sums equal those of a shuffle.
+__device__ __forceinline__ float xor32_max(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return vmax(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor32_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float xor16_max(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return vmax(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor16_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Load this thread's share of a split's indices: entry j = tid * per + k (k < per) of
 // `irow`.  With kPaged the entries are request-local token positions, resolved here exactly
 // as hs_resolve_topk does (P3 "vllm 分析（十二）——Hisparse下篇", resolve_topk listing:
