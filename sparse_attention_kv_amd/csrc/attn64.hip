@@ -125,7 +125,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn64_kernel(
       cnt += ok;
     }
     int wave_total;
-    const int ex = wave_exclusive_scan(cnt, wave_total);
+    static_assert(kMaxKeysPerSplit / kThreads <= kSmallScanMax, "per-lane key count fits the scan");
+    const int ex = wave_exclusive_scan_small(cnt, wave_total);
     if (l == 0) s_scan[w] = wave_total;
     lds_barrier();
     int base = 0, total = 0;

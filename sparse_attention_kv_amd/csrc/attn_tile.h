@@ -54,6 +54,24 @@ __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x3f70)
 // vmcnt bits [3:0] and [15:14]).
 constexpr int vmcnt_imm(int n) { return ((n >> 4) & 3) << 14 | 0x3f70 | (n & 15); }
 
+// Exclusive prefix sum across the wave of v in [0, 15] (a lane's count of valid keys), and
+// the wave total: one ballot per bit of v and a count of the set bits below the lane, in
+// place of a six-round shuffle scan on the path to the first gather.
+constexpr int kSmallScanMax = 15;
+__device__ __forceinline__ int wave_exclusive_scan_small(int v, int &total) {
+  int ex = 0, tot = 0;
+#pragma unroll
+  for (int bit = 0; bit < 4; ++bit) {
+    const uint64_t m = __builtin_amdgcn_ballot_w64(((v >> bit) & 1) != 0);
+    const int below = __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(m >> 32),
+                                                __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0u));
+    ex += below << bit;
+    tot += __builtin_popcountll(m) << bit;
+  }
+  total = tot;
+  return ex;
+}
+
 // v_max_f32 (inputs here are finite or -inf)
 __device__ __forceinline__ float vmax(float a, float b) { return __builtin_fmaxf(a, b); }
 
