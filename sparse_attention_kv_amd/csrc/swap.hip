@@ -12,10 +12,13 @@
 //      hit slots are marked pinned in LDS; misses are compacted in entry order with a
 //      wave-ballot/prefix-sum scan.
 //   B  LRU threshold: the need-th smallest (stamp, slot) key among unpinned slots via a
-//      4-pass, 8-bit radix select over LDS histograms.
+//      4-pass, 8-bit radix select over LDS histograms.  Each thread owns a run of slots
+//      whose stamps and held rows it loaded into registers before the first copy round's
+//      host reads went out, so B-E wait on no memory load while those reads are in flight.
 //   C  victims in ascending slot order: a second ordered scan over slot runs picks every
 //      unpinned slot below the threshold stamp plus the lowest-numbered ones at it.
-//   D  install: miss m takes victim m; the evicted row's map entry is cleared.
+//   D  install: miss m takes victim m (done by the victim slot's owner); the evicted row's
+//      map entry is cleared.
 //   E  stamp every used slot with `tick`, emit hot indices.
 //   F  copy the miss rows from the pinned host pool into the hot buffer with 16-byte
 //      loads (the host link is the bound; many independent loads per thread are kept
@@ -28,6 +31,7 @@ namespace {
 
 constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / 64;
+static_assert(kMaxCapacity <= 16 * kThreads, "a thread holds at most 16 slots in registers");
 
 struct SwapLds {
   int *hist;           // [256]
@@ -83,6 +87,7 @@ __device__ __forceinline__ uint32_t order_key(int32_t stamp) {
   return static_cast<uint32_t>(stamp) ^ 0x80000000u;  // signed order as unsigned order
 }
 
+template <int kSper>
 __global__ __launch_bounds__(kThreads) void swap_in_kernel(
     int32_t capacity, int32_t *__restrict__ slot_loc, int32_t *__restrict__ slot_stamp,
     int32_t *__restrict__ loc_to_hot, int64_t host_rows, int32_t row_bytes,
@@ -138,7 +143,41 @@ __global__ __launch_bounds__(kThreads) void swap_in_kernel(
   if (tid == 0) out_miss_count[b] = need;
   __syncthreads();
 
-  const int32_t *stamps = slot_stamp + slot_base;
+  // ---- this thread's slots [s0, s0 + sper): stamps and held rows into registers, so that
+  // victim choice loads nothing from memory once the copy's first host reads are out (the
+  // wait for such a load would also wait for every host read issued before it) ----
+  const int sper = (capacity + kThreads - 1) / kThreads;  // <= kSper
+  const int s0 = tid * sper;
+  const int s_last = max(0, min(s0 + sper, capacity) - 1);
+  int32_t st_own[kSper], held[kSper];
+  if (need > 0) {
+#pragma unroll
+    for (int k = 0; k < kSper; ++k) {
+      const int s = min(s0 + k, s_last);  // slots past the thread's run re-read its last one
+      st_own[k] = slot_stamp[slot_base + s];
+      held[k] = slot_loc[slot_base + s];
+    }
+  }
+
+  // ---- F, first round: host reads of the miss rows (known since A) go out now ----
+  const int chunks = row_bytes >> 4;
+  const int total = need * chunks;
+  constexpr int kUnroll = 8;
+  i32x4 v[kUnroll];
+  // All kUnroll loads are issued before the first store: chunks past the end re-read the
+  // last chunk (no branch around a load, which would make each load wait for the one before
+  // it) and are not stored.
+  auto load_round = [&](int base) {
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int c = min(base + u * kThreads + tid, total - 1);
+      const int mi = c / chunks;
+      const int part = c - mi * chunks;
+      v[u] = *reinterpret_cast<const i32x4 *>(host_pool + (int64_t)sm.miss_row[mi] * row_bytes + part * 16);
+    }
+  };
+  if (need > 0) load_round(0);
+
   if (need > 0) {
     // ---- B: radix select of the need-th smallest key among unpinned slots ----
     uint32_t prefix = 0;
@@ -148,9 +187,11 @@ __global__ __launch_bounds__(kThreads) void swap_in_kernel(
       for (int i = tid; i < 256; i += kThreads) sm.hist[i] = 0;
       if (tid == 0) { sm.sel[0] = 0; sm.sel[1] = remaining; }
       __syncthreads();
-      for (int s = tid; s < capacity; s += kThreads) {
-        if (sm.pinned[s]) continue;
-        const uint32_t key = order_key(stamps[s]);
+#pragma unroll
+      for (int k = 0; k < kSper; ++k) {
+        const int s = s0 + k;
+        if (k >= sper || s >= capacity || sm.pinned[s]) continue;
+        const uint32_t key = order_key(st_own[k]);
         if (pass == 0 || (key >> (shift + 8)) == (prefix >> (shift + 8)))
           atomicAdd(&sm.hist[(key >> shift) & 255u], 1);
       }
@@ -182,51 +223,48 @@ __global__ __launch_bounds__(kThreads) void swap_in_kernel(
     const uint32_t tau = prefix;
     const int take_eq = remaining;  // slots with key == tau to take, lowest slot first
 
-    // ---- C: victims in ascending slot order (thread owns slots [s0, s0 + sper)) ----
-    const int sper = (capacity + kThreads - 1) / kThreads;
-    const int s0 = tid * sper;
+    // ---- C: victims in ascending slot order ----
     int my_eq = 0;
-    for (int k = 0; k < sper; ++k) {
+#pragma unroll
+    for (int k = 0; k < kSper; ++k) {
       const int s = s0 + k;
-      if (s >= capacity) break;
-      if (!sm.pinned[s] && order_key(stamps[s]) == tau) ++my_eq;
+      if (k < sper && s < capacity && !sm.pinned[s] && order_key(st_own[k]) == tau) ++my_eq;
     }
     int unused;
     int eq_rank = block_exclusive_scan(my_eq, sm.scan, unused);
     int my_vic = 0;
-    uint32_t flags = 0;  // sper <= 16 (capacity <= 16384)
-    for (int k = 0; k < sper; ++k) {
+    uint32_t flags = 0;
+#pragma unroll
+    for (int k = 0; k < kSper; ++k) {
       const int s = s0 + k;
-      if (s >= capacity) break;
-      if (sm.pinned[s]) continue;
-      const uint32_t key = order_key(stamps[s]);
-      bool v = false;
+      if (k >= sper || s >= capacity || sm.pinned[s]) continue;
+      const uint32_t key = order_key(st_own[k]);
+      bool vk = false;
       if (key < tau) {
-        v = true;
+        vk = true;
       } else if (key == tau) {
-        v = eq_rank < take_eq;
+        vk = eq_rank < take_eq;
         ++eq_rank;
       }
-      if (v) { flags |= 1u << k; ++my_vic; }
+      if (vk) { flags |= 1u << k; ++my_vic; }
     }
     int vrank = block_exclusive_scan(my_vic, sm.scan, unused);
-    for (int k = 0; k < sper; ++k)
-      if ((flags & (1u << k)) && vrank < need) sm.victim[vrank++] = s0 + k;
-    __syncthreads();
 
-    // ---- D: install misses into victims ----
-    // A row repeated within the request installs once per copy.  Two writes to one
-    // loc_to_hot entry (two copies, or an install and an eviction of a slot still holding
-    // the row) land in no set order; either way the entry names -1 or a slot with the row.
-    for (int i = tid; i < need; i += kThreads) {
-      const int v = sm.victim[i];
+    // ---- D: the slot's owner installs miss vrank into it; the evicted row's map entry is
+    // cleared ----
+#pragma unroll
+    for (int k = 0; k < kSper; ++k) {
+      if (!(flags & (1u << k)) || vrank >= need) continue;
+      const int i = vrank++;
+      const int vs = s0 + k;
       const int row = sm.miss_row[i];
-      const int64_t g = slot_base + v;
-      const int old = slot_loc[g];
+      const int64_t g = slot_base + vs;
+      const int old = held[k];
       if (old >= 0 && old < host_rows) loc_to_hot[old] = -1;
       slot_loc[g] = row;
       loc_to_hot[row] = (int32_t)g;
-      sm.slot_of_entry[sm.miss_entry[i]] = v;
+      sm.victim[i] = vs;
+      sm.slot_of_entry[sm.miss_entry[i]] = vs;
     }
     __syncthreads();
   }
@@ -243,27 +281,17 @@ __global__ __launch_bounds__(kThreads) void swap_in_kernel(
   }
 
   // ---- F: copy miss rows host pool -> hot buffer, 16 bytes per lane access ----
-  const int chunks = row_bytes >> 4;
-  const int total = need * chunks;
-  constexpr int kUnroll = 8;
   for (int base = 0; base < total; base += kThreads * kUnroll) {
-    // All kUnroll loads are issued before the first store: chunks past the end re-read the
-    // last chunk (no branch around a load, which would make each load wait for the one
-    // before it) and are not stored.
-    i32x4 v[kUnroll];
-    int64_t dst[kUnroll];
+    if (base > 0) load_round(base);
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-      const int c = min(base + u * kThreads + tid, total - 1);
-      const int mi = c / chunks;
-      const int part = c - mi * chunks;
-      const int64_t src = (int64_t)sm.miss_row[mi] * row_bytes + part * 16;
-      v[u] = *reinterpret_cast<const i32x4 *>(host_pool + src);
-      dst[u] = (slot_base + sm.victim[mi]) * row_bytes + part * 16;
+      const int c = base + u * kThreads + tid;
+      if (c < total) {
+        const int mi = c / chunks;
+        const int part = c - mi * chunks;
+        *reinterpret_cast<i32x4 *>(hot_kv + (slot_base + sm.victim[mi]) * row_bytes + part * 16) = v[u];
+      }
     }
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u)
-      if (base + u * kThreads + tid < total) *reinterpret_cast<i32x4 *>(hot_kv + dst[u]) = v[u];
   }
 }
 
@@ -276,12 +304,14 @@ hipError_t launch_swap_in(const hs_hot_state &st, const void *host_pool_dev,
   const int elem = st.dtype == HS_BF16 ? 2 : 4;
   const int32_t row_bytes = st.row_elems * elem;
   const size_t lds = lds_bytes(topk, st.capacity);
+  // slots per thread held in registers: 4 up to 4096 slots, else up to 16 (16384 slots)
+  const auto kern = st.capacity <= 4 * kThreads ? swap_in_kernel<4> : swap_in_kernel<16>;
   if (lds > 65536) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(swap_in_kernel),
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(swap_in_kernel, dim3(st.num_reqs), dim3(kThreads), lds, stream, st.capacity,
+  hipLaunchKernelGGL(kern, dim3(st.num_reqs), dim3(kThreads), lds, stream, st.capacity,
                      st.slot_loc, st.slot_stamp, st.loc_to_hot, st.host_rows, row_bytes,
                      static_cast<uint8_t *>(st.hot_kv), static_cast<const uint8_t *>(host_pool_dev),
                      wave_rows, topk, tick, out_hot_idx, out_miss_count, out_miss_pos);
