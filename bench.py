@@ -325,6 +325,7 @@ def gpu_busy(us=100.0):
 
 
 MFMA_BF16_PEAK_TFLOPS = 2500.0
+SETTLE_MS = 50.0  # untimed back-to-back work before a timed region (clock settling)
 
 
 def measure_attn_sweep(dev, sizes=(32, 64, 128, 256), reps=50):
@@ -351,10 +352,18 @@ def measure_attn_sweep(dev, sizes=(32, 64, 128, 256), reps=50):
         lse = torch.empty((rows, H), dtype=torch.float32, device=dev)
         wsb = hs.hs_attn_workspace_bytes(rows, H, D, DV, K, torch.bfloat16)
         ws = torch.empty((max(wsb, 16),), dtype=torch.uint8, device=dev) if wsb else None
+        # Untimed warm-up of >= SETTLE_MS of back-to-back calls: the shader clock takes tens
+        # of milliseconds of sustained load to settle, and calls timed before that run slow.
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(main)
         for _ in range(5):
             hs.hs_sparse_decode_attn(q, kv, idx, D ** -0.5, DV, out, lse, ws)
+        e1.record(main)
         torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        est_us = e0.elapsed_time(e1) * 1e3 / 5
+        for _ in range(int(SETTLE_MS * 1e3 / max(est_us, 1.0)) + 1):
+            hs.hs_sparse_decode_attn(q, kv, idx, D ** -0.5, DV, out, lse, ws)
+        torch.cuda.synchronize()
         e0.record(main)
         for _ in range(reps):
             hs.hs_sparse_decode_attn(q, kv, idx, D ** -0.5, DV, out, lse, ws)
@@ -640,7 +649,10 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    # The default warm-up covers the shader clock's settling time (tens of ms of sustained
+    # load; the resident step takes ~17 us, so 3000 steps are ~50 ms): steps timed before
+    # that run about 7 % slow.
+    ap.add_argument("--warmup", type=int, default=3000)
     ap.add_argument("--workload", default="resident")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-graph", action="store_true")
