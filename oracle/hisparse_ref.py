@@ -138,9 +138,15 @@ def swap_in(st: HotState, wave_rows: np.ndarray, tick: int, host_pool: np.ndarra
        ``loc_to_hot[L[j]] >= 0``; misses are listed in ascending ``j``;
     2. hit slots are pinned for this wave; the victims are the ``#misses``
        least-recently-used unpinned slots (stamp, then slot, ascending);
-    3. miss ``m`` goes to the ``m``-th victim in ascending slot order: the evicted
-       row's map entry is cleared, the new row mapped, its KV copied bitwise;
+    3. miss ``m`` goes to the ``m``-th victim in ascending slot order, applied in that
+       order: the evicted row's map entry is cleared if it names the evicted slot, the
+       new row is mapped to its slot, its KV copied bitwise;
     4. every valid entry's slot gets stamp ``tick``; ``hot_idx = b*cap + slot``.
+
+    A host row belongs to one request (no shared prefix pages): a row of request ``b``
+    mapped into another request's slots is a caller error (``ValueError``).  Rows
+    repeated within a request (top-k sets never repeat) follow from the order in 3:
+    each copy of a miss takes its own victim and the map names the last one installed.
 
     Mutates ``st``.  Returns ``(hot_idx [B,K], miss_count [B], miss_pos [B,K])``
     (``miss_pos`` is -1 past ``miss_count``).
@@ -158,6 +164,8 @@ def swap_in(st: HotState, wave_rows: np.ndarray, tick: int, host_pool: np.ndarra
         hotg[valid] = st.loc_to_hot[L[valid]]
         hit = valid & (hotg >= 0)
         miss = valid & (hotg < 0)
+        if ((hotg[hit] < b * cap) | (hotg[hit] >= (b + 1) * cap)).any():
+            raise ValueError(f"request {b} selects a host row mapped into another request's slots")
         M = np.nonzero(miss)[0]
         slot = np.full(K, -1, dtype=np.int64)
         slot[hit] = hotg[hit] - b * cap
@@ -167,7 +175,7 @@ def swap_in(st: HotState, wave_rows: np.ndarray, tick: int, host_pool: np.ndarra
         for m in range(len(M)):
             v, j = int(V[m]), int(M[m])
             old = int(st.slot_loc[b, v])
-            if old >= 0:
+            if old >= 0 and st.loc_to_hot[old] == b * cap + v:
                 st.loc_to_hot[old] = -1
             st.slot_loc[b, v] = L[j]
             st.loc_to_hot[L[j]] = b * cap + v
@@ -347,8 +355,10 @@ def finalize_accepted(st: HotState, host_pool: np.ndarray, new_kv: np.ndarray,
     that position is emptied (map cleared, stamp -1); its host row is left alone.  Rows
     ``r <= L_b`` are kept: ``new_kv`` is written to the position's host row and to the
     hot buffer (overwrite if resident, else install with the swap-in victim rule, the
-    slots of this request's resident kept rows pinned), stamp ``tick``.  Rejected rows
-    are processed before kept rows.  Returns ``committed = n + L_b + 1`` per request.
+    slots of this request's resident kept rows pinned, an evicted row's map entry
+    cleared if it names the evicted slot), stamp ``tick``.  Rejected rows are processed
+    before kept rows.  As in ``swap_in``, a row mapped into another request's slots is a
+    caller error.  Returns ``committed = n + L_b + 1`` per request.
     Mutates ``st`` and ``host_pool``.
     """
     B, R, cap = len(seq_len), rows_per_req, st.capacity
@@ -364,6 +374,9 @@ def finalize_accepted(st: HotState, host_pool: np.ndarray, new_kv: np.ndarray,
         for r in range(L + 1, R):
             loc = int(locs[r])
             if loc >= 0 and st.loc_to_hot[loc] >= 0:
+                if not b * cap <= st.loc_to_hot[loc] < (b + 1) * cap:
+                    raise ValueError(f"request {b} drops a host row mapped into another "
+                                     "request's slots")
                 s = int(st.loc_to_hot[loc]) - b * cap
                 st.slot_loc[b, s] = -1
                 st.slot_stamp[b, s] = -1
@@ -375,6 +388,8 @@ def finalize_accepted(st: HotState, host_pool: np.ndarray, new_kv: np.ndarray,
             loc = int(locs[r])
             host_pool[loc] = new_kv[r * B + b]
             g = int(st.loc_to_hot[loc])
+            if g >= 0 and not b * cap <= g < (b + 1) * cap:
+                raise ValueError(f"request {b} keeps a host row mapped into another request's slots")
             if g >= 0:
                 pinned[g - b * cap] = True
                 st.hot_kv[g] = new_kv[r * B + b]
@@ -385,7 +400,7 @@ def finalize_accepted(st: HotState, host_pool: np.ndarray, new_kv: np.ndarray,
         for m, r in enumerate(miss_rows):
             v, loc = int(V[m]), int(locs[r])
             old = int(st.slot_loc[b, v])
-            if old >= 0:
+            if old >= 0 and st.loc_to_hot[old] == b * cap + v:
                 st.loc_to_hot[old] = -1
             st.slot_loc[b, v] = loc
             st.loc_to_hot[loc] = b * cap + v

@@ -133,3 +133,102 @@ def test_finalize_installs_misses_with_lru_rule():
     assert st.slot_loc[0].tolist()[:3] == [3, 12, 13]
     assert st.slot_stamp[0].tolist() == [50, 50, 50, 13, 14, 15]
     check_state_invariants(st, pool)
+
+
+def test_finalize_pins_kept_hits_when_tick_is_not_newest():
+    """Worked by hand.  Block size 4, table [1, 0]: verify positions 6 and 7 (R = 2) live in
+    host rows 2 and 3.  Slot 0 holds row 2 (stamp 10); slots 1-3 hold rows 8, 9, 10 (stamps
+    11-13).  Both rows are kept (L = 1) with tick 5, below every stamp.  Row 2 hits slot 0:
+    overwritten and restamped 5, and pinned, so although its stamp is now the lowest the miss
+    of row 3 must evict slot 1 (stamp 11), not slot 0."""
+    bs = 4
+    seq = np.array([8], np.int32)
+    bt = np.array([[1, 0]], np.int32)
+    pool = np.arange(16 * 2, dtype=np.float32).reshape(16, 2)
+    st = HotState(4, np.array([[2, 8, 9, 10]], np.int32), np.array([[10, 11, 12, 13]], np.int32),
+                  np.full(16, -1, np.int32), pool[[2, 8, 9, 10]].copy())
+    st.loc_to_hot[[2, 8, 9, 10]] = [0, 1, 2, 3]
+    rows, _ = resolve_topk(np.array([[6, 7]], np.int32), np.array([0], np.int32), seq, bt, bs, bs, 1)
+    assert rows.tolist() == [[2, 3]]
+    new_kv = np.array([[-1.0, -2.0], [-3.0, -4.0]], np.float32)
+    committed = finalize_accepted(st, pool, new_kv, np.array([1]), seq, bt, bs, 2, tick=5)
+    assert committed.tolist() == [8]
+    assert st.slot_loc[0].tolist() == [2, 3, 9, 10]
+    assert st.slot_stamp[0].tolist() == [5, 5, 12, 13]
+    assert st.loc_to_hot[2] == 0 and st.loc_to_hot[3] == 1 and st.loc_to_hot[8] == -1
+    assert np.array_equal(st.hot_kv[[0, 1]], new_kv)
+    assert np.array_equal(pool[[2, 3]], new_kv)
+    check_state_invariants(st, pool)
+
+
+def test_finalize_keeps_every_kept_row_resident_at_any_tick():
+    """Random states and ticks (including ticks below existing stamps): after finalize every
+    kept row is resident and holds its new KV, every dropped position is not, and the maps
+    stay mutually inverse."""
+    rng = np.random.default_rng(11)
+    for trial in range(60):
+        bs, cap, R = 4, int(rng.integers(4, 10)), int(rng.integers(1, 4))
+        npages = 8
+        seq = np.array([int(rng.integers(R, npages * bs + 1))], np.int32)
+        bt = rng.permutation(npages).astype(np.int32)[None]
+        pool = rng.standard_normal((npages * bs, 3)).astype(np.float32)
+        n_res = int(rng.integers(0, min(cap, int(seq[0])) + 1))
+        init_pos = np.full((1, cap), -1, np.int32)
+        init_stamp = np.full((1, cap), -1, np.int32)
+        where = rng.choice(cap, n_res, replace=False)
+        init_pos[0, where] = rng.choice(int(seq[0]), n_res, replace=False)
+        init_stamp[0, where] = rng.integers(0, 20, size=n_res)
+        st = build_hot_state(init_pos, init_stamp, seq, bt, bs, pool)
+        new_kv = rng.standard_normal((R, 3)).astype(np.float32)
+        L = int(rng.integers(0, R))
+        tick = int(rng.integers(0, 25))
+        finalize_accepted(st, pool, new_kv, np.array([L]), seq, bt, bs, R, tick=tick)
+        rows, _ = resolve_topk((seq[0] - R + np.arange(R, dtype=np.int32))[None], np.array([0], np.int32),
+                               seq, bt, bs, bs, 1)
+        for r in range(R):
+            g = st.loc_to_hot[rows[0, r]]
+            if r <= L:
+                assert g >= 0, (trial, r)
+                assert np.array_equal(st.hot_kv[g], new_kv[r]) and st.slot_stamp[0, g] == tick
+            else:
+                assert g == -1, (trial, r)
+        check_state_invariants(st, pool)
+
+
+def test_argmax_ignores_nan_like_numpy_nanargmax():
+    """NaN never wins: on rows that hold NaNs next to finite values the argmax is numpy's
+    nanargmax (lowest index of the largest non-NaN value).  A row of only NaN and -inf
+    has no winner and keeps the lowest index, 0."""
+    rng = np.random.default_rng(12)
+    lg = rng.standard_normal((40, 33)).astype(np.float32)
+    for i in range(40):
+        lg[i, rng.choice(33, int(rng.integers(1, 10)), replace=False)] = np.nan
+    lg[3, :] = np.nan
+    lg[3, 5] = -np.inf
+    t = torch.from_numpy(lg).to(torch.bfloat16)
+    _, _, am = greedy_accept(raw(t), np.zeros(40, np.int32), 40, 1)
+    f = t.float().numpy()
+    for i in range(40):
+        if i == 3:
+            assert am[i] == 0
+        else:
+            assert am[i] == np.nanargmax(f[i]), i
+
+
+def test_finalize_eviction_keeps_the_map_of_a_live_copy():
+    """Worked by hand.  Slot 1 holds a stale copy of row 9 (the map names slot 0).  The one
+    verify row (position 7: page index 1 -> table entry 0 -> host row 3) is kept and missing,
+    so it evicts the least-recent slot, slot 1 (stamp 0).  loc_to_hot[9] keeps naming slot 0."""
+    bs = 4
+    seq = np.array([8], np.int32)
+    bt = np.array([[1, 0]], np.int32)
+    pool = np.arange(16 * 2, dtype=np.float32).reshape(16, 2)
+    st = HotState(4, np.array([[9, 9, 10, 11]], np.int32), np.array([[1, 0, 5, 6]], np.int32),
+                  np.full(16, -1, np.int32), pool[[9, 9, 10, 11]].copy())
+    st.loc_to_hot[[9, 10, 11]] = [0, 2, 3]
+    new_kv = np.array([[-5.0, -6.0]], np.float32)
+    finalize_accepted(st, pool, new_kv, np.array([0]), seq, bt, bs, 1, tick=20)
+    assert st.slot_loc[0].tolist() == [9, 3, 10, 11]
+    assert st.slot_stamp[0].tolist() == [1, 20, 5, 6]
+    assert st.loc_to_hot[9] == 0 and st.loc_to_hot[3] == 1
+    assert np.array_equal(st.hot_kv[1], new_kv[0]) and np.array_equal(pool[3], new_kv[0])

@@ -56,3 +56,12 @@ def test_residency_rules_hand_worked():
     seq = np.array([18, 8, 13])
     assert oracle.reclaimable_pages(bt, seq, 4) == [(0, 0), (0, 1), (2, 0), (2, 1)]
     assert oracle.is_fully_resident(bt, seq, 4).tolist() == [False, True, True]
+
+
+def test_fully_resident_needs_every_used_page_inside_the_table_row():
+    """A request whose token count needs more pages than its table row has cannot be fully
+    resident, even when every entry the row does have is mapped.  Block size 4: 9 tokens use
+    pages 0, 1 and 2, but the table rows are 2 wide; 8 tokens fit; 0 tokens need no page."""
+    bt = np.array([[3, 5], [1, 2], [-1, -1]])
+    seq = np.array([9, 8, 0])
+    assert oracle.is_fully_resident(bt, seq, 4).tolist() == [False, True, True]

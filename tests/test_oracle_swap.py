@@ -195,6 +195,43 @@ def _duplicate_waves(name, over):
                 else:
                     seen_miss_dup += 1
                     assert len(np.unique(hot_idx[b, js])) == len(js)
-                    if t == 0:
-                        assert st.loc_to_hot[row] == hot_idx[b, js[-1]]
+                    # the map names the copy installed last (the highest victim slot)
+                    assert st.loc_to_hot[row] == hot_idx[b, js[-1]]
+            # no eviction of a stale copy unmaps a row this wave selected
+            assert (st.loc_to_hot[wave[b, valid[b]]] >= 0).all()
     assert seen_hit_dup > 0 and seen_miss_dup > 0
+
+
+def test_swap_map_rule_for_repeats_and_stale_copies_hand_worked():
+    """Worked by hand.  Slot 2 holds a stale copy of row 10 (the map names slot 0 for it);
+    the wave selects row 20 twice and row 11 once.  Row 11 hits slot 1 (pinned).  Victims:
+    the two least-recent unpinned slots by (stamp, slot) are slot 3 (empty, -1) and slot 2
+    (stamp 0); in ascending slot order miss 0 -> slot 2, miss 1 -> slot 3.  Evicting slot 2
+    leaves loc_to_hot[10] alone (it names slot 0), and the map names slot 3, the copy of
+    row 20 installed last."""
+    pool = np.arange(100 * 2, dtype=np.float32).reshape(100, 2)
+    st = _empty_state(1, 4, 100, 2)
+    for slot, row, stamp in ((0, 10, 1), (1, 11, 2), (2, 10, 0)):
+        st.slot_loc[0, slot], st.slot_stamp[0, slot] = row, stamp
+        st.hot_kv[slot] = pool[row]
+    st.loc_to_hot[10], st.loc_to_hot[11] = 0, 1
+    hot_idx, mc, mp = swap_in(st, np.array([[20, 20, 11]], np.int32), 5, pool)
+    assert hot_idx.tolist() == [[2, 3, 1]]
+    assert mc.tolist() == [2] and mp.tolist() == [[0, 1, -1]]
+    assert st.slot_loc[0].tolist() == [10, 11, 20, 20]
+    assert st.slot_stamp[0].tolist() == [1, 5, 5, 5]
+    assert st.loc_to_hot[10] == 0 and st.loc_to_hot[11] == 1 and st.loc_to_hot[20] == 3
+    assert np.array_equal(st.hot_kv[[2, 3]], pool[[20, 20]])
+
+
+def test_swap_rejects_a_row_owned_by_another_request():
+    """Host rows belong to one request: request 0 selecting a row that request 1's slot
+    holds is a caller error, and nothing is written."""
+    pool = np.zeros((50, 2), np.float32)
+    st = _empty_state(2, 4, 50, 2)
+    st.slot_loc[1, 2], st.slot_stamp[1, 2], st.loc_to_hot[7] = 7, 3, 4 + 2
+    before = st.copy()
+    with pytest.raises(ValueError):
+        swap_in(st, np.array([[7, 8], [-1, -1]], np.int32), 9, pool)
+    assert np.array_equal(st.slot_loc, before.slot_loc)
+    assert np.array_equal(st.loc_to_hot, before.loc_to_hot)
