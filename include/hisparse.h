@@ -137,21 +137,25 @@ hs_status hs_resolve_topk(const int32_t *topk_pos, int32_t num_rows, int32_t top
  *   out_miss_pos   [num_reqs, topk] int32 or NULL  entry indices of the misses in
  *                                          ascending order, -1 after miss_count
  *
+ * Precondition: a host row belongs to one request (no shared prefix pages), so
+ * loc_to_hot[row] is -1 or a slot of the request that selects the row.  Outside it the
+ * results are not defined (every access still stays in bounds).
  * Rule (the pages print none; this is the library's definition): an entry hits iff
- * loc_to_hot[row] >= 0; hit slots are pinned; the victims are the #misses unpinned slots
- * with the smallest (stamp, slot); miss m (ascending entry index) takes the m-th victim
- * in ascending slot order, the evicted row's loc_to_hot entry is cleared and the host
- * row is copied bit for bit into hot_kv; every used slot gets stamp `tick`.
+ * loc_to_hot[row] names a slot of its request; hit slots are pinned; the victims are the
+ * #misses unpinned slots with the smallest (stamp, slot); miss m (ascending entry index)
+ * takes the m-th victim in ascending slot order.  Applied in that order: the evicted
+ * row's loc_to_hot entry is cleared if it names the evicted slot, the miss's row is
+ * mapped to its slot, and the host row is copied bit for bit into hot_kv.  Every used
+ * slot gets stamp `tick`.
  * Repeated host rows within one request (top-k sets have none): each copy of a hit uses
  * that hit's slot; each copy of a miss is a miss of its own (counted and listed) and takes
- * its own victim, so every hot index still names a slot that holds its row.  When two
- * writes to one row's loc_to_hot entry fall in one call (two copies of a miss, or an
- * install and the eviction of a slot still holding that row), which write lands last is
- * not defined.  A row's entry, when set, always names a slot holding that row; a copy the
- * map does not name stays resident until it is evicted.
- * hot_kv is written only by work queued on `stream`; it may run concurrently with
- * attention over an earlier wave when capacity >= 2*topk (victims are then never slots
- * the previous wave used).
+ * its own victim, so every hot index names a slot that holds its row, and the row's map
+ * entry names the copy installed last (the highest of those slots).  A copy the map does
+ * not name stays resident until it is evicted; evicting it leaves the map alone.
+ * hot_kv is written only by work queued on `stream`.  It may run concurrently with
+ * attention over the previous wave when capacity >= 2*topk and `tick` is above every
+ * stamp that was in the state before that wave: the previous wave's slots then hold the
+ * newest stamp and are never victims.
  * Errors: HS_ERR_CAPACITY if topk > capacity; HS_ERR_INVALID_ARG for null pointers,
  * non-positive sizes, row bytes not a multiple of 16 or misaligned hot_kv/host_pool,
  * or a host_pool that is not device-accessible pinned memory; HS_ERR_UNSUPPORTED for
@@ -319,7 +323,9 @@ hs_status hs_sparse_decode_attn_mixed(const void *q, const void *kv_a, int64_t k
  * emptied; the host row is left as is); rows r <= L_b have new_kv written to their
  * host-pool row (PINNED HOST, device stores) and to the hot buffer (overwrite if
  * resident, else installed with the hs_swap_in victim rule, the slots of the request's
- * resident kept rows pinned), stamp `tick`.  Dropped rows are processed first.
+ * resident kept rows pinned, an evicted row's map entry cleared only if it names the
+ * evicted slot), stamp `tick`.  Dropped rows are processed first.  The hs_swap_in
+ * precondition applies: a verify row's host row is unmapped or mapped into its request.
  * Errors: HS_ERR_INVALID_ARG (null pointers, sizes, rows_per_req < 1 or >
  * st->capacity, vocab < 1); HS_ERR_UNSUPPORTED (rows_per_req > 64).
  */
@@ -400,6 +406,22 @@ hs_status hs_append_accepted(void *ctx_cache, int64_t ctx_rows, int32_t row_byte
                              int32_t block_size, int32_t physical_block_stride, int32_t *ctx_len,
                              const void *new_rows, const int32_t *accept_len, int32_t num_reqs,
                              int32_t rows_per_req, void *stream);
+
+/*
+ * hs_host_read -- the host link's reference read rate (not a step of the path): copies
+ * `bytes` from pinned host memory into device memory with a streaming zero-copy kernel,
+ * the same kind of access the swap-in copy makes to the pinned host pool (P1 "1. 启动阶段":
+ * pinned host pool; P3 "数据 back up": host cache in pinned DRAM), but over one contiguous
+ * range.  Asynchronous on `stream`.
+ *
+ *   host_src  PINNED HOST, 16-byte aligned, device-accessible
+ *   dst       device memory, 16-byte aligned, at least `bytes` long
+ *   bytes     a multiple of 16 (0 is a no-op)
+ *
+ * Errors: HS_ERR_INVALID_ARG (null or misaligned pointers, bytes not a multiple of 16 or
+ * negative, host_src not pinned host memory).
+ */
+hs_status hs_host_read(const void *host_src, void *dst, int64_t bytes, void *stream);
 
 /* Static description of a status code. */
 const char *hs_status_string(int32_t status);

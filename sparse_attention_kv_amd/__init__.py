@@ -24,7 +24,7 @@ HS_BF16, HS_F32 = 0, 1
 EXPORTED = ("hs_resolve_topk", "hs_swap_in", "hs_sparse_decode_attn", "hs_sparse_decode_attn_paged",
             "hs_sparse_decode_attn_mixed",
             "hs_attn_workspace_bytes", "hs_attn_plan_info", "hs_finalize_accepted", "hs_backup_rows", "hs_apply_plan",
-            "hs_append_accepted",
+            "hs_append_accepted", "hs_host_read",
             "hs_status_string", "hs_version")
 
 
@@ -75,6 +75,8 @@ def _load() -> ctypes.CDLL:
     lib.hs_apply_plan.restype = i32
     lib.hs_append_accepted.argtypes = [vp, i64, i32, vp, i32, i32, i32, vp, vp, vp, i32, i32, vp]
     lib.hs_append_accepted.restype = i32
+    lib.hs_host_read.argtypes = [vp, vp, i64, vp]
+    lib.hs_host_read.restype = i32
     lib.hs_status_string.argtypes = [i32]
     lib.hs_status_string.restype = ctypes.c_char_p
     lib.hs_version.argtypes = []
@@ -100,6 +102,13 @@ def _check(fn: str, status: int):
 
 def _ptr(t: Optional[torch.Tensor]):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _shape(ok: bool, what: str):
+    """Shape agreement between arguments, checked before any device or dtype check: a
+    mis-sized buffer would otherwise become an out-of-bounds device access."""
+    if not ok:
+        raise ValueError(f"shape mismatch: {what}")
 
 
 def _dev(t: torch.Tensor, name: str, dtype=None):
@@ -132,12 +141,17 @@ def hs_resolve_topk(topk_pos: torch.Tensor, req_id: torch.Tensor, causal_limit: 
                     stream=None):
     """Top-k token positions [rows, topk] -> physical KV rows (see include/hisparse.h)."""
     i32 = torch.int32
+    _shape(topk_pos.dim() == 2 and block_table.dim() == 2, "topk_pos and block_table must be 2-D")
+    rows, topk = topk_pos.shape
+    _shape(tuple(req_id.shape) == (rows,) and tuple(causal_limit.shape) == (rows,),
+           "req_id and causal_limit must be [rows]")
+    _shape(out_slots.shape == topk_pos.shape, "out_slots must be [rows, topk]")
+    _shape(out_valid is None or tuple(out_valid.shape) == (rows,), "out_valid must be [rows]")
     _dev(topk_pos, "topk_pos", i32); _dev(req_id, "req_id", i32)
     _dev(causal_limit, "causal_limit", i32); _dev(block_table, "block_table", i32)
     _dev(out_slots, "out_slots", i32)
     if out_valid is not None:
         _dev(out_valid, "out_valid", i32)
-    rows, topk = topk_pos.shape
     num_reqs, bt_stride = block_table.shape
     _check("hs_resolve_topk", _lib.hs_resolve_topk(
         _ptr(topk_pos), rows, topk, _ptr(req_id), _ptr(causal_limit), num_reqs,
@@ -153,10 +167,31 @@ class HotState:
     loc_to_hot: torch.Tensor   # int32 [host_rows]
     hot_kv: torch.Tensor       # [num_reqs * capacity, row_elems]
     host_pool: torch.Tensor    # pinned host [host_rows, row_elems] (or device)
+    # Host-side record of the newest tick stamped into this state through the wrappers
+    # (None: unknown).  DecodeStep overlaps wave r+1's swap with wave r's attention only
+    # when its first tick is above it (victims are then never slots wave r uses).
+    max_stamp: Optional[int] = None
+
+    def note_tick(self, tick: int):
+        self.max_stamp = tick if self.max_stamp is None else max(self.max_stamp, tick)
+
+    def check_shapes(self):
+        _shape(self.slot_loc.dim() == 2 and self.slot_stamp.shape == self.slot_loc.shape,
+               "slot_loc and slot_stamp must be [num_reqs, capacity]")
+        num_reqs, cap = self.slot_loc.shape
+        _shape(self.loc_to_hot.dim() == 1 and self.host_pool.dim() == 2 and
+               self.loc_to_hot.shape[0] == self.host_pool.shape[0],
+               "loc_to_hot must be [host_rows] with host_pool [host_rows, row_elems]")
+        _shape(self.hot_kv.dim() == 2 and self.hot_kv.shape[0] == num_reqs * cap and
+               self.hot_kv.shape[1] == self.host_pool.shape[1],
+               "hot_kv must be [num_reqs * capacity, row_elems]")
 
     def as_struct(self) -> HsHotState:
+        self.check_shapes()
         for name in ("slot_loc", "slot_stamp", "loc_to_hot", "hot_kv"):
             _dev(getattr(self, name), name)
+        for name in ("slot_loc", "slot_stamp", "loc_to_hot"):
+            _dev(getattr(self, name), name, torch.int32)
         if not self.host_pool.is_contiguous():
             raise ValueError("host_pool must be contiguous")
         if self.host_pool.dtype != self.hot_kv.dtype:
@@ -173,6 +208,14 @@ def hs_swap_in(state: HotState, wave_rows: torch.Tensor, tick: int, out_hot_idx:
                stream=None):
     """One wave of swap-in: wave_rows [num_reqs, topk] host rows (see include/hisparse.h)."""
     i32 = torch.int32
+    state.check_shapes()
+    num_reqs = state.slot_loc.shape[0]
+    _shape(wave_rows.dim() == 2 and wave_rows.shape[0] == num_reqs,
+           "wave_rows must be [num_reqs, topk]")
+    _shape(out_hot_idx.shape == wave_rows.shape, "out_hot_idx must be [num_reqs, topk]")
+    _shape(tuple(out_miss_count.shape) == (num_reqs,), "out_miss_count must be [num_reqs]")
+    _shape(out_miss_pos is None or out_miss_pos.shape == wave_rows.shape,
+           "out_miss_pos must be [num_reqs, topk]")
     _dev(wave_rows, "wave_rows", i32); _dev(out_hot_idx, "out_hot_idx", i32)
     _dev(out_miss_count, "out_miss_count", i32)
     if out_miss_pos is not None:
@@ -181,6 +224,7 @@ def hs_swap_in(state: HotState, wave_rows: torch.Tensor, tick: int, out_hot_idx:
     _check("hs_swap_in", _lib.hs_swap_in(ctypes.byref(st), _ptr(wave_rows), wave_rows.shape[1],
                                          tick, _ptr(out_hot_idx), _ptr(out_miss_count),
                                          _ptr(out_miss_pos), _stream(stream)))
+    state.note_tick(tick)
 
 
 def hs_attn_workspace_bytes(num_rows: int, num_heads: int, d_qk: int, d_v: int, topk: int,
@@ -203,6 +247,7 @@ def hs_sparse_decode_attn(q: torch.Tensor, kv: torch.Tensor, indices: torch.Tens
                           d_v: int, out: torch.Tensor, lse: Optional[torch.Tensor] = None,
                           workspace: Optional[torch.Tensor] = None, stream=None):
     """Sparse attention of q [rows, H, d_qk] over kv[indices] (see include/hisparse.h)."""
+    _attn_shapes(q, kv, indices, d_v, out, lse)
     _dev(q, "q"); _dev(kv, "kv"); _dev(indices, "indices", torch.int32); _dev(out, "out", q.dtype)
     if kv.dtype != q.dtype:
         raise ValueError("q and kv dtypes differ")
@@ -218,10 +263,25 @@ def hs_sparse_decode_attn(q: torch.Tensor, kv: torch.Tensor, indices: torch.Tens
         _stream(stream)))
 
 
+def _attn_shapes(q, kv, indices, d_v, out, lse):
+    _shape(q.dim() == 3 and kv.dim() == 2 and indices.dim() == 2, "q [rows, H, d_qk], kv "
+           "[kv_rows, d_qk] and indices [rows, topk] expected")
+    rows, heads, d_qk = q.shape
+    _shape(kv.shape[1] == d_qk, "kv rows must be d_qk wide")
+    _shape(indices.shape[0] == rows, "indices must have one row per query row")
+    _shape(tuple(out.shape) == (rows, heads, d_v), "out must be [rows, H, d_v]")
+    _shape(lse is None or tuple(lse.shape) == (rows, heads), "lse must be [rows, H]")
+
+
 def _paged_args(q, kv_pool, topk_pos, req_id, causal_limit, block_table, block_size,
                 physical_block_stride, scale, d_v, out, lse, workspace):
     """Checks and converts the arguments of hs_sparse_decode_attn_paged (all but the stream)."""
     i32 = torch.int32
+    _attn_shapes(q, kv_pool, topk_pos, d_v, out, lse)
+    rows = q.shape[0]
+    _shape(tuple(req_id.shape) == (rows,) and tuple(causal_limit.shape) == (rows,),
+           "req_id and causal_limit must be [rows]")
+    _shape(block_table.dim() == 2, "block_table must be [num_reqs, bt_stride]")
     _dev(q, "q"); _dev(kv_pool, "kv_pool"); _dev(out, "out", q.dtype)
     _dev(topk_pos, "topk_pos", i32); _dev(req_id, "req_id", i32)
     _dev(causal_limit, "causal_limit", i32); _dev(block_table, "block_table", i32)
@@ -283,6 +343,19 @@ def hs_finalize_accepted(state: HotState, logits: torch.Tensor, draft_ids: torch
                          out_next_token: torch.Tensor, stream=None):
     """Greedy accept + accepted-prefix KV keep (see include/hisparse.h)."""
     i32 = torch.int32
+    state.check_shapes()
+    num_reqs = state.slot_loc.shape[0]
+    rows = num_reqs * rows_per_req
+    _shape(logits.dim() == 2 and logits.shape[0] == rows, "logits must be [num_reqs * rows_per_req, vocab]")
+    _shape(tuple(draft_ids.shape) == (rows,) and tuple(out_argmax.shape) == (rows,),
+           "draft_ids and out_argmax must be [num_reqs * rows_per_req]")
+    _shape(tuple(new_kv.shape) == (rows, state.hot_kv.shape[1]),
+           "new_kv must be [num_reqs * rows_per_req, row_elems]")
+    _shape(tuple(seq_len.shape) == (num_reqs,) and tuple(out_accept_len.shape) == (num_reqs,) and
+           tuple(out_next_token.shape) == (num_reqs,),
+           "seq_len, out_accept_len and out_next_token must be [num_reqs]")
+    _shape(block_table.dim() == 2 and block_table.shape[0] == num_reqs,
+           "block_table must be [num_reqs, bt_stride]")
     _dev(logits, "logits", torch.bfloat16); _dev(draft_ids, "draft_ids", i32)
     _dev(new_kv, "new_kv", state.hot_kv.dtype); _dev(seq_len, "seq_len", i32)
     _dev(block_table, "block_table", i32); _dev(out_argmax, "out_argmax", i32)
@@ -292,6 +365,7 @@ def hs_finalize_accepted(state: HotState, logits: torch.Tensor, draft_ids: torch
         ctypes.byref(st), _ptr(logits), logits.shape[1], _ptr(draft_ids), _ptr(new_kv),
         rows_per_req, _ptr(seq_len), _ptr(block_table), block_table.shape[1], block_size, tick,
         _ptr(out_argmax), _ptr(out_accept_len), _ptr(out_next_token), _stream(stream)))
+    state.note_tick(tick)
 
 
 def hs_backup_rows(dev_cache: torch.Tensor, host_cache: torch.Tensor, src_slots: torch.Tensor,
@@ -385,6 +459,8 @@ def hs_sparse_decode_attn_mixed(q: torch.Tensor, kv_a: torch.Tensor, indices_a: 
                                 workspace: Optional[torch.Tensor] = None, stream=None):
     """Attention whose rows read one of two caches (see include/hisparse.h)."""
     i32 = torch.int32
+    _attn_shapes(q, kv_a, indices_a, d_v, out, lse)
+    _shape(kv_b.dim() == 2 and kv_b.shape[1] == q.shape[2], "kv_b rows must be d_qk wide")
     _dev(q, "q"); _dev(kv_a, "kv_a", q.dtype); _dev(kv_b, "kv_b", q.dtype)
     _dev(indices_a, "indices_a", i32); _dev(indices_b, "indices_b", i32)
     _dev(row_sel, "row_sel", i32); _dev(out, "out", q.dtype)
@@ -423,3 +499,15 @@ def hs_append_accepted(ctx_cache: torch.Tensor, ctx_block_table: torch.Tensor,
         _ptr(ctx_cache), ctx_cache.shape[0], ctx_cache.shape[1] * ctx_cache.element_size(),
         _ptr(ctx_block_table), ctx_block_table.shape[1], block_size, physical_block_stride,
         _ptr(ctx_len), _ptr(new_rows), _ptr(accept_len), num_reqs, rows_per_req, _stream(stream)))
+
+
+def hs_host_read(host_src: torch.Tensor, dst: torch.Tensor, stream=None):
+    """Streaming zero-copy read of a pinned host tensor into a device tensor of the same byte
+    size: the host link's reference read rate (see include/hisparse.h)."""
+    if host_src.is_cuda or not host_src.is_pinned() or not host_src.is_contiguous():
+        raise ValueError("host_src must be a contiguous pinned host tensor")
+    nbytes = host_src.numel() * host_src.element_size()
+    _shape(dst.numel() * dst.element_size() == nbytes, "dst must hold as many bytes as host_src")
+    _dev(dst, "dst")
+    _check("hs_host_read", _lib.hs_host_read(ctypes.c_void_p(host_src.data_ptr()), _ptr(dst),
+                                             nbytes, _stream(stream)))

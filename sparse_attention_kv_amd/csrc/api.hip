@@ -293,6 +293,22 @@ hs_status hs_finalize_accepted(const hs_hot_state *st, const void *logits, int32
                                       static_cast<hipStream_t>(stream)));
 }
 
+hs_status hs_host_read(const void *host_src, void *dst, int64_t bytes, void *stream) {
+  if (bytes < 0 || bytes % 16 != 0) return HS_ERR_INVALID_ARG;
+  if (bytes == 0) return HS_OK;
+  if (!host_src || !dst || !aligned16(host_src) || !aligned16(dst)) return HS_ERR_INVALID_ARG;
+  const void *src_dev = nullptr;
+  const hs_status s = device_view(host_src, &src_dev);
+  if (s != HS_OK) return s;
+  hipPointerAttribute_t attr;
+  std::memset(&attr, 0, sizeof(attr));
+  if (hipPointerGetAttributes(&attr, host_src) != hipSuccess || attr.type != hipMemoryTypeHost) {
+    (void)hipGetLastError();
+    return HS_ERR_INVALID_ARG;  // the source must be pinned host memory
+  }
+  return from_hip(hs::launch_host_read(src_dev, dst, bytes / 16, static_cast<hipStream_t>(stream)));
+}
+
 const char *hs_status_string(int32_t status) {
   switch (status) {
     case HS_OK: return "ok";

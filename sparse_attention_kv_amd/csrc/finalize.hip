@@ -328,7 +328,10 @@ __global__ __launch_bounds__(kFinThreads) void finalize_kernel(
     const int r = s_miss[tid];
     const int64_t g = slot_base + s_slot[r];
     const int old = s_owner[r];
-    if (old >= 0 && old < host_rows) loc_to_hot[old] = -1;
+    // the evicted row is unmapped only while the map names this slot (a stale copy leaves
+    // its row's live mapping alone); the kept row's own entry is never this slot's value
+    // before the store below, so the compare-and-swap and the store commute
+    if (old >= 0 && old < host_rows && old != s_loc[r]) atomicCAS(&loc_to_hot[old], (int32_t)g, -1);
     slot_loc[g] = s_loc[r];
     loc_to_hot[s_loc[r]] = (int32_t)g;
   }

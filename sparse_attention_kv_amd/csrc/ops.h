@@ -50,4 +50,8 @@ hipError_t launch_append_accepted(void *ctx_cache, int64_t ctx_rows, int32_t row
                                   const int32_t *accept_len, int32_t num_reqs,
                                   int32_t rows_per_req, hipStream_t stream);
 
+// Streaming zero-copy read of pinned host memory (host_src_dev: its device address) into
+// device memory, chunks of 16 bytes; the host link's reference read rate.
+hipError_t launch_host_read(const void *host_src_dev, void *dst, int64_t chunks, hipStream_t stream);
+
 }  // namespace hs

@@ -17,8 +17,12 @@
 //      host reads went out, so B-E wait on no memory load while those reads are in flight.
 //   C  victims in ascending slot order: a second ordered scan over slot runs picks every
 //      unpinned slot below the threshold stamp plus the lowest-numbered ones at it.
-//   D  install: miss m takes victim m (done by the victim slot's owner); the evicted row's
-//      map entry is cleared.
+//   D  install: miss m takes victim m (done by the victim slot's owner).  The evicted row's
+//      map entry is cleared only while it names the evicted slot (a compare-and-swap), and
+//      the new row's entry takes the largest slot installed for it (an atomic max), so a
+//      row repeated within a request maps to its last install in pairing order.  Both are
+//      atomics whose results are unused: nothing waits for them, and their outcome does not
+//      depend on the order in which they reach memory.
 //   E  stamp every used slot with `tick`, emit hot indices.
 //   F  copy the miss rows from the pinned host pool into the hot buffer with 16-byte
 //      loads (the host link is the bound; many independent loads per thread are kept
@@ -250,8 +254,12 @@ __global__ __launch_bounds__(kThreads) void swap_in_kernel(
     }
     int vrank = block_exclusive_scan(my_vic, sm.scan, unused);
 
-    // ---- D: the slot's owner installs miss vrank into it; the evicted row's map entry is
-    // cleared ----
+    // ---- D: the slot's owner installs miss vrank into it.  Misses map to -1 before the
+    // wave (a mapping into this request's slots is a hit; other requests' rows are never
+    // selected), so the max over the wave's installs of one row is its highest victim slot.
+    // An entry naming this slot belongs to a row this wave does not select (it would be a
+    // hit and the slot pinned), so no install races with the clear; a slot whose stale copy
+    // is the row it now receives skips the clear. ----
 #pragma unroll
     for (int k = 0; k < kSper; ++k) {
       if (!(flags & (1u << k)) || vrank >= need) continue;
@@ -260,9 +268,9 @@ __global__ __launch_bounds__(kThreads) void swap_in_kernel(
       const int row = sm.miss_row[i];
       const int64_t g = slot_base + vs;
       const int old = held[k];
-      if (old >= 0 && old < host_rows) loc_to_hot[old] = -1;
+      if (old >= 0 && old < host_rows && old != row) atomicCAS(&loc_to_hot[old], (int32_t)g, -1);
       slot_loc[g] = row;
-      loc_to_hot[row] = (int32_t)g;
+      atomicMax(&loc_to_hot[row], (int32_t)g);
       sm.victim[i] = vs;
       sm.slot_of_entry[sm.miss_entry[i]] = vs;
     }

@@ -11,9 +11,13 @@ resident batch reads the paged device cache directly, otherwise KV is swapped in
                    wave r+1 overlaps the attention of wave r.  hs_finalize_accepted
                    closes the step when draft rows are verified.
 
-The copy stream waits for the attention of wave r-2 before swapping wave r (victims of
-wave r are never slots wave r-1 used when capacity >= 2*topk); with a smaller hot
-buffer it waits for wave r-1.  Both streams run at the default priority.
+The copy stream waits for the attention of wave r-2 before swapping wave r.  That is safe
+when capacity >= 2*topk and tick0 is above every stamp already in the state: wave r-1's
+slots then carry the newest stamp, and at least #misses unpinned slots are older, so none
+of them is a victim of wave r.  The state's host-side record (HotState.max_stamp, set by
+build_hot_state and advanced by every wrapper call) decides it; with a smaller hot buffer,
+a tick0 not above that record, or no record, the copy stream waits for wave r-1 instead.
+Both streams run at the default priority.
 
 Mixed batch (P3 reclaim_resident_blocks, build_offload_command): ResidencyTracker keeps
 the resident block table and tells which requests are still fully resident; run_mixed lets
@@ -53,6 +57,7 @@ def build_hot_state(init_pos: torch.Tensor, init_stamp: torch.Tensor, seq_len: t
                     block_table, block_size, block_size, slot_loc)
     stamps = torch.where(slot_loc >= 0, init_stamp.to(device=device, dtype=torch.int32),
                          torch.full_like(slot_loc, -1)).contiguous()
+    max_stamp = int(stamps.max().item()) if stamps.numel() else -1
     host_rows = host_pool.shape[0]
     loc_to_hot = torch.full((host_rows,), -1, dtype=torch.int32, device=device)
     flat = slot_loc.view(-1)
@@ -63,7 +68,7 @@ def build_hot_state(init_pos: torch.Tensor, init_stamp: torch.Tensor, seq_len: t
     rows_cpu = flat[occ].long().cpu()
     if rows_cpu.numel():
         hot_kv[occ] = host_pool.index_select(0, rows_cpu).to(device)
-    return HotState(slot_loc, stamps, loc_to_hot, hot_kv, host_pool)
+    return HotState(slot_loc, stamps, loc_to_hot, hot_kv, host_pool, max_stamp=max_stamp)
 
 
 @dataclass
@@ -135,12 +140,26 @@ class DecodeStep:
                                     b.workspace)
 
     # -- swap batch (waves) -------------------------------------------------------------
+    def overlaps(self, state: HotState, tick0: int) -> bool:
+        """Whether wave r+1's swap may run during wave r's attention (see the module doc)."""
+        return (self.capacity >= 2 * self.K and state.max_stamp is not None
+                and tick0 > state.max_stamp)
+
     def run_swap(self, state: HotState, topk_pos, req_id, causal_limit, block_table, block_size,
-                 q, scale, tick0: int, finalize: Optional[dict] = None):
+                 q, scale, tick0: int, finalize: Optional[dict] = None,
+                 timing: Optional[dict] = None):
+        """One swap-path step.  ``timing`` (optional): lists "swap" and "attn" of R
+        (start, end) timing events each and a "finalize" pair, recorded around each call on
+        the stream it runs on (so their elapsed times are those calls' device durations)."""
         b, B, R = self.buf, self.B, self.R
+
+        def mark(kind, r, i, stream):
+            if timing is not None:
+                ev = timing[kind][r] if r is not None else timing[kind]
+                ev[i].record(stream)
         main = torch.cuda.current_stream()
         copy = self.copy_stream
-        serialize = self.capacity < 2 * self.K
+        serialize = not self.overlaps(state, tick0)
         hs_resolve_topk(topk_pos, req_id, causal_limit, block_table, block_size, block_size,
                         b.slots, b.valid)
         self.e_resolve.record(main)
@@ -151,18 +170,24 @@ class DecodeStep:
                 copy.wait_event(self.e_attn[r - 1])
             elif r >= 2:
                 copy.wait_event(self.e_attn[r - 2])
+            mark("swap", r, 0, copy)
             hs_swap_in(state, b.slots[lo:hi], tick0 + r, b.hot_idx[lo:hi], b.miss_count[r],
                        None if b.miss_pos is None else b.miss_pos[lo:hi], stream=copy)
+            mark("swap", r, 1, copy)
             self.e_swap[r].record(copy)
             main.wait_event(self.e_swap[r])
+            mark("attn", r, 0, main)
             hs_sparse_decode_attn(q[lo:hi], state.hot_kv, b.hot_idx[lo:hi], scale, self.d_v,
                                   b.out[lo:hi], b.lse[lo:hi], b.workspace, stream=main)
+            mark("attn", r, 1, main)
             self.e_attn[r].record(main)
         if finalize is not None:
+            mark("finalize", None, 0, main)
             hs_finalize_accepted(state, finalize["logits"], finalize["draft_ids"],
                                  finalize["new_kv"], R, finalize["seq_len"], block_table,
                                  block_size, tick0 + R, b.argmax, b.accept_len, b.next_token,
                                  stream=main)
+            mark("finalize", None, 1, main)
             d = finalize.get("dflash")
             if d is not None:  # P2 ⑤: the draft model's context KV takes the accepted prefix
                 hs_append_accepted(d["ctx_cache"], d["ctx_block_table"], d["ctx_len"],
@@ -183,7 +208,7 @@ class DecodeStep:
             raise ValueError("run_mixed needs a DecodeStep built with capacity > 0 and mixed=True")
         main = torch.cuda.current_stream()
         copy = self.copy_stream
-        serialize = self.capacity < 2 * self.K
+        serialize = not self.overlaps(state, tick0)
         hs_resolve_topk(topk_pos, req_id_swap, causal_limit, host_block_table, block_size,
                         block_size, b.slots, b.valid)
         self.e_resolve.record(main)

@@ -31,12 +31,17 @@ def test_algorithmic_bytes_of_the_resident_step():
 
 
 def test_cpu_baseline_record():
+    """The oracle leg on a small mixed + finalize workload: every stage of the step is timed
+    and the record carries the fields the benchmark line needs."""
     import bench
     from workloads import generate, spec
-    s = spec("tiny")
+    s = spec("mixed_finalize", num_reqs=6, vocab=64, topk=128, capacity=512,
+             seq_rule=("uniform", 300, 900))
     w = generate(s)
-    r = bench.cpu_baseline(w, s, budget_s=0.2, one_thread_s=0.1)
+    pool_before = w.kv_pool.clone()
+    r = bench.cpu_baseline(s, w, sample_reqs=4, reps=2)
     assert r["kind"] == "oracle" and r["unit"] == "rows/s"
-    assert r["value"] > 0 and r["cores"] >= 1 and r["sample"]
-    assert set(r["stage_ms"]) == {"resolve", "attention"}
+    assert r["value"] > 0 and r["cores"] >= 1 and "first 4 of 6 requests (12 rows" in r["sample"]
+    assert set(r["stage_ms"]) == {"resolve", "swap_in", "attention", "accept", "finalize"}
     assert r["one_thread"]["value"] > 0
+    assert __import__("torch").equal(w.kv_pool, pool_before)   # finalize's host rows put back

@@ -209,6 +209,82 @@ def test_finalize_capacity_beyond_register_keys():
                             new_kv, tick=60)
     assert acc.tolist() == [3, 1, 2]
 
+def test_finalize_tick_below_stamps_keeps_kept_hits_pinned():
+    """Full buffers whose stamps are all above the finalize tick: a kept row that hits is
+    restamped to the tick, the lowest stamp in its request, and must stay pinned while the
+    request's kept misses pick their victims (the LRU rule would otherwise evict it)."""
+    rng = np.random.default_rng(515)
+    B, R, cap, bs, width = 12, 4, 16, 8, 12
+    bt = rng.permutation(B * width).astype(np.int32).reshape(B, width)
+    seq = rng.integers(cap + R + 1, width * bs, size=B).astype(np.int32)
+    pool = rng.standard_normal((B * width * bs, 8)).astype(np.float32)
+    init_pos = np.full((B, cap), -1, np.int32)
+    init_stamp = np.full((B, cap), -1, np.int32)
+    for b in range(B):
+        verify = seq[b] - R + np.arange(R)
+        hit = verify[rng.random(R) < 0.5]                 # some verify rows already resident
+        others = rng.choice(int(seq[b]) - R, cap - len(hit), replace=False)
+        init_pos[b] = rng.permutation(np.concatenate([hit, others]))
+        init_stamp[b] = rng.integers(10, 40, size=cap)
+    vocab = 300
+    gen = torch.Generator().manual_seed(515)
+    logits = torch.randn(B * R, vocab, generator=gen).to(torch.bfloat16)
+    plant = rng.integers(0, vocab, size=B * R)
+    logits[torch.arange(B * R), torch.from_numpy(plant)] = 9.0
+    draft = rng.integers(0, vocab, size=B * R).astype(np.int32)
+    for r in range(1, R):
+        for b in range(B):
+            if rng.random() < 0.8:
+                draft[r * B + b] = plant[(r - 1) * B + b]
+    new_kv = rng.standard_normal((B * R, 8)).astype(np.float32)
+    acc, _, _, ost, _ = _run_finalize(B, R, cap, seq, bt, bs, pool, init_pos, init_stamp, logits,
+                                      draft, new_kv, tick=5)
+    # the case is reached: some request keeps a resident row and installs a missing one
+    reached = 0
+    for b in range(B):
+        kept = seq[b] - R + np.arange(acc[b] + 1)
+        was = np.isin(kept, init_pos[b])
+        reached += bool(was.any() and (~was).any())
+    log(f"finalize low tick: {reached} requests keep a hit and install a miss")
+    assert reached > 0
+
+
+def test_finalize_eviction_of_a_stale_copy():
+    """Slot 1 holds a stale copy of host row 9 (the map names slot 0); the kept verify row
+    misses and evicts slot 1, the least recent: row 9 stays mapped to slot 0 (worked by hand
+    in the oracle's pins; here the kernel must give the same state)."""
+    import sparse_attention_kv_amd as hs
+    bs, cap, R = 4, 4, 1
+    seq = np.array([8], np.int32)
+    bt = np.array([[1, 0]], np.int32)
+    pool = np.arange(16 * 8, dtype=np.float32).reshape(16, 8)
+    slot_loc = np.array([[9, 9, 10, 11]], np.int32)
+    stamps = np.array([[1, 0, 5, 6]], np.int32)
+    l2h = np.full(16, -1, np.int32)
+    l2h[[9, 10, 11]] = [0, 2, 3]
+    ost = oracle.HotState(cap, slot_loc.copy(), stamps.copy(), l2h.copy(), pool[[9, 9, 10, 11]].copy())
+    opool = pool.copy()
+    new_kv = -np.arange(8, dtype=np.float32)[None] - 1
+    logits = torch.zeros((1, 16), dtype=torch.bfloat16)
+    oracle.finalize_accepted(ost, opool, new_kv, np.array([0]), seq, bt, bs, R, 20)
+    hpool = _pinned(pool)
+    gst = hs.HotState(to_dev(slot_loc), to_dev(stamps), to_dev(l2h),
+                      torch.from_numpy(pool[[9, 9, 10, 11]].copy()).to(dev()), hpool)
+    am = torch.empty((1,), dtype=torch.int32, device=dev())
+    acc = torch.empty((1,), dtype=torch.int32, device=dev())
+    nxt = torch.empty((1,), dtype=torch.int32, device=dev())
+    hs.hs_finalize_accepted(gst, logits.to(dev()), to_dev(np.zeros(1, np.int32)),
+                            torch.from_numpy(new_kv).to(dev()), R, to_dev(seq), to_dev(bt), bs, 20,
+                            am, acc, nxt)
+    torch.cuda.synchronize()
+    assert ost.slot_loc.tolist() == [[9, 3, 10, 11]] and ost.loc_to_hot[9] == 0
+    assert np.array_equal(gst.slot_loc.cpu().numpy(), ost.slot_loc)
+    assert np.array_equal(gst.slot_stamp.cpu().numpy(), ost.slot_stamp)
+    assert np.array_equal(gst.loc_to_hot.cpu().numpy(), ost.loc_to_hot)
+    assert np.array_equal(gst.hot_kv.cpu().numpy(), ost.hot_kv)
+    assert np.array_equal(hpool.numpy(), opool)
+
+
 def test_attention_identical_on_resident_and_swap_paths():
     """Same rows, same index order: the paged pool and the hot buffer give equal bits."""
     import sparse_attention_kv_amd as hs

@@ -73,7 +73,10 @@ def _swap_waves(name, **over):
         assert np.array_equal(hot.cpu().numpy(), oh), f"{name} wave {r} hot_idx"
         assert np.array_equal(mc.cpu().numpy(), omc), f"{name} wave {r} miss_count"
         assert np.array_equal(mp.cpu().numpy(), omp), f"{name} wave {r} miss_pos"
-        _compare_state(ost, gst, f"{name} wave {r}", with_kv=(r == s.rows_per_req - 1 or name == "tiny"))
+        # hot-buffer bytes after every wave on tiny and the MTP workload, after the last
+        # wave on the larger ones
+        _compare_state(ost, gst, f"{name} wave {r}",
+                       with_kv=(r == s.rows_per_req - 1 or name in ("tiny", "mtp_swap")))
         log(f"swap {name} wave {r}: misses/row {omc.mean():.1f} hit rate "
             f"{1 - omc.sum() / max(1, (wave >= 0).sum()):.3f}")
     check_state_invariants(ost, pool)
@@ -166,11 +169,12 @@ def _pipeline_case(name, sample_rows_per_wave=6):
         assert np.array_equal(step.buf.miss_count[r].cpu().numpy(), omc)
         assert np.array_equal(step.buf.miss_pos[r * B:(r + 1) * B].cpu().numpy(), omp)
     assert np.array_equal(step.buf.hot_idx.cpu().numpy(), hot_all)
-    # attention on sampled rows of every wave, against the oracle over the host pool
+    # attention against the oracle over the host pool: every row of the first wave (it runs
+    # while the second wave's swap is in flight), sampled rows of the others
     rng = np.random.default_rng(0)
     q_raw = raw(w.q)
-    sample = np.concatenate([r * B + rng.choice(B, min(B, sample_rows_per_wave), replace=False)
-                             for r in range(R)])
+    sample = np.concatenate([np.arange(B)] + [r * B + rng.choice(B, min(B, sample_rows_per_wave), replace=False)
+                                              for r in range(1, R)])
     ref, rlse = oracle.sparse_decode_attn(q_raw[sample], pool, slots[sample], s.scale, s.d_v)
     tol = F32_TOL if s.dtype == "f32" else BF16_TOL
     assert_close(out_f64(step.buf.out[torch.from_numpy(sample).to(dev())]), ref, tol, f"{name} attention")
@@ -195,7 +199,7 @@ def _pipeline_case(name, sample_rows_per_wave=6):
     check_state_invariants(ost, pool)
 
 
-@pytest.mark.parametrize("name", ["tiny", "mtp_swap"])
+@pytest.mark.parametrize("name", ["tiny", "mtp_swap", "long"])
 def test_pipeline_step(name):
     _pipeline_case(name)
 
@@ -204,32 +208,16 @@ def test_pipeline_step_with_finalize_full():
     _pipeline_case("mixed_finalize", sample_rows_per_wave=4)
 
 
-def _racy_rows(before, wave, hot_idx, mc, mp):
-    """Map entries that two writers set in one wave, with the values they write: every miss
-    installs its row (the slot it took), every eviction clears the row its victim held (-1)."""
-    held = before.slot_loc.reshape(-1)
-    writes = {}
-    for b in range(wave.shape[0]):
-        for m in range(mc[b]):
-            j = mp[b, m]
-            g = int(hot_idx[b, j])
-            writes.setdefault(int(wave[b, j]), []).append(g)
-            if held[g] >= 0:
-                writes.setdefault(int(held[g]), []).append(-1)
-    return {r: set(v) for r, v in writes.items() if len(v) >= 2}
-
-
 @pytest.mark.parametrize("name,over", [
     ("tiny", {}),
     ("mtp_swap", {"num_reqs": 3, "seq_rule": ("const", 6000), "capacity": 1024, "topk": 256}),
 ], ids=["tiny", "mtp_small"])
 def test_swap_duplicate_rows_in_a_request(name, over):
-    """Rows repeated within a request (top-k sets never do this; the call still defines it).
-    Hot indices, miss lists, slot_loc, stamps and the hot rows match the oracle bit for bit.
-    A map entry that two writers set in the same wave (two copies of a miss, or a miss and the
-    eviction of a slot that held the same row) has no defined order: the device must hold one
-    of the written values, and the oracle then takes the device's map so that the next wave
-    starts from the same state."""
+    """Rows repeated within a request (top-k sets never do this; the call still defines it):
+    each copy of a miss takes its own victim, an eviction clears a map entry only while it
+    names the evicted slot, and the map names a repeated row's last install.  Hot indices,
+    miss lists, slot_loc, stamps, loc_to_hot and the hot rows match the oracle bit for bit
+    after every call, with no state carried over from the device."""
     import sparse_attention_kv_amd as hs
     from tests.helpers import check_state_weak, with_duplicates
     s, w = make(name, **over)
@@ -237,9 +225,9 @@ def test_swap_duplicate_rows_in_a_request(name, over):
     ost, gst, pool = _both_states(s, w, g)
     slots, _ = oracle_resolve(s, w)
     B, K = s.num_reqs, s.topk
-    racy_total = install_vs_evict = 0
+    stale_evictions = 0
     # wave 0 comes back after every other wave: rows then sit in slots the map no longer
-    # names, and evicting such a slot can race with installing its row again
+    # names, and evicting such a slot must leave the row's live mapping alone
     sched = [r for k in range(s.rows_per_req) for r in (k, 0)]
     for t, r in enumerate(sched):
         wave = with_duplicates(slots[r * B:(r + 1) * B])
@@ -254,21 +242,73 @@ def test_swap_duplicate_rows_in_a_request(name, over):
         assert np.array_equal(hot.cpu().numpy(), oh), f"{name} call {t} hot_idx"
         assert np.array_equal(mc.cpu().numpy(), omc), f"{name} call {t} miss_count"
         assert np.array_equal(mp.cpu().numpy(), omp), f"{name} call {t} miss_pos"
-        assert np.array_equal(gst.slot_loc.cpu().numpy(), ost.slot_loc), f"{name} call {t} slot_loc"
-        assert np.array_equal(gst.slot_stamp.cpu().numpy(), ost.slot_stamp), f"{name} call {t} stamps"
-        racy = _racy_rows(before, wave, oh, omc, omp)
-        racy_total += len(racy)
-        install_vs_evict += sum(1 for v in racy.values() if -1 in v and len(v) > 1)
-        gl = gst.loc_to_hot.cpu().numpy()
-        for row in np.nonzero(gl != ost.loc_to_hot)[0]:
-            assert int(row) in racy, f"{name} call {t} loc_to_hot[{row}] differs outside a race"
-            assert int(gl[row]) in racy[int(row)], f"{name} call {t} loc_to_hot[{row}] = {gl[row]}"
-        ost.loc_to_hot[:] = gl
-        occ = np.nonzero(ost.slot_loc.reshape(-1) >= 0)[0]
-        assert np.array_equal(raw(gst.hot_kv.cpu())[occ], ost.hot_kv[occ]), f"{name} call {t} hot_kv"
+        _compare_state(ost, gst, f"{name} call {t}")
         check_state_weak(ost, pool)
-    log(f"swap duplicates {name}: {racy_total} map entries with two writers, "
-        f"{install_vs_evict} of them an install against an eviction")
-    assert racy_total > 0
+        # evicted slots whose old row the map named elsewhere (stale copies)
+        held = before.slot_loc.reshape(-1)
+        for b in range(B):
+            for m in range(omc[b]):
+                gslot = int(oh[b, omp[b, m]])
+                old = int(held[gslot])
+                if old >= 0 and before.loc_to_hot[old] != gslot:
+                    stale_evictions += 1
+    log(f"swap duplicates {name}: {stale_evictions} evictions of stale copies")
     if name == "tiny":
-        assert install_vs_evict > 0
+        assert stale_evictions > 0
+
+
+def _next_step_positions(w, s, rng, keep_frac=0.5):
+    """Top-k positions of a following step: per row, a random half of this step's set plus
+    fresh distinct positions below the same causal limit (top-k sets stay distinct)."""
+    out = np.full_like(w.topk_pos, -1)
+    K = s.topk
+    for i in range(out.shape[0]):
+        c = int(w.causal_limit[i])
+        prev = w.topk_pos[i][w.topk_pos[i] >= 0]
+        keep = rng.choice(prev, min(len(prev), int(K * keep_frac)), replace=False)
+        rest = np.setdiff1d(np.arange(c), keep)
+        fresh = rng.choice(rest, min(K - len(keep), len(rest)), replace=False)
+        row = rng.permutation(np.concatenate([keep, fresh]))
+        out[i, :len(row)] = row
+    return out.astype(np.int32)
+
+
+@pytest.mark.parametrize("second_tick", ["after", "stale"])
+def test_pipeline_two_consecutive_steps(second_tick):
+    """Two decode steps on one hot state.  With the second step's first tick above every
+    stamp of the first ("after": tick0 + R + 1) the pipeline overlaps each wave's swap with
+    the previous wave's attention; with a tick reused ("stale": tick0 again) it must fall
+    back to waiting for the previous wave, since victims may then be that wave's slots.
+    Both steps are compared with the oracle: hot indices, miss lists, state, hot-buffer
+    bytes, and attention on every row."""
+    from sparse_attention_kv_amd.pipeline import DecodeStep
+    s, w = make("mtp_swap", num_reqs=8)
+    g = gpu_inputs(s, w)
+    ost, gst, pool = _both_states(s, w, g)
+    B, R = s.num_reqs, s.rows_per_req
+    step = DecodeStep(num_reqs=B, rows_per_req=R, topk=s.topk, num_heads=s.num_heads, d_qk=s.d_qk,
+                      d_v=s.d_v, dtype=w.q.dtype, capacity=s.capacity, want_miss_pos=True,
+                      device=dev())
+    rng = np.random.default_rng(31)
+    pos2 = _next_step_positions(w, s, rng)
+    tick2 = s.tick0 + R + 1 if second_tick == "after" else s.tick0
+    for t, (pos, tick) in enumerate(((w.topk_pos, s.tick0), (pos2, tick2))):
+        expect_overlap = t == 0 or second_tick == "after"
+        assert step.overlaps(gst, tick) == expect_overlap
+        log(f"two steps ({second_tick}): step {t} tick {tick} overlap {expect_overlap}")
+        step.run_swap(gst, to_dev(pos), g["req_id"], g["causal_limit"], g["block_table"],
+                      s.block_size, g["q"], s.scale, tick)
+        torch.cuda.synchronize()
+        assert gst.max_stamp == tick + R - 1
+        slots, _ = oracle.resolve_topk(pos, w.req_id, w.causal_limit, w.block_table, s.block_size,
+                                       s.block_size, B)
+        assert np.array_equal(step.buf.slots.cpu().numpy(), slots)
+        for r in range(R):
+            oh, omc, omp = oracle.swap_in(ost, slots[r * B:(r + 1) * B], tick + r, pool)
+            assert np.array_equal(step.buf.hot_idx[r * B:(r + 1) * B].cpu().numpy(), oh), (t, r)
+            assert np.array_equal(step.buf.miss_count[r].cpu().numpy(), omc), (t, r)
+            assert np.array_equal(step.buf.miss_pos[r * B:(r + 1) * B].cpu().numpy(), omp), (t, r)
+        _compare_state(ost, gst, f"two steps ({second_tick}) after step {t}")
+        ref, _ = oracle.sparse_decode_attn(raw(w.q), pool, slots, s.scale, s.d_v)
+        assert_close(out_f64(step.buf.out), ref, BF16_TOL, f"two steps ({second_tick}) step {t}")
+        check_state_invariants(ost, pool)

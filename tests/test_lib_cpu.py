@@ -205,3 +205,62 @@ def test_attn_plan_info():
     assert lib.hs_attn_plan_info(0, 128, 576, 512, 2048, hs.HS_BF16, ctypes.byref(h), ctypes.byref(s)) == hs.HS_ERR_INVALID_ARG
     assert lib.hs_attn_plan_info(8, 100, 576, 512, 2048, hs.HS_BF16, None, None) == hs.HS_ERR_UNSUPPORTED
     assert lib.hs_attn_plan_info(8, 128, 576, 512, 2048, 9, None, None) == hs.HS_ERR_INVALID_ARG
+
+
+def test_binding_rejects_mis_sized_tensors_before_any_call():
+    """The Python binding checks that argument shapes agree before it checks devices or calls
+    the library, so a mis-sized buffer never reaches a kernel (no GPU needed: the tensors
+    here are CPU tensors; correctly sized ones fail the device check instead)."""
+    import torch
+    hs, _ = _lib()
+    i32 = dict(dtype=torch.int32)
+    z = lambda *sh, **kw: torch.zeros(sh, **(kw or i32))  # noqa: E731
+
+    def shape_error(fn, *a):
+        with pytest.raises(ValueError, match="shape mismatch"):
+            fn(*a)
+
+    def device_error(fn, *a):
+        with pytest.raises(ValueError, match="device tensor"):
+            fn(*a)
+
+    # resolve: per-row vectors and the output must match the position array
+    device_error(hs.hs_resolve_topk, z(4, 16), z(4), z(4), z(2, 8), 16, 16, z(4, 16), z(4))
+    shape_error(hs.hs_resolve_topk, z(4, 16), z(3), z(4), z(2, 8), 16, 16, z(4, 16))
+    shape_error(hs.hs_resolve_topk, z(4, 16), z(4), z(4), z(2, 8), 16, 16, z(4, 15))
+    shape_error(hs.hs_resolve_topk, z(4, 16), z(4), z(4), z(2, 8), 16, 16, z(4, 16), z(5))
+    # hot state: stamps, reverse map and hot buffer sized from slot_loc and the host pool
+    f32 = dict(dtype=torch.float32)
+
+    def state(**kw):
+        d = dict(slot_loc=z(2, 24), slot_stamp=z(2, 24), loc_to_hot=z(256),
+                 hot_kv=z(48, 64, **f32), host_pool=z(256, 64, **f32))
+        d.update(kw)
+        return hs.HotState(**d)
+    device_error(hs.hs_swap_in, state(), z(2, 16), 5, z(2, 16), z(2))
+    shape_error(hs.hs_swap_in, state(slot_stamp=z(2, 23)), z(2, 16), 5, z(2, 16), z(2))
+    shape_error(hs.hs_swap_in, state(loc_to_hot=z(255)), z(2, 16), 5, z(2, 16), z(2))
+    shape_error(hs.hs_swap_in, state(hot_kv=z(47, 64, **f32)), z(2, 16), 5, z(2, 16), z(2))
+    shape_error(hs.hs_swap_in, state(), z(3, 16), 5, z(3, 16), z(3))
+    shape_error(hs.hs_swap_in, state(), z(2, 16), 5, z(2, 17), z(2))
+    shape_error(hs.hs_swap_in, state(), z(2, 16), 5, z(2, 16), z(3))
+    shape_error(hs.hs_swap_in, state(), z(2, 16), 5, z(2, 16), z(2), z(2, 15))
+    # attention: kv width, index rows, output and lse shapes
+    q = z(3, 4, 64, **f32)
+    device_error(hs.hs_sparse_decode_attn, q, z(10, 64, **f32), z(3, 8), 0.1, 48, z(3, 4, 48, **f32), z(3, 4, **f32))
+    shape_error(hs.hs_sparse_decode_attn, q, z(10, 32, **f32), z(3, 8), 0.1, 48, z(3, 4, 48, **f32))
+    shape_error(hs.hs_sparse_decode_attn, q, z(10, 64, **f32), z(2, 8), 0.1, 48, z(3, 4, 48, **f32))
+    shape_error(hs.hs_sparse_decode_attn, q, z(10, 64, **f32), z(3, 8), 0.1, 48, z(3, 4, 47, **f32))
+    shape_error(hs.hs_sparse_decode_attn, q, z(10, 64, **f32), z(3, 8), 0.1, 48, z(3, 4, 48, **f32), z(3, 5, **f32))
+    shape_error(hs.hs_sparse_decode_attn_paged, q, z(10, 64, **f32), z(3, 8), z(2), z(3), z(2, 4), 16, 16,
+                0.1, 48, z(3, 4, 48, **f32))
+    shape_error(hs.hs_sparse_decode_attn_mixed, q, z(10, 64, **f32), z(3, 8), z(10, 63, **f32), z(3, 8), z(3),
+                0.1, 48, z(3, 4, 48, **f32))
+    # finalize: logits, drafts and new rows are num_reqs * rows_per_req long
+    fin = lambda st, logits, draft, new_kv, seq: hs.hs_finalize_accepted(  # noqa: E731
+        st, logits, draft, new_kv, 3, seq, z(2, 8), 16, 9, z(6), z(2), z(2))
+    device_error(fin, state(), z(6, 100, dtype=torch.bfloat16), z(6), z(6, 64, **f32), z(2))
+    shape_error(fin, state(), z(5, 100, dtype=torch.bfloat16), z(6), z(6, 64, **f32), z(2))
+    shape_error(fin, state(), z(6, 100, dtype=torch.bfloat16), z(7), z(6, 64, **f32), z(2))
+    shape_error(fin, state(), z(6, 100, dtype=torch.bfloat16), z(6), z(6, 32, **f32), z(2))
+    shape_error(fin, state(), z(6, 100, dtype=torch.bfloat16), z(6), z(6, 64, **f32), z(3))
