@@ -61,7 +61,8 @@ typedef enum {
   HS_ERR_INVALID_ARG = -1,  /* null pointer, bad size, misaligned buffer, bad dtype      */
   HS_ERR_CAPACITY = -2,     /* topk exceeds the hot-buffer capacity; nothing was changed */
   HS_ERR_UNSUPPORTED = -3,  /* shape/dtype combination the kernels are not built for    */
-  HS_ERR_HIP = -4           /* a HIP runtime call or kernel launch failed                */
+  HS_ERR_HIP = -4,          /* a HIP runtime call or kernel launch failed                */
+  HS_ERR_SCRATCH = -5       /* the shape needs more workspace than the fixed scratch     */
 } hs_status;
 
 typedef enum { HS_BF16 = 0, HS_F32 = 1 } hs_dtype;
@@ -267,6 +268,27 @@ hs_status hs_sparse_decode_attn_paged(const void *q, const void *kv_pool, int64_
 hs_status hs_attn_plan_info(int32_t num_rows, int32_t num_heads, int32_t d_qk, int32_t d_v,
                             int32_t topk, int32_t dtype, int32_t *heads_per_wg,
                             int32_t *splits);
+
+/*
+ * hs_sparse_decode_attn_noalloc -- hs_sparse_decode_attn for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): the same computation and arguments without workspace, workspace_bytes.  The
+ * key-split partials go to a scratch array the library keeps in device memory, one per GPU
+ * for the life of the process (HS_NOALLOC_SCRATCH_BYTES = 32 MiB; enough for every shape
+ * with topk <= 2048).  The call allocates nothing.  All calls on one GPU share that GPU's
+ * scratch: calls that may overlap on one GPU (different streams without ordering) race and
+ * must be ordered by the caller.  Its contents persist between calls and need no clearing
+ * (every partial is written before it is read).
+ * Errors: as hs_sparse_decode_attn; HS_ERR_SCRATCH when hs_attn_workspace_bytes(...) for
+ * these sizes exceeds HS_NOALLOC_SCRATCH_BYTES (nothing is launched); HS_ERR_HIP if the
+ * scratch array's device address cannot be obtained.
+ */
+#define HS_NOALLOC_SCRATCH_BYTES (32u << 20)
+hs_status hs_sparse_decode_attn_noalloc(const void *q, const void *kv, int64_t kv_rows,
+                                        const int32_t *indices, int32_t num_rows,
+                                        int32_t num_heads, int32_t d_qk, int32_t d_v, int32_t topk,
+                                        float scale, int32_t dtype, void *out, float *lse,
+                                        void *stream);
 
 /* Device workspace hs_sparse_decode_attn(_paged) needs for these sizes (0 when none). */
 size_t hs_attn_workspace_bytes(int32_t num_rows, int32_t num_heads, int32_t d_qk, int32_t d_v,

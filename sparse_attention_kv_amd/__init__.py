@@ -19,12 +19,14 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libhisparse.so")
 
 HS_OK, HS_ERR_INVALID_ARG, HS_ERR_CAPACITY, HS_ERR_UNSUPPORTED, HS_ERR_HIP = 0, -1, -2, -3, -4
+HS_ERR_SCRATCH = -5
+NOALLOC_SCRATCH_BYTES = 32 << 20
 HS_BF16, HS_F32 = 0, 1
 
 EXPORTED = ("hs_resolve_topk", "hs_swap_in", "hs_sparse_decode_attn", "hs_sparse_decode_attn_paged",
             "hs_sparse_decode_attn_mixed",
             "hs_attn_workspace_bytes", "hs_attn_plan_info", "hs_finalize_accepted", "hs_backup_rows", "hs_apply_plan",
-            "hs_append_accepted", "hs_host_read",
+            "hs_append_accepted", "hs_host_read", "hs_sparse_decode_attn_noalloc",
             "hs_status_string", "hs_version")
 
 
@@ -75,6 +77,9 @@ def _load() -> ctypes.CDLL:
     lib.hs_apply_plan.restype = i32
     lib.hs_append_accepted.argtypes = [vp, i64, i32, vp, i32, i32, i32, vp, vp, vp, i32, i32, vp]
     lib.hs_append_accepted.restype = i32
+    lib.hs_sparse_decode_attn_noalloc.argtypes = [vp, vp, i64, vp, i32, i32, i32, i32, i32, f32,
+                                                  i32, vp, vp, vp]
+    lib.hs_sparse_decode_attn_noalloc.restype = i32
     lib.hs_host_read.argtypes = [vp, vp, i64, vp]
     lib.hs_host_read.restype = i32
     lib.hs_status_string.argtypes = [i32]
@@ -261,6 +266,23 @@ def hs_sparse_decode_attn(q: torch.Tensor, kv: torch.Tensor, indices: torch.Tens
         _ptr(q), _ptr(kv), kv.shape[0], _ptr(indices), rows, heads, d_qk, d_v, indices.shape[1],
         float(scale), _dtype_code(q.dtype), _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes,
         _stream(stream)))
+
+
+def hs_sparse_decode_attn_noalloc(q: torch.Tensor, kv: torch.Tensor, indices: torch.Tensor,
+                                  scale: float, d_v: int, out: torch.Tensor,
+                                  lse: Optional[torch.Tensor] = None, stream=None):
+    """hs_sparse_decode_attn with the key-split workspace in the library's fixed per-GPU
+    scratch: for callers that cannot allocate (see include/hisparse.h)."""
+    _attn_shapes(q, kv, indices, d_v, out, lse)
+    _dev(q, "q"); _dev(kv, "kv"); _dev(indices, "indices", torch.int32); _dev(out, "out", q.dtype)
+    if kv.dtype != q.dtype:
+        raise ValueError("q and kv dtypes differ")
+    if lse is not None:
+        _dev(lse, "lse", torch.float32)
+    rows, heads, d_qk = q.shape
+    _check("hs_sparse_decode_attn_noalloc", _lib.hs_sparse_decode_attn_noalloc(
+        _ptr(q), _ptr(kv), kv.shape[0], _ptr(indices), rows, heads, d_qk, d_v, indices.shape[1],
+        float(scale), _dtype_code(q.dtype), _ptr(out), _ptr(lse), _stream(stream)))
 
 
 def _attn_shapes(q, kv, indices, d_v, out, lse):

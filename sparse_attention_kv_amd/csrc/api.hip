@@ -185,6 +185,20 @@ hs_status hs_sparse_decode_attn(const void *q, const void *kv, int64_t kv_rows,
                                 int32_t d_qk, int32_t d_v, int32_t topk, float scale,
                                 int32_t dtype, void *out, float *lse, void *workspace,
                                 size_t workspace_bytes, void *stream) {
+  return hs::sparse_decode_attn_checked(q, kv, kv_rows, indices, num_rows, num_heads, d_qk, d_v,
+                                        topk, scale, dtype, out, lse, workspace, workspace_bytes,
+                                        stream);
+}
+
+}  // extern "C"
+
+// Validation and launch of hs_sparse_decode_attn, shared with the entry point whose
+// workspace is the library's own scratch array.
+hs_status hs::sparse_decode_attn_checked(const void *q, const void *kv, int64_t kv_rows,
+                                         const int32_t *indices, int32_t num_rows,
+                                         int32_t num_heads, int32_t d_qk, int32_t d_v, int32_t topk,
+                                         float scale, int32_t dtype, void *out, float *lse,
+                                         void *workspace, size_t workspace_bytes, void *stream) {
   if (num_rows < 0 || num_heads <= 0 || d_qk <= 0 || d_v <= 0 || topk <= 0 || kv_rows < 0)
     return HS_ERR_INVALID_ARG;
   if (dtype != HS_BF16 && dtype != HS_F32) return HS_ERR_INVALID_ARG;
@@ -208,6 +222,8 @@ hs_status hs_sparse_decode_attn(const void *q, const void *kv, int64_t kv_rows,
                                       kv_rows, indices, num_rows, num_heads, d_qk, d_v, topk, scale,
                                       static_cast<float *>(out), lse, st));
 }
+
+extern "C" {
 
 hs_status hs_sparse_decode_attn_paged(const void *q, const void *kv_pool, int64_t kv_rows,
                                       const int32_t *topk_pos, const int32_t *req_id,
@@ -316,6 +332,7 @@ const char *hs_status_string(int32_t status) {
     case HS_ERR_CAPACITY: return "top-k exceeds hot-buffer capacity";
     case HS_ERR_UNSUPPORTED: return "unsupported shape or dtype";
     case HS_ERR_HIP: return "HIP runtime error";
+    case HS_ERR_SCRATCH: return "shape needs more workspace than the library's fixed scratch";
     default: return "unknown status";
   }
 }
