@@ -28,7 +28,7 @@ objects: `hbm_roofline` (the step's attention dispatches against the 8 TB/s HBM 
 (the 32-request MTP workload), `finalize`, `backup`, `resolve`, and `cpu_baseline` (the CPU
 oracle on a sample of the headline step).
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--headline-only]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--part NAME]
 """
 
 from __future__ import annotations
@@ -904,8 +904,11 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--headline-only", action="store_true",
-                    help="only the headline step (and B_host): for profiler runs")
+    ap.add_argument("--part", default="all",
+                    choices=["all", "headline", "long", "resident", "sweep", "swap", "finalize",
+                             "backup", "resolve"],
+                    help="run one section only (for profiler runs); the JSON line then holds "
+                         "that section's object, and the headline fields only with 'headline'")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
@@ -922,12 +925,17 @@ def main():
     log("host link")
     link = measure_host_link(dev)
     b_host = link["B_host_GBps"]
+    if args.part not in ("all", "headline"):
+        res = {"part": args.part, "host_link": link}
+        run_sections(dev, args, b_host, res, [args.part])
+        print(json.dumps(res))
+        return
 
     log(f"headline: {HEADLINE} step, warmup {args.warmup}, steps {args.steps}")
     rig = StepRig(dev, HEADLINE)
     head = measure_step(rig, args.steps, args.warmup, b_host)
     s = rig.s
-    swap_counters = stored_counters("swap_mixed_counters.txt", "swap")
+    swap_counters = stored_counters("swap_in_mixed_finalize_counters.txt", "swap")
     traffic = None
     if swap_counters:
         try:
@@ -957,6 +965,7 @@ def main():
                      "kernel": "swap_in_kernel (hs_swap_in): zero-copy gather of the missed "
                                "1152-B rows from the pinned host pool",
                      "alg_bytes_per_launch": alg_per_launch,
+                     "alg_bytes_read_and_write_per_launch": 2 * alg_per_launch,
                      "launch_us": head["swap_launch_us_mean"],
                      "measured_B_host_GBps": b_host, "frac_of_B_host": achieved / b_host,
                      "peak_source": "PCIe 5.0 x16, 64 GB/s per direction (MI355X host interface)"},
@@ -975,26 +984,40 @@ def main():
         res["cpu_baseline"] = cpu_baseline(rig.s, rig.w)
     rig.release()
     del rig
-    if not args.headline_only:
-        log("long-context step")
-        lrig = StepRig(dev, "long")
-        res["long_context_step"] = measure_step(lrig, min(args.steps, 10), max(1, min(args.warmup, 2)),
-                                                b_host)
-        lrig.release()
-        del lrig
-        log("resident decode (warm and cold)")
-        res["resident_decode"] = measure_resident(dev, args.steps, args.warmup)
-        log("attention sweep (cold)")
-        res["attn_sweep"] = measure_attn_sweep(dev)
-        log("MTP swap workload")
-        res["swap_in"] = measure_swap(dev, b_host)
-        log("finalize")
-        res["finalize"] = measure_finalize(dev)
-        log("backup")
-        res["backup"] = measure_backup(dev)
-        log("resolve")
-        res["resolve"] = measure_resolve(dev)
+    if args.part == "all":
+        run_sections(dev, args, b_host, res,
+                     ["long", "resident", "sweep", "swap", "finalize", "backup", "resolve"])
     print(json.dumps(res))
+
+
+def run_sections(dev, args, b_host, res, parts):
+    """The secondary measurements, each an object of the JSON line."""
+    for part in parts:
+        if part == "long":
+            log("long-context step")
+            lrig = StepRig(dev, "long")
+            res["long_context_step"] = measure_step(lrig, min(args.steps, 10),
+                                                    max(1, min(args.warmup, 2)), b_host)
+            lrig.release()
+            del lrig
+        elif part == "resident":
+            log("resident decode (warm and cold)")
+            res["resident_decode"] = measure_resident(dev, args.steps, args.warmup)
+        elif part == "sweep":
+            log("attention sweep (cold)")
+            res["attn_sweep"] = measure_attn_sweep(dev)
+        elif part == "swap":
+            log("MTP swap workload")
+            res["swap_in"] = measure_swap(dev, b_host)
+        elif part == "finalize":
+            log("finalize")
+            res["finalize"] = measure_finalize(dev)
+        elif part == "backup":
+            log("backup")
+            res["backup"] = measure_backup(dev)
+        elif part == "resolve":
+            log("resolve")
+            res["resolve"] = measure_resolve(dev)
 
 
 if __name__ == "__main__":
