@@ -39,6 +39,7 @@ from .hisparse_ref import (  # noqa: F401
     plan_backup_rows,
     reclaimable_pages,
     resolve_topk,
+    select_reclaim_pages,
     sparse_decode_attn,
     sparse_decode_attn_mixed,
     swap_in,

@@ -293,6 +293,32 @@ def reclaimable_pages(block_table: np.ndarray, seq_len: np.ndarray, block_size: 
     return out
 
 
+def select_reclaim_pages(block_table: np.ndarray, seq_len: np.ndarray, block_size: int,
+                         deficit: int, priority=None, hot_pages=None):
+    """The resident pages to give back when the cache manager is ``deficit`` blocks short.
+
+    P3 reclaim_resident_blocks: allocation fails for lack of blocks; the coordinator is asked
+    to reclaim that many; the resident manager offers every request's older pages (never
+    the last two); the coordinator screens them by priority, hot pages and budget and
+    releases the chosen ones (the table entry becomes null, the block returns to the pool);
+    allocation then checks its capacity again.
+
+    Reading (the screening is not printed): the candidates are ``reclaimable_pages``; a page
+    marked in ``hot_pages`` ([num_reqs, bt_stride] bool, e.g. pages the latest top-k
+    selections touched) is screened out; the rest are taken in the order (request priority
+    ascending -- ``priority[b]``, default 0, the larger the longer a request keeps its pages
+    --, page index ascending, i.e. oldest first, then request id), and the budget is the
+    deficit: the first ``min(deficit, #candidates)`` are returned as ``(b, page_index)``.
+    Fewer than ``deficit`` means the allocation still fails; that is the caller's concern.
+    """
+    nreq = block_table.shape[0]
+    prio = np.zeros(nreq, dtype=np.int64) if priority is None else np.asarray(priority, np.int64)
+    cand = [(int(prio[b]), p, b) for (b, p) in reclaimable_pages(block_table, seq_len, block_size)
+            if hot_pages is None or not hot_pages[b, p]]
+    cand.sort()
+    return [(b, p) for (_, p, b) in cand[:max(0, int(deficit))]]
+
+
 def is_fully_resident(block_table: np.ndarray, seq_len: np.ndarray, block_size: int) -> np.ndarray:
     """Per request: every page that holds one of its tokens is still mapped in the resident
     pool (P3: once any of a request's resident KV is reclaimed, fully_resident is false;

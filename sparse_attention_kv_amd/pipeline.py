@@ -265,6 +265,32 @@ class ResidencyTracker:
             self.block_table[b, page] = -1
             self.free_blocks.append(blk)
 
+    def reclaim(self, deficit: int, priority=None, hot_pages=None) -> list[tuple[int, int]]:
+        """Give back up to ``deficit`` resident pages and return them as (request, page).
+
+        P3 reclaim_resident_blocks: the cache manager is ``deficit`` blocks short; of the
+        reclaimable pages (older pages, never a request's last two) the hot ones are
+        screened out (``hot_pages`` [num_reqs, bt_stride] bool, e.g. pages the latest
+        selections touched), the rest go in the order request priority ascending
+        (``priority[b]``, default 0; a larger value keeps its pages longer), then oldest
+        page first, then request id, up to the deficit.  Each chosen page is released (its
+        table entry becomes -1, the block goes to the free list), so its request is no
+        longer fully resident.  Fewer than ``deficit`` pages means the caller's allocation
+        still falls short."""
+        prio = np.zeros(self.block_table.shape[0], np.int64) if priority is None \
+            else np.asarray(priority, np.int64)
+        if prio.shape != (self.block_table.shape[0],):
+            raise ValueError("priority must have one entry per request")
+        if hot_pages is not None and np.shape(hot_pages) != self.block_table.shape:
+            raise ValueError("hot_pages must be [num_reqs, bt_stride]")
+        cands = [(int(prio[b]), p, b) for (b, p) in self.reclaimable_pages()
+                 if hot_pages is None or not hot_pages[b][p]]
+        cands.sort()
+        chosen = [(b, p) for (_, p, b) in cands[:max(0, int(deficit))]]
+        for b, p in chosen:
+            self.release_resident_page(b, p)
+        return chosen
+
     def fully_resident(self) -> np.ndarray:
         used = self._used_pages()
         width = self.block_table.shape[1]

@@ -65,3 +65,49 @@ def test_fully_resident_needs_every_used_page_inside_the_table_row():
     bt = np.array([[3, 5], [1, 2], [-1, -1]])
     seq = np.array([9, 8, 0])
     assert oracle.is_fully_resident(bt, seq, 4).tolist() == [False, True, True]
+
+
+def test_reclaim_selection_hand_worked():
+    """Worked by hand (block size 4).  Request 0: 18 tokens, pages 0-4 used, reclaimable
+    pages 0, 1, 2 (never the last two).  Request 1: 20 tokens, pages 0-4 used, reclaimable
+    0, 1, 2.  Request 2: 8 tokens, pages 0-1: nothing reclaimable.  Priorities 5, 1, 0:
+    request 1 gives first (lowest priority among those with candidates), oldest page first;
+    request 0 after it.  Page 1 of request 1 is hot: screened out."""
+    bt = np.array([[10, 11, 12, 13, 14, -1],
+                   [20, 21, 22, 23, 24, -1],
+                   [30, 31, -1, -1, -1, -1]])
+    seq = np.array([18, 20, 8])
+    prio = np.array([5, 1, 0])
+    hot = np.zeros(bt.shape, dtype=bool)
+    hot[1, 1] = True
+    sel = oracle.select_reclaim_pages
+    assert sel(bt, seq, 4, 2, prio, hot) == [(1, 0), (1, 2)]
+    assert sel(bt, seq, 4, 3, prio, hot) == [(1, 0), (1, 2), (0, 0)]
+    assert sel(bt, seq, 4, 9, prio, hot) == [(1, 0), (1, 2), (0, 0), (0, 1), (0, 2)]
+    assert sel(bt, seq, 4, 0, prio, hot) == []
+    # no priorities and no hot pages: oldest page index first across requests, then request
+    assert sel(bt, seq, 4, 4) == [(0, 0), (1, 0), (0, 1), (1, 1)]
+
+
+def test_reclaim_selection_respects_the_budget_and_the_last_two_pages():
+    """Random tables: the selection is at most the deficit, only reclaimable cold pages, in
+    (priority, page, request) order, and it is a prefix of the same ordering with a larger
+    deficit."""
+    rng = np.random.default_rng(21)
+    for trial in range(40):
+        B, W, bs = 6, 10, 8
+        seq = rng.integers(1, W * bs + 1, size=B)
+        bt = rng.permutation(B * W).reshape(B, W)
+        bt[rng.random((B, W)) < 0.15] = -1
+        prio = rng.integers(0, 3, size=B)
+        hot = rng.random((B, W)) < 0.2
+        d = int(rng.integers(0, 12))
+        got = oracle.select_reclaim_pages(bt, seq, bs, d, prio, hot)
+        assert len(got) <= d
+        ok = set(oracle.reclaimable_pages(bt, seq, bs))
+        assert all(bp in ok and not hot[bp] for bp in got)
+        keys = [(prio[b], p, b) for b, p in got]
+        assert keys == sorted(keys)
+        assert got == oracle.select_reclaim_pages(bt, seq, bs, d + 5, prio, hot)[:len(got)]
+        if len(got) < d:  # everything eligible was taken
+            assert len(got) == sum(1 for bp in ok if not hot[bp])

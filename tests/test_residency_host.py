@@ -35,3 +35,27 @@ def test_row_inputs_split_rows_by_their_request():
     assert a.tolist() == [0, -1, 2, 0, -1, 2, -1]
     assert b.tolist() == [-1, 1, -1, -1, 1, -1, -1]
     assert sel.tolist() == [0, 1, 0, 0, 1, 0, 1]
+
+
+def test_reclaim_matches_oracle_selection_and_releases():
+    """ResidencyTracker.reclaim picks the oracle's pages (P3 reclaim_resident_blocks reading)
+    and releases exactly those; requests that gave pages stop being fully resident."""
+    rng = np.random.default_rng(17)
+    for trial in range(30):
+        B, W, bs = 7, 12, 16
+        seq = rng.integers(1, W * bs + 1, size=B)
+        bt = rng.permutation(B * W).reshape(B, W).astype(np.int32)
+        t = ResidencyTracker(bt, seq, bs)
+        for _ in range(3):
+            prio = rng.integers(0, 4, size=B)
+            hot = rng.random((B, W)) < 0.25
+            d = int(rng.integers(0, 9))
+            want = oracle.select_reclaim_pages(t.block_table, seq, bs, d, prio, hot)
+            before = t.block_table.copy()
+            got = t.reclaim(d, prio, hot)
+            assert got == want
+            for b, p in got:
+                assert t.block_table[b, p] == -1 and before[b, p] in t.free_blocks
+            changed = np.argwhere(t.block_table != before)
+            assert sorted(map(tuple, changed.tolist())) == sorted(got)
+            assert np.array_equal(t.fully_resident(), oracle.is_fully_resident(t.block_table, seq, bs))
