@@ -45,6 +45,9 @@
  *     limit, unmapped pages and out-of-range rows become -1 entries.
  *   - Device buffers must not overlap unless stated.  Calls that share state buffers
  *     must be ordered by the caller (same stream, or events).
+ *   - Size limits: a KV row of any cache is at most 65536 bytes; an attention call has at
+ *     most 2^24 (row, head) pairs and top-k at most 2^20.  Beyond them a call returns
+ *     HS_ERR_UNSUPPORTED before any launch (hs_attn_workspace_bytes returns 0).
  */
 #ifndef HISPARSE_H
 #define HISPARSE_H

@@ -39,6 +39,11 @@ hs_status device_view(const void *p, const void **out) {
   return HS_ERR_INVALID_ARG;
 }
 
+// Attention sizes beyond the kernels' limits (rows x heads, keys per row).
+inline bool attn_too_large(int32_t num_rows, int32_t num_heads, int32_t topk) {
+  return static_cast<int64_t>(num_rows) * num_heads > hs::kMaxRowHeads || topk > hs::kMaxAttnTopk;
+}
+
 hs_status check_state(const hs_hot_state *st) {
   if (st == nullptr) return HS_ERR_INVALID_ARG;
   if (st->num_reqs <= 0 || st->capacity <= 0 || st->host_rows <= 0 || st->row_elems <= 0)
@@ -49,6 +54,7 @@ hs_status check_state(const hs_hot_state *st) {
     return HS_ERR_INVALID_ARG;
   const int elem = st->dtype == HS_BF16 ? 2 : 4;
   if ((static_cast<int64_t>(st->row_elems) * elem) % 16 != 0) return HS_ERR_INVALID_ARG;
+  if (static_cast<int64_t>(st->row_elems) * elem > hs::kMaxRowBytes) return HS_ERR_UNSUPPORTED;
   if (!aligned16(st->hot_kv) || !aligned16(st->host_pool)) return HS_ERR_INVALID_ARG;
   if (static_cast<int64_t>(st->num_reqs) * st->capacity > 0x7fffffffLL) return HS_ERR_INVALID_ARG;
   return HS_OK;
@@ -101,6 +107,7 @@ hs_status hs_backup_rows(const void *dev_cache, int64_t dev_layer_rows, void *ho
   if (!dev_cache || !host_cache || !src_slots || !dst_rows) return HS_ERR_INVALID_ARG;
   if (dev_layer_rows > 0x7fffffffLL || host_layer_rows > 0x7fffffffLL) return HS_ERR_INVALID_ARG;
   if (!aligned16(dev_cache) || !aligned16(host_cache)) return HS_ERR_INVALID_ARG;
+  if (row_bytes > hs::kMaxRowBytes) return HS_ERR_UNSUPPORTED;
   const void *host_dev = nullptr;
   hs_status s = device_view(host_cache, &host_dev);
   if (s != HS_OK) return s;
@@ -128,6 +135,7 @@ hs_status hs_apply_plan(void *hot_kv, const void *host_pool, int64_t host_rows,
   if (host_rows > 0x7fffffffLL || static_cast<int64_t>(num_reqs) * capacity > 0x7fffffffLL)
     return HS_ERR_INVALID_ARG;
   if (!aligned16(hot_kv) || !aligned16(host_pool)) return HS_ERR_INVALID_ARG;
+  if (row_bytes > hs::kMaxRowBytes) return HS_ERR_UNSUPPORTED;
   const void *pool = nullptr;
   hs_status s = device_view(host_pool, &pool);
   if (s != HS_OK) return s;
@@ -148,6 +156,7 @@ hs_status hs_append_accepted(void *ctx_cache, int64_t ctx_rows, int32_t row_byte
     return HS_ERR_INVALID_ARG;
   if (ctx_rows > 0x7fffffffLL) return HS_ERR_INVALID_ARG;
   if (!aligned16(ctx_cache) || !aligned16(new_rows)) return HS_ERR_INVALID_ARG;
+  if (row_bytes > hs::kMaxRowBytes || rows_per_req > (1 << 16)) return HS_ERR_UNSUPPORTED;
   return from_hip(hs::launch_append_accepted(ctx_cache, ctx_rows, row_bytes, ctx_block_table,
                                              bt_stride, block_size, physical_block_stride, ctx_len,
                                              new_rows, accept_len, num_reqs, rows_per_req,
@@ -166,6 +175,7 @@ hs_status hs_attn_plan_info(int32_t num_rows, int32_t num_heads, int32_t d_qk, i
   }
   if (dtype != HS_BF16) return HS_ERR_INVALID_ARG;
   if (d_qk != 576 || d_v != 512 || num_heads % 32 != 0) return HS_ERR_UNSUPPORTED;
+  if (attn_too_large(num_rows, num_heads, topk)) return HS_ERR_UNSUPPORTED;
   const hs::AttnPlan p = hs::plan_attn_bf16(num_rows, num_heads, topk);
   if (heads_per_wg) *heads_per_wg = p.heads_per_wg;
   if (splits) *splits = p.splits;
@@ -175,7 +185,7 @@ hs_status hs_attn_plan_info(int32_t num_rows, int32_t num_heads, int32_t d_qk, i
 size_t hs_attn_workspace_bytes(int32_t num_rows, int32_t num_heads, int32_t d_qk, int32_t d_v,
                                int32_t topk, int32_t dtype) {
   if (dtype != HS_BF16 || num_rows <= 0 || topk <= 0 || num_heads <= 0 || num_heads % 32 != 0 ||
-      d_qk != 576 || d_v != 512)
+      d_qk != 576 || d_v != 512 || attn_too_large(num_rows, num_heads, topk))
     return 0;
   return hs::plan_attn_bf16(num_rows, num_heads, topk).workspace;
 }
@@ -205,6 +215,7 @@ hs_status hs::sparse_decode_attn_checked(const void *q, const void *kv, int64_t 
   if (num_rows == 0) return HS_OK;
   if (!q || !kv || !indices || !out) return HS_ERR_INVALID_ARG;
   if (kv_rows > 0x7fffffffLL) return HS_ERR_INVALID_ARG;
+  if (attn_too_large(num_rows, num_heads, topk)) return HS_ERR_UNSUPPORTED;
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (dtype == HS_BF16) {
     if (d_qk != 576 || d_v != 512 || num_heads % 32 != 0) return HS_ERR_UNSUPPORTED;
@@ -244,6 +255,7 @@ hs_status hs_sparse_decode_attn_paged(const void *q, const void *kv_pool, int64_
   if (kv_rows > 0x7fffffffLL) return HS_ERR_INVALID_ARG;
   if (dtype != HS_BF16 || d_qk != 576 || d_v != 512 || num_heads % 32 != 0)
     return HS_ERR_UNSUPPORTED;
+  if (attn_too_large(num_rows, num_heads, topk)) return HS_ERR_UNSUPPORTED;
   if (!aligned16(q) || !aligned16(kv_pool) || !aligned16(out)) return HS_ERR_INVALID_ARG;
   const hs::AttnPlan plan = hs::plan_attn_bf16(num_rows, num_heads, topk);
   if (plan.workspace > 0 &&
@@ -273,6 +285,7 @@ hs_status hs_sparse_decode_attn_mixed(const void *q, const void *kv_a, int64_t k
     return HS_ERR_INVALID_ARG;
   if (kv_a_rows > 0x7fffffffLL || kv_b_rows > 0x7fffffffLL) return HS_ERR_INVALID_ARG;
   if (d_qk != 576 || d_v != 512 || num_heads % 32 != 0) return HS_ERR_UNSUPPORTED;
+  if (attn_too_large(num_rows, num_heads, topk)) return HS_ERR_UNSUPPORTED;
   if (!aligned16(q) || !aligned16(kv_a) || !aligned16(kv_b) || !aligned16(out))
     return HS_ERR_INVALID_ARG;
   const hs::AttnPlan plan = hs::plan_attn_bf16(num_rows, num_heads, topk);

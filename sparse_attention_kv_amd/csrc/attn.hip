@@ -535,20 +535,22 @@ AttnPlan plan_attn_bf16(int32_t num_rows, int32_t num_heads, int32_t topk) {
   // 64 heads per workgroup (each gathered tile serves twice as many heads) once there are
   // enough (row, 64-head) groups; the 32-head kernel has the shorter critical path for
   // small batches.
-  p.heads_per_wg = (num_heads % 64 == 0 && num_rows * (num_heads / 64) >= kMinGroups64) ? 64 : kHG;
-  if (num_heads % 128 == 0 && num_rows * (num_heads / 128) >= kMinGroups128) p.heads_per_wg = 128;
-  const int groups = num_rows * (num_heads / p.heads_per_wg);
+  // (64-bit arithmetic: the callers bound the sizes, this keeps any int32 input defined)
+  const int64_t rows = num_rows, heads = num_heads, keys = topk;
+  p.heads_per_wg = (heads % 64 == 0 && rows * (heads / 64) >= kMinGroups64) ? 64 : kHG;
+  if (heads % 128 == 0 && rows * (heads / 128) >= kMinGroups128) p.heads_per_wg = 128;
+  const int64_t groups = rows * (heads / p.heads_per_wg);
   // Enough workgroups to cover the 256 CUs once, but keep every split >= min_tiles tiles.
-  const int min_keys = (p.heads_per_wg == kHG ? 4 : 2) * kTK;
-  int splits = (topk + kMaxKeysPerSplit - 1) / kMaxKeysPerSplit;
-  while (groups * splits < 256 && (topk + 2 * splits - 1) / (2 * splits) >= min_keys) splits *= 2;
-  int kps = (topk + splits - 1) / splits;
+  const int64_t min_keys = (p.heads_per_wg == kHG ? 4 : 2) * kTK;
+  int64_t splits = (keys + kMaxKeysPerSplit - 1) / kMaxKeysPerSplit;
+  while (groups * splits < 256 && (keys + 2 * splits - 1) / (2 * splits) >= min_keys) splits *= 2;
+  int64_t kps = (keys + splits - 1) / splits;
   kps = (kps + kTK - 1) / kTK * kTK;
-  splits = (topk + kps - 1) / kps;
-  p.splits = splits;
-  p.keys_per_split = kps;
+  splits = (keys + kps - 1) / kps;
+  p.splits = (int)splits;
+  p.keys_per_split = (int)kps;
   // bf16 partial outputs, then fp32 (max, sum) pairs
-  p.workspace = splits > 1 ? (size_t)splits * num_rows * num_heads * (kDV * 2 + 2 * sizeof(float)) : 0;
+  p.workspace = splits > 1 ? (size_t)splits * rows * heads * (kDV * 2 + 2 * sizeof(float)) : 0;
   return p;
 }
 

@@ -18,6 +18,11 @@ typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 
 #define HS_LDS __attribute__((address_space(3)))
 
+// ---- size limits the entry points enforce (beyond them: HS_ERR_UNSUPPORTED) ----
+constexpr int64_t kMaxRowBytes = 1 << 16;      // one KV row of any cache
+constexpr int64_t kMaxRowHeads = 1 << 24;      // attention rows x heads per call
+constexpr int32_t kMaxAttnTopk = 1 << 20;      // attention keys per row
+
 // ---- attention launchers; return hipSuccess or the launch error ----
 // Block-table description for attention that resolves top-k token positions itself
 // (the fully resident batch); null = the indices are already KV rows.
