@@ -333,13 +333,17 @@ hs_status hs_sparse_decode_attn_mixed(const void *q, const void *kv_a, int64_t k
  * no KV yet.  P2 ⑥/timeline table: the next anchor follows the kept prefix.  P1 summary:
  * accepted-KV finalize ends the main line.
  *
- *   logits        [rows, vocab] bf16, rows = st->num_reqs * rows_per_req (wave-major)
+ *   logits        [rows, vocab] bf16, rows = st->num_reqs * rows_per_req (wave-major);
+ *                 or NULL when out_argmax already holds every row's argmax (from
+ *                 hs_greedy_argmax, run earlier on any stream ordered before this call):
+ *                 the call then only accepts and finalizes (vocab is then ignored)
  *   draft_ids     [rows] int32 (the anchor rows' entries are ignored)
  *   new_kv        [rows, st->row_elems] of st->dtype: the verified KV of each row
  *   seq_len       [num_reqs] int32: committed length + rows_per_req (row r of request b
  *                 sits at position seq_len[b] - rows_per_req + r)
  *   block_table   [num_reqs, bt_stride] int32 (physical block stride = block_size)
- *   out_argmax    [rows] int32: lowest index of each row's maximum (NaN never wins)
+ *   out_argmax    [rows] int32: lowest index of each row's maximum (NaN never wins);
+ *                 an input instead when logits is NULL
  *   out_accept_len [num_reqs] int32: L_b = longest l <= rows_per_req-1 with
  *                 draft_ids[row(b,k)] == argmax[row(b,k-1)] for 1 <= k <= l
  *   out_next_token [num_reqs] int32: argmax[row(b, L_b)]
@@ -360,6 +364,21 @@ hs_status hs_finalize_accepted(const hs_hot_state *st, const void *logits, int32
                                int32_t bt_stride, int32_t block_size, int32_t tick,
                                int32_t *out_argmax, int32_t *out_accept_len,
                                int32_t *out_next_token, void *stream);
+
+/*
+ * hs_greedy_argmax -- the greedy choice of P2 ④ on its own: out_argmax[i] = the lowest
+ * index of the maximum of logits row i (bf16, compared exactly; NaN never wins; a row of
+ * only NaN and -inf gives 0).  It depends on the logits alone, so a decode step can run it
+ * ahead of the swap waves and pass its result to hs_finalize_accepted with logits = NULL.
+ *
+ *   logits      [rows, vocab] bf16, 16-byte aligned
+ *   out_argmax  [rows] int32
+ *
+ * Errors: HS_ERR_INVALID_ARG (null or misaligned pointers, rows < 0, vocab < 1); rows == 0
+ * is a no-op.
+ */
+hs_status hs_greedy_argmax(const void *logits, int32_t rows, int32_t vocab, int32_t *out_argmax,
+                           void *stream);
 
 /*
  * Device -> host backup of KV rows: the copy behind prefill staging and page spills.

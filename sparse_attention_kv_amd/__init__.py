@@ -27,6 +27,7 @@ EXPORTED = ("hs_resolve_topk", "hs_swap_in", "hs_sparse_decode_attn", "hs_sparse
             "hs_sparse_decode_attn_mixed",
             "hs_attn_workspace_bytes", "hs_attn_plan_info", "hs_finalize_accepted", "hs_backup_rows", "hs_apply_plan",
             "hs_append_accepted", "hs_host_read", "hs_sparse_decode_attn_noalloc",
+            "hs_greedy_argmax",
             "hs_status_string", "hs_version")
 
 
@@ -80,6 +81,8 @@ def _load() -> ctypes.CDLL:
     lib.hs_sparse_decode_attn_noalloc.argtypes = [vp, vp, i64, vp, i32, i32, i32, i32, i32, f32,
                                                   i32, vp, vp, vp]
     lib.hs_sparse_decode_attn_noalloc.restype = i32
+    lib.hs_greedy_argmax.argtypes = [vp, i32, i32, vp, vp]
+    lib.hs_greedy_argmax.restype = i32
     lib.hs_host_read.argtypes = [vp, vp, i64, vp]
     lib.hs_host_read.restype = i32
     lib.hs_status_string.argtypes = [i32]
@@ -358,17 +361,29 @@ class PagedAttnCall:
             raise HsError("hs_sparse_decode_attn_paged", status, status_string(status))
 
 
-def hs_finalize_accepted(state: HotState, logits: torch.Tensor, draft_ids: torch.Tensor,
+def hs_greedy_argmax(logits: torch.Tensor, out_argmax: torch.Tensor, stream=None):
+    """Lowest index of each bf16 logit row's maximum (see include/hisparse.h)."""
+    _shape(logits.dim() == 2 and tuple(out_argmax.shape) == (logits.shape[0],),
+           "logits [rows, vocab] and out_argmax [rows] expected")
+    _dev(logits, "logits", torch.bfloat16); _dev(out_argmax, "out_argmax", torch.int32)
+    _check("hs_greedy_argmax", _lib.hs_greedy_argmax(_ptr(logits), logits.shape[0],
+                                                     logits.shape[1], _ptr(out_argmax),
+                                                     _stream(stream)))
+
+
+def hs_finalize_accepted(state: HotState, logits: Optional[torch.Tensor], draft_ids: torch.Tensor,
                          new_kv: torch.Tensor, rows_per_req: int, seq_len: torch.Tensor,
                          block_table: torch.Tensor, block_size: int, tick: int,
                          out_argmax: torch.Tensor, out_accept_len: torch.Tensor,
                          out_next_token: torch.Tensor, stream=None):
-    """Greedy accept + accepted-prefix KV keep (see include/hisparse.h)."""
+    """Greedy accept + accepted-prefix KV keep (see include/hisparse.h).  ``logits=None``:
+    ``out_argmax`` already holds the rows' argmax (hs_greedy_argmax) and is read."""
     i32 = torch.int32
     state.check_shapes()
     num_reqs = state.slot_loc.shape[0]
     rows = num_reqs * rows_per_req
-    _shape(logits.dim() == 2 and logits.shape[0] == rows, "logits must be [num_reqs * rows_per_req, vocab]")
+    _shape(logits is None or (logits.dim() == 2 and logits.shape[0] == rows),
+           "logits must be [num_reqs * rows_per_req, vocab]")
     _shape(tuple(draft_ids.shape) == (rows,) and tuple(out_argmax.shape) == (rows,),
            "draft_ids and out_argmax must be [num_reqs * rows_per_req]")
     _shape(tuple(new_kv.shape) == (rows, state.hot_kv.shape[1]),
@@ -378,13 +393,16 @@ def hs_finalize_accepted(state: HotState, logits: torch.Tensor, draft_ids: torch
            "seq_len, out_accept_len and out_next_token must be [num_reqs]")
     _shape(block_table.dim() == 2 and block_table.shape[0] == num_reqs,
            "block_table must be [num_reqs, bt_stride]")
-    _dev(logits, "logits", torch.bfloat16); _dev(draft_ids, "draft_ids", i32)
+    if logits is not None:
+        _dev(logits, "logits", torch.bfloat16)
+    _dev(draft_ids, "draft_ids", i32)
     _dev(new_kv, "new_kv", state.hot_kv.dtype); _dev(seq_len, "seq_len", i32)
     _dev(block_table, "block_table", i32); _dev(out_argmax, "out_argmax", i32)
     _dev(out_accept_len, "out_accept_len", i32); _dev(out_next_token, "out_next_token", i32)
     st = state.as_struct()
     _check("hs_finalize_accepted", _lib.hs_finalize_accepted(
-        ctypes.byref(st), _ptr(logits), logits.shape[1], _ptr(draft_ids), _ptr(new_kv),
+        ctypes.byref(st), _ptr(logits), 0 if logits is None else logits.shape[1], _ptr(draft_ids),
+        _ptr(new_kv),
         rows_per_req, _ptr(seq_len), _ptr(block_table), block_table.shape[1], block_size, tick,
         _ptr(out_argmax), _ptr(out_accept_len), _ptr(out_next_token), _stream(stream)))
     state.note_tick(tick)

@@ -306,13 +306,15 @@ hs_status hs_finalize_accepted(const hs_hot_state *st, const void *logits, int32
                                int32_t *out_next_token, void *stream) {
   hs_status s = check_state(st);
   if (s != HS_OK) return s;
-  if (vocab <= 0 || rows_per_req <= 0 || bt_stride <= 0 || block_size <= 0) return HS_ERR_INVALID_ARG;
-  if (!logits || !draft_ids || !new_kv || !seq_len || !block_table || !out_argmax ||
-      !out_accept_len || !out_next_token)
+  if ((logits != nullptr && vocab <= 0) || rows_per_req <= 0 || bt_stride <= 0 || block_size <= 0)
+    return HS_ERR_INVALID_ARG;
+  if (!draft_ids || !new_kv || !seq_len || !block_table || !out_argmax || !out_accept_len ||
+      !out_next_token)
     return HS_ERR_INVALID_ARG;
   if (rows_per_req > st->capacity) return HS_ERR_INVALID_ARG;
   if (rows_per_req > hs::finalize_max_rows_per_req()) return HS_ERR_UNSUPPORTED;
-  if (!aligned16(new_kv) || !aligned16(logits)) return HS_ERR_INVALID_ARG;
+  if (!aligned16(new_kv) || (logits != nullptr && !aligned16(logits))) return HS_ERR_INVALID_ARG;
+  if (static_cast<int64_t>(st->num_reqs) * rows_per_req > 0x7fffffffLL) return HS_ERR_INVALID_ARG;
   const void *pool = nullptr;
   s = device_view(st->host_pool, &pool);
   if (s != HS_OK) return s;
@@ -320,6 +322,14 @@ hs_status hs_finalize_accepted(const hs_hot_state *st, const void *logits, int32
                                       seq_len, block_table, bt_stride, block_size, tick, out_argmax,
                                       out_accept_len, out_next_token,
                                       static_cast<hipStream_t>(stream)));
+}
+
+hs_status hs_greedy_argmax(const void *logits, int32_t rows, int32_t vocab, int32_t *out_argmax,
+                           void *stream) {
+  if (rows < 0 || vocab <= 0) return HS_ERR_INVALID_ARG;
+  if (rows == 0) return HS_OK;
+  if (!logits || !out_argmax || !aligned16(logits)) return HS_ERR_INVALID_ARG;
+  return from_hip(hs::launch_argmax(logits, rows, vocab, out_argmax, static_cast<hipStream_t>(stream)));
 }
 
 hs_status hs_host_read(const void *host_src, void *dst, int64_t bytes, void *stream) {

@@ -10,7 +10,9 @@
 // finalize closes the main line.
 //
 // Kernel 1 (one workgroup per row): argmax over the vocabulary, lowest index on ties,
-//   16-byte loads of 8 bf16 logits (HBM-bound streaming read).
+//   16-byte loads of 8 bf16 logits (HBM-bound streaming read).  It depends on the logits
+//   only, so a caller may run it on its own (hs_greedy_argmax) ahead of the rest of the
+//   step and hand its result to kernel 2.
 // Kernel 2 (one workgroup per request): acceptance length, then
 //   dropped rows -> hot slots holding them are emptied;
 //   kept rows    -> new KV stored to the pinned host pool (device stores over the host
@@ -349,16 +351,22 @@ __global__ __launch_bounds__(kFinThreads) void finalize_kernel(
 
 }  // namespace
 
+hipError_t launch_argmax(const void *logits, int32_t rows, int32_t vocab, int32_t *out_argmax,
+                         hipStream_t stream) {
+  hipLaunchKernelGGL(argmax_kernel, dim3(rows), dim3(kArgThreads), 0, stream,
+                     static_cast<const uint16_t *>(logits), vocab, out_argmax);
+  return hipGetLastError();
+}
+
 hipError_t launch_finalize(const hs_hot_state &st, const void *host_pool_dev, const void *logits,
                            int32_t vocab, const int32_t *draft_ids, const void *new_kv,
                            int32_t rows_per_req, const int32_t *seq_len, const int32_t *block_table,
                            int32_t bt_stride, int32_t block_size, int32_t tick, int32_t *out_argmax,
                            int32_t *out_accept_len, int32_t *out_next_token, hipStream_t stream) {
-  const int rows = st.num_reqs * rows_per_req;
-  hipLaunchKernelGGL(argmax_kernel, dim3(rows), dim3(kArgThreads), 0, stream,
-                     static_cast<const uint16_t *>(logits), vocab, out_argmax);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (logits != nullptr) {  // else out_argmax already holds every row's argmax
+    const hipError_t e = launch_argmax(logits, st.num_reqs * rows_per_req, vocab, out_argmax, stream);
+    if (e != hipSuccess) return e;
+  }
   const int elem = st.dtype == HS_BF16 ? 2 : 4;
   hipLaunchKernelGGL(finalize_kernel, dim3(st.num_reqs), dim3(kFinThreads), 0, stream, st.num_reqs,
                      st.capacity, st.slot_loc, st.slot_stamp, st.loc_to_hot, st.host_rows,

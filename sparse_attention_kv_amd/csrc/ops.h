@@ -23,6 +23,11 @@ hipError_t launch_swap_in(const hs_hot_state &st, const void *host_pool_dev,
                           int32_t *out_hot_idx, int32_t *out_miss_count, int32_t *out_miss_pos,
                           hipStream_t stream);
 
+// Argmax of each bf16 logit row (lowest index of the maximum, NaN never wins).
+hipError_t launch_argmax(const void *logits, int32_t rows, int32_t vocab, int32_t *out_argmax,
+                         hipStream_t stream);
+
+// logits == nullptr: out_argmax already holds the rows' argmax (only kernel 2 runs).
 hipError_t launch_finalize(const hs_hot_state &st, const void *host_pool_dev, const void *logits,
                            int32_t vocab, const int32_t *draft_ids, const void *new_kv,
                            int32_t rows_per_req, const int32_t *seq_len, const int32_t *block_table,

@@ -37,7 +37,7 @@ import numpy as np
 import torch
 
 from . import (HotState, hs_append_accepted, hs_attn_workspace_bytes, hs_backup_rows,
-               hs_finalize_accepted,
+               hs_finalize_accepted, hs_greedy_argmax,
                hs_resolve_topk, hs_sparse_decode_attn, hs_sparse_decode_attn_mixed,
                hs_sparse_decode_attn_paged, hs_swap_in)
 
@@ -164,6 +164,10 @@ class DecodeStep:
                         b.slots, b.valid)
         self.e_resolve.record(main)
         copy.wait_event(self.e_resolve)
+        if finalize is not None:
+            # the greedy choice needs only the logits: it runs while wave 0's swap-in holds
+            # the host link, and finalize later reads its result
+            hs_greedy_argmax(finalize["logits"], b.argmax, stream=main)
         for r in range(R):
             lo, hi = r * B, (r + 1) * B
             if r >= 1 and serialize:
@@ -183,10 +187,9 @@ class DecodeStep:
             self.e_attn[r].record(main)
         if finalize is not None:
             mark("finalize", None, 0, main)
-            hs_finalize_accepted(state, finalize["logits"], finalize["draft_ids"],
-                                 finalize["new_kv"], R, finalize["seq_len"], block_table,
-                                 block_size, tick0 + R, b.argmax, b.accept_len, b.next_token,
-                                 stream=main)
+            hs_finalize_accepted(state, None, finalize["draft_ids"], finalize["new_kv"], R,
+                                 finalize["seq_len"], block_table, block_size, tick0 + R,
+                                 b.argmax, b.accept_len, b.next_token, stream=main)
             mark("finalize", None, 1, main)
             d = finalize.get("dflash")
             if d is not None:  # P2 ⑤: the draft model's context KV takes the accepted prefix

@@ -63,6 +63,12 @@ int main() {
   expect("finalize null", hs_finalize_accepted(&st, nullptr, 100, p, v, 3, p, p, 8, 16, 1, p, p, p, nullptr), E);
   expect("finalize misaligned", hs_finalize_accepted(&st, v, 100, p, mis, 3, p, p, 8, 16, 1, p, p, p, nullptr), E);
 
+  expect("argmax zero rows", hs_greedy_argmax(nullptr, 0, 10, nullptr, nullptr), HS_OK);
+  expect("argmax vocab", hs_greedy_argmax(v, 4, 0, p, nullptr), E);
+  expect("argmax misaligned", hs_greedy_argmax(mis, 4, 10, p, nullptr), E);
+  expect("argmax null out", hs_greedy_argmax(v, 4, 10, nullptr, nullptr), E);
+  expect("finalize from argmax, misaligned rows", hs_finalize_accepted(&st, nullptr, 0, p, mis, 3, p, p, 8, 16, 1, p, p, p, nullptr), E);
+
   // attention
   expect("attn zero rows", hs_sparse_decode_attn(v, v, 10, p, 0, 128, 576, 512, 2048, 0.1f, HS_BF16, v, nullptr, nullptr, 0, nullptr), HS_OK);
   expect("attn dtype", hs_sparse_decode_attn(v, v, 10, p, 2, 128, 576, 512, 2048, 0.1f, 9, v, nullptr, nullptr, 0, nullptr), E);

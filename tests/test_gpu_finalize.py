@@ -285,6 +285,61 @@ def test_finalize_eviction_of_a_stale_copy():
     assert np.array_equal(hpool.numpy(), opool)
 
 
+@pytest.mark.parametrize("vocab", [9, 129280])
+def test_greedy_argmax_alone_then_finalize_from_it(vocab):
+    """hs_greedy_argmax gives the oracle's argmax (special values included), and
+    hs_finalize_accepted with logits=None, reading that argmax, leaves the same state,
+    host rows and outputs as the one-call form."""
+    import sparse_attention_kv_amd as hs
+    from sparse_attention_kv_amd.pipeline import build_hot_state
+    rng = np.random.default_rng(vocab + 5)
+    B, R, cap, bs, width = 6, 3, 24, 8, 10
+    bt = rng.permutation(B * width).astype(np.int32).reshape(B, width)
+    seq = rng.integers(cap + R, width * bs, size=B).astype(np.int32)
+    pool = rng.standard_normal((B * width * bs, 8)).astype(np.float32)
+    init_pos = np.full((B, cap), -1, np.int32)
+    init_stamp = np.full((B, cap), -1, np.int32)
+    for b in range(B):
+        init_pos[b] = rng.choice(int(seq[b]), cap, replace=False)
+        init_stamp[b] = rng.integers(0, 30, size=cap)
+    gen = torch.Generator().manual_seed(vocab)
+    logits = torch.randn(B * R, vocab, generator=gen).to(torch.bfloat16)
+    logits[0, :] = float("nan"); logits[1, :] = -float("inf"); logits[2, vocab - 1] = 60.0
+    plant = rng.integers(0, vocab, size=B * R)
+    logits[torch.arange(3, B * R), torch.from_numpy(plant[3:])] = 40.0
+    draft = rng.integers(0, vocab, size=B * R).astype(np.int32)
+    for r in range(1, R):
+        for b in range(B):
+            if rng.random() < 0.7:
+                draft[r * B + b] = plant[(r - 1) * B + b]
+    new_kv = rng.standard_normal((B * R, 8)).astype(np.float32)
+    _, _, am = oracle.greedy_accept(raw(logits), draft, B, R)
+    results = []
+    for split in (False, True):
+        hpool = _pinned(pool)
+        gst = build_hot_state(torch.from_numpy(init_pos), torch.from_numpy(init_stamp), to_dev(seq),
+                              to_dev(bt), bs, hpool, dev())
+        g_am = torch.full((B * R,), -5, dtype=torch.int32, device=dev())
+        g_acc = torch.empty((B,), dtype=torch.int32, device=dev())
+        g_nxt = torch.empty((B,), dtype=torch.int32, device=dev())
+        lg = logits.to(dev())
+        log(f"finalize split={split} vocab={vocab}")
+        if split:
+            hs.hs_greedy_argmax(lg, g_am)
+            torch.cuda.synchronize()
+            assert np.array_equal(g_am.cpu().numpy(), am), "hs_greedy_argmax"
+            hs.hs_finalize_accepted(gst, None, to_dev(draft), torch.from_numpy(new_kv).to(dev()), R,
+                                    to_dev(seq), to_dev(bt), bs, 50, g_am, g_acc, g_nxt)
+        else:
+            hs.hs_finalize_accepted(gst, lg, to_dev(draft), torch.from_numpy(new_kv).to(dev()), R,
+                                    to_dev(seq), to_dev(bt), bs, 50, g_am, g_acc, g_nxt)
+        torch.cuda.synchronize()
+        results.append([t.cpu().clone() for t in (g_am, g_acc, g_nxt, gst.slot_loc, gst.slot_stamp,
+                                                  gst.loc_to_hot, gst.hot_kv)] + [hpool.clone()])
+    for i, (a, b_) in enumerate(zip(*results)):
+        assert torch.equal(a, b_), f"output {i} differs between the one-call and split forms"
+
+
 def test_attention_identical_on_resident_and_swap_paths():
     """Same rows, same index order: the paged pool and the hot buffer give equal bits."""
     import sparse_attention_kv_amd as hs
