@@ -22,15 +22,10 @@ constexpr int kMaxKeysPerSplit = 2048;
 constexpr int kWaves = kThreads / 64;
 constexpr float kLn2 = 0.69314718055994530942f;
 
-// LDS-only barrier: waits for this wave's LDS traffic, then s_barrier.  Outstanding
-// global loads (the next tile's direct-to-LDS gathers) are deliberately not waited for:
-// an LDS release fence would make the compiler wait for them too (they write LDS), so the
-// wait and the barrier are one asm statement whose memory clobber keeps the compiler from
-// moving memory accesses across it.  Code that needs a gathered tile waits with
-// wait_vmem() first.
-__device__ __forceinline__ void lds_barrier() {
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
+// The kernels synchronise with lds_barrier() (common.h): outstanding global loads (the
+// next tile's direct-to-LDS gathers) are deliberately not waited for there, since an LDS
+// release fence would make the compiler wait for them too (they write LDS).  Code that
+// needs a gathered tile waits with wait_vmem() first.
 // Direct-to-LDS 16-byte load: lane l's 16 bytes from src land at LDS byte lds_base + 16 l.
 // Written as inline asm so that the compiler's wait-count insertion does not treat every
 // later LDS read of either tile buffer as dependent on it (it cannot tell the buffers

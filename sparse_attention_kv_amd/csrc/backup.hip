@@ -7,8 +7,8 @@
 // host pool asynchronously and the request decodes once that event has fired.
 //
 // The copy is a zero-copy scatter: every thread reads 16-byte chunks of source rows from
-// HBM and writes them with vector stores straight into the pinned host cache through its
-// device mapping.  Chunks are numbered (layer, entry, chunk of row) so that consecutive
+// HBM and writes them with write-through vector stores straight into the pinned host cache
+// through its device mapping.  Chunks are numbered (layer, entry, chunk of row) so that consecutive
 // lanes write consecutive 16 bytes of one host row and a wave's stores form whole lines
 // on the host link.  Each thread keeps kUnroll chunk loads in flight before it stores.
 
@@ -61,7 +61,7 @@ __global__ __launch_bounds__(kThreads) void backup_rows_kernel(
     }
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u)
-      if (dst[u] >= 0) *reinterpret_cast<i32x4 *>(host_cache + dst[u]) = v[u];
+      if (dst[u] >= 0) store_through16(host_cache + dst[u], v[u]);
   }
 }
 

@@ -109,18 +109,40 @@ __global__ __launch_bounds__(kArgThreads) void argmax_kernel(const uint16_t *__r
   }
 }
 
+// One step of a wave minimum over 64-bit keys: each lane takes the minimum of its key and
+// the key of the lane that the DPP control selects (lanes without a source, or in rows the
+// mask leaves out, keep their own).
+template <int kCtrl, int kRowMask>
+__device__ __forceinline__ uint64_t dpp_min_step(uint64_t v) {
+  const int lo = static_cast<int>(v), hi = static_cast<int>(v >> 32);
+  const uint32_t plo = __builtin_amdgcn_update_dpp(lo, lo, kCtrl, kRowMask, 0xf, false);
+  const uint32_t phi = __builtin_amdgcn_update_dpp(hi, hi, kCtrl, kRowMask, 0xf, false);
+  const uint64_t p = (static_cast<uint64_t>(phi) << 32) | plo;
+  return p < v ? p : v;
+}
+
+// Wave minimum: row_shr 1, 2, 4, 8 leave each 16-lane row's minimum in its lane 15;
+// row_bcast 15 then 31 carry it across rows, so lane 63 ends with the wave's minimum.
+__device__ __forceinline__ uint64_t wave_min_u64(uint64_t v) {
+  v = dpp_min_step<0x111, 0xf>(v);
+  v = dpp_min_step<0x112, 0xf>(v);
+  v = dpp_min_step<0x114, 0xf>(v);
+  v = dpp_min_step<0x118, 0xf>(v);
+  v = dpp_min_step<0x142, 0xa>(v);
+  v = dpp_min_step<0x143, 0xc>(v);
+  const uint32_t lo = __builtin_amdgcn_readlane(static_cast<int>(v), 63);
+  const uint32_t hi = __builtin_amdgcn_readlane(static_cast<int>(v >> 32), 63);
+  return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+
 // Block-wide minimum of (stamp, slot) keys packed in 64 bits.
 __device__ __forceinline__ uint64_t block_min_u64(uint64_t v, uint64_t *s_red) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) {
-    const uint64_t o = __shfl_xor(v, off, 64);
-    v = o < v ? o : v;
-  }
+  v = wave_min_u64(v);
   if (lane_id() == 0) s_red[threadIdx.x >> 6] = v;
-  __syncthreads();
+  lds_barrier();
   uint64_t r = s_red[0];
   for (int wv = 1; wv < kFinThreads / 64; ++wv) r = s_red[wv] < r ? s_red[wv] : r;
-  __syncthreads();
+  lds_barrier();
   return r;
 }
 
@@ -216,7 +238,7 @@ __global__ __launch_bounds__(kFinThreads) void finalize_kernel(
     }
     s_loc[tid] = loc;
   }
-  __syncthreads();
+  lds_barrier();
   const int L = s_L;
 
   // The slot each verify row occupies, looked up once (the rows' host rows are distinct,
@@ -228,8 +250,8 @@ __global__ __launch_bounds__(kFinThreads) void finalize_kernel(
     s_slot[tid] = -1;
   }
 
-  // kept rows' new KV -> their host-pool rows (device stores over the host link); issued
-  // early so the link transfer overlaps the slot bookkeeping below
+  // kept rows' new KV -> their host-pool rows (device stores written through over the host
+  // link); issued early so the link transfer overlaps the slot bookkeeping below
   for (int c = tid; c < (L + 1) * chunks; c += kFinThreads) {
     const int r = c / chunks;
     const int part = c - r * chunks;
@@ -237,9 +259,9 @@ __global__ __launch_bounds__(kFinThreads) void finalize_kernel(
     if (loc < 0) continue;
     const i32x4 v = c == tid ? kv_first : *reinterpret_cast<const i32x4 *>(
         new_kv + ((int64_t)r * num_reqs + b) * row_bytes + part * 16);
-    *reinterpret_cast<i32x4 *>(host_pool + (int64_t)loc * row_bytes + part * 16) = v;
+    store_through16(host_pool + (int64_t)loc * row_bytes + part * 16, v);
   }
-  __syncthreads();
+  lds_barrier();
 
   // dropped rows: empty the slot that holds them (host rows untouched)
   if (tid < R && tid > L && s_hit[tid] >= 0) {
@@ -269,7 +291,9 @@ __global__ __launch_bounds__(kFinThreads) void finalize_kernel(
     if (miss) s_miss[__builtin_popcountll(mm & ((1ull << r) - 1))] = r;
     if (tid == 0) s_nmiss = __builtin_popcountll(mm);
   }
-  __syncthreads();
+  // (the slow victim search below re-reads stamps and owners from memory, which the
+  // dropped-row clears above wrote: it needs the full barrier)
+  if (in_regs) lds_barrier(); else __syncthreads();
   const int nmiss = s_nmiss;
 
   // victims: repeatedly the least-recently-used unpinned, unchosen slot (nmiss <= R).  (A
@@ -295,7 +319,7 @@ __global__ __launch_bounds__(kFinThreads) void finalize_kernel(
           s_vown[k] = owner[i];
         }
     }
-    __syncthreads();
+    lds_barrier();
   } else if (nmiss > 0) {
     for (int k = 0; k < nmiss; ++k) {
       uint64_t best = ~0ull;
@@ -325,7 +349,7 @@ __global__ __launch_bounds__(kFinThreads) void finalize_kernel(
     s_slot[s_miss[rank]] = v;
     s_owner[s_miss[rank]] = s_vown[tid];
   }
-  __syncthreads();
+  lds_barrier();
   if (tid < nmiss && s_slot[s_miss[tid]] >= 0) {
     const int r = s_miss[tid];
     const int64_t g = slot_base + s_slot[r];
