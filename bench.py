@@ -26,7 +26,8 @@ objects: `hbm_roofline` (the step's attention dispatches against the 8 TB/s HBM 
 `long_context_step` (64 requests x 4 rows at seq_len 131072, 9.66 GB pinned pool),
 `resident_decode` (8 fully resident rows, warm and cold caches), `attn_sweep`, `swap_in`
 (the 32-request MTP workload), `finalize`, `backup`, `resolve`, and `cpu_baseline` (the CPU
-oracle on a sample of the headline step).
+oracle on a sample of the headline step).  `--part power` (not in the default run) adds
+`attn_power`: socket power and gfx clock (amd-smi) while the attention op runs back to back.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--part NAME]
 """
@@ -561,6 +562,100 @@ def measure_attn_sweep(dev, sizes=(32, 64, 128, 256), reps=40):
                         "128 heads x 576/512 bf16, cold caches", "sizes": out_rows}
 
 
+def smi_power_clock():
+    """(socket W, gfx MHz) from one `amd-smi metric -p -c --json` reading, or None."""
+    import subprocess
+    try:
+        p = subprocess.run(["amd-smi", "metric", "-p", "-c", "--json"], capture_output=True,
+                           text=True, timeout=20)
+        d = json.loads(p.stdout)
+    except (OSError, ValueError, subprocess.SubprocessError):
+        return None
+    g = d[0] if isinstance(d, list) else d
+    if isinstance(g, dict) and "gpu_data" in g:
+        g = g["gpu_data"][0]
+
+    def val(x):
+        return x.get("value") if isinstance(x, dict) else x
+    try:
+        return float(val(g["power"]["socket_power"])), float(val(g["clock"]["gfx_0"]["clk"]))
+    except (KeyError, TypeError, ValueError):
+        return None
+
+
+def measure_power(dev, sizes=(8, 64, 128, 256), secs=6.0):
+    """Socket power and gfx clock while the attention op runs back to back for `secs` at
+    each size (the sweep's inputs: top-k 2048 distinct rows of a 1M-row pool, 128 heads,
+    cold index sets), read with amd-smi from a second thread 2, 3 and 4 s into the run.
+    Shows which sizes run at the board's power limit, where time per call follows energy
+    per call rather than cycles."""
+    import threading
+
+    import torch
+
+    import sparse_attention_kv_amd as hs
+    H, D, DV, K, N = 128, 576, 512, 2048, 1 << 20
+    g = torch.Generator(device=dev).manual_seed(20261202)
+    kv = torch.randn((N, D), generator=g, device=dev).to(torch.bfloat16)
+    main = torch.cuda.current_stream()
+    idle = smi_power_clock()
+    out_rows = []
+    for rows in sizes:
+        alg = attn_alg_bytes([K] * rows, H, D, DV, K)
+        nsets = max(2, min(16, math.ceil(600e6 / alg)))
+        qs = [torch.randn((rows, H, D), generator=g, device=dev).to(torch.bfloat16) for _ in range(nsets)]
+        idx = [torch.stack([torch.randperm(N, generator=g, device=dev)[:K] for _ in range(rows)])
+               .to(torch.int32).contiguous() for _ in range(nsets)]
+        out = torch.empty((rows, H, DV), dtype=torch.bfloat16, device=dev)
+        lse = torch.empty((rows, H), dtype=torch.float32, device=dev)
+        wsb = hs.hs_attn_workspace_bytes(rows, H, D, DV, K, torch.bfloat16)
+        ws = torch.empty((max(wsb, 16),), dtype=torch.uint8, device=dev) if wsb else None
+
+        def call(i):
+            hs.hs_sparse_decode_attn(qs[i % nsets], kv, idx[i % nsets], D ** -0.5, DV, out, lse, ws)
+        for i in range(2 * nsets):
+            call(i)
+        torch.cuda.synchronize()
+        readings = []
+
+        def sample():
+            time.sleep(2.0)
+            for _ in range(3):
+                r = smi_power_clock()
+                if r is not None:
+                    readings.append(r)
+                time.sleep(0.5)
+        th = threading.Thread(target=sample)
+        a, z = ev(), ev()
+        t0 = time.time()
+        th.start()
+        a.record(main)
+        n = 0
+        while time.time() - t0 < secs:
+            for i in range(100):
+                call(n + i)
+            n += 100
+            torch.cuda.synchronize()
+        z.record(main)
+        torch.cuda.synchronize()
+        th.join()
+        us = a.elapsed_time(z) * 1e3 / n
+        hpw, spl = hs.hs_attn_plan_info(rows, H, D, DV, K, torch.bfloat16)
+        out_rows.append({
+            "rows": rows, "kernel_heads_per_wg": hpw, "splits": spl, "us": us, "calls": n,
+            "hbm_frac": alg / (us / 1e6) / 1e9 / HBM_PEAK_GBS,
+            "socket_W": statistics.median(w for w, _ in readings) if readings else None,
+            "gfx_MHz": statistics.median(c for _, c in readings) if readings else None,
+            "energy_per_row_mJ": (statistics.median(w for w, _ in readings) * us / 1e6 / rows * 1e3
+                                  if readings else None)})
+        del qs, idx, out, lse, ws
+    del kv
+    torch.cuda.empty_cache()
+    return {"workload": "attention op back to back, top-k 2048 distinct rows of a 1M-row pool, "
+                        "128 heads x 576/512 bf16, cold index sets; amd-smi socket power and gfx clock",
+            "idle_W_MHz": idle, "board_power_limit_W": 1400, "sizes": out_rows}
+
+
 # ----------------------------------------------------------------------------------------
 # MTP swap workload: waves, plan reuse, mixed batch, cold wave
 # ----------------------------------------------------------------------------------------
@@ -906,7 +1001,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--part", default="all",
                     choices=["all", "headline", "long", "resident", "sweep", "swap", "finalize",
-                             "backup", "resolve"],
+                             "backup", "resolve", "power"],
                     help="run one section only (for profiler runs); the JSON line then holds "
                          "that section's object, and the headline fields only with 'headline'")
     args = ap.parse_args()
@@ -1018,6 +1113,9 @@ def run_sections(dev, args, b_host, res, parts):
         elif part == "resolve":
             log("resolve")
             res["resolve"] = measure_resolve(dev)
+        elif part == "power":
+            log("attention power and clock")
+            res["attn_power"] = measure_power(dev)
 
 
 if __name__ == "__main__":
