@@ -81,14 +81,6 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-// 16-byte vector store with the system-scope cache policy (sc0 sc1): written through to
-// memory rather than held in L2 until the kernel-end writeback.  For stores into pinned host
-// memory, where a held store otherwise crosses the host link only after the kernel's last
-// instruction (measured: the finalize call's 280 host rows then cost ~4.5 us of tail).
-__device__ __forceinline__ void store_through16(void *p, const i32x4 &v) {
-  asm volatile("global_store_dwordx4 %0, %1, off sc0 sc1" : : "v"(p), "v"(v) : "memory");
-}
-
 // Exclusive prefix sum of `v` across the 64 lanes of a wave; `total` receives the sum.
 __device__ __forceinline__ int wave_exclusive_scan(int v, int &total) {
   int x = v;
