@@ -147,6 +147,45 @@ def test_finalize_sixty_four_verify_rows(accept):
                             new_kv, tick=40)
     assert acc.tolist() == [accept] * B
 
+@pytest.mark.parametrize("accept", [3, 1, 0])
+def test_finalize_large_capacity_with_resident_and_dropped_rows(accept):
+    """4608 hot slots per request, beyond the 4096 (stamp, slot) keys the kernel keeps in
+    registers, with verify rows already resident: kept ones are pinned, dropped ones are
+    emptied in memory first, and the victim search then reads those emptied slots (the
+    preferred victims) from memory.  Nearly full buffers with stamps from a small range
+    (many ties, broken by slot)."""
+    rng = np.random.default_rng(4608 + accept)
+    B, R, cap, bs, width = 3, 4, 4608, 64, 80
+    bt = rng.permutation(B * width).astype(np.int32).reshape(B, width)
+    seq = np.full(B, width * bs - 3, np.int32)
+    pool = rng.standard_normal((B * width * bs, 16)).astype(np.float32)
+    init_pos = np.full((B, cap), -1, np.int32)
+    init_stamp = np.full((B, cap), -1, np.int32)
+    for b in range(B):
+        sl = rng.permutation(cap)
+        pos = rng.choice(int(seq[b]) - R, cap - 8, replace=False)
+        init_pos[b, sl[:cap - 8]] = pos
+        init_stamp[b, sl[:cap - 8]] = rng.integers(0, 30, size=cap - 8)
+        hits = seq[b] - R + np.array([0, 2, 3]) if b != 1 else seq[b] - R + np.array([1])
+        init_pos[b, sl[cap - 8:cap - 8 + len(hits)]] = hits  # resident verify rows
+        init_stamp[b, sl[cap - 8:cap - 8 + len(hits)]] = rng.integers(0, 30, size=len(hits))
+    vocab = 300
+    gen = torch.Generator().manual_seed(4608 + accept)
+    logits = torch.randn(B * R, vocab, generator=gen).to(torch.bfloat16)
+    plant = rng.integers(0, vocab, size=B * R)
+    logits[torch.arange(B * R), torch.from_numpy(plant)] = 9.0
+    draft = rng.integers(0, vocab, size=B * R).astype(np.int32)
+    for b in range(B):
+        for r in range(1, accept + 1):
+            draft[r * B + b] = plant[(r - 1) * B + b]
+        if accept + 1 < R:
+            draft[(accept + 1) * B + b] = (plant[accept * B + b] + 1) % vocab
+    new_kv = rng.standard_normal((B * R, 16)).astype(np.float32)
+    acc, *_ = _run_finalize(B, R, cap, seq, bt, bs, pool, init_pos, init_stamp, logits, draft,
+                            new_kv, tick=31)
+    assert acc.tolist() == [accept] * B
+
+
 @pytest.mark.parametrize("vocab", [129280, 129281, 8, 9])
 def test_argmax_special_values(vocab):
     """Argmax rows with NaN, -inf, all-NaN and all -inf rows, the maximum in the first or
