@@ -17,9 +17,9 @@ def _bf16(a: np.ndarray) -> torch.Tensor:
     return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev())
 
 
-def test_append_rounds_match_oracle():
+def test_append_steps_match_oracle():
     """The verify shape of the mixed workload (128 requests x 3 rows, 576-wide bf16 rows),
-    three rounds, with unmapped pages and out-of-range accept lengths."""
+    three decode steps, with unmapped pages and out-of-range accept lengths."""
     import sparse_attention_kv_amd as hs
     rng = np.random.default_rng(12)
     B, R, E, bs, W = 128, 3, 576, 64, 40
@@ -31,7 +31,7 @@ def test_append_rounds_match_oracle():
     for rnd in range(3):
         rows = rng.integers(0, 2 ** 16, size=(B * R, E), dtype=np.uint16)
         acc = rng.integers(-1, R + 1, size=B).astype(np.int32)
-        log(f"append round {rnd}")
+        log(f"append step {rnd}")
         hs.hs_append_accepted(g_cache, g_bt, g_len, _bf16(rows), to_dev(acc), bs, bs, R)
         torch.cuda.synchronize()
         cache, lens64 = oracle.append_accepted(cache, bt, lens, rows, acc, R, bs, bs)

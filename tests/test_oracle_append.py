@@ -11,7 +11,7 @@ import oracle
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "worked_example.json")
 
 
-def test_worked_example_round_one():
+def test_worked_example_first_verify_step():
     g = json.load(open(GOLDEN))
     d, names = g["dflash_context"], g["token_names"]
     rows = [names[t] for t in g["verify_rows"]]         # a0, b1, b2, b3 (one request)
@@ -27,8 +27,9 @@ def test_worked_example_round_one():
     assert out[written, 0].tolist() == [names[t] for t in d["appended_rows"]]
 
 
-def test_two_rounds_continue_where_the_first_stopped():
-    """Round 2 appends after round 1's last position; nothing else is written."""
+def test_two_appends_continue_where_the_first_stopped():
+    """A second append continues after the first one's last position; nothing else is
+    written."""
     rng = np.random.default_rng(1)
     B, R, bs, W = 4, 4, 8, 10
     bt = rng.permutation(B * W).reshape(B, W)
