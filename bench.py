@@ -589,7 +589,7 @@ def smi_power_clock():
         return None
 
 
-def measure_power(dev, sizes=(8, 64, 128, 256), secs=6.0):
+def measure_power(dev, sizes=(8, 32, 64, 128, 256), secs=6.0):
     """Socket power and gfx clock while the attention op runs back to back for `secs` at
     each size (the sweep's inputs: top-k 2048 distinct rows of a 1M-row pool, 128 heads,
     cold index sets), read with amd-smi from a second thread 2, 3 and 4 s into the run.
