@@ -550,10 +550,18 @@ AttnPlan plan_attn_bf16(int32_t num_rows, int32_t num_heads, int32_t topk) {
   p.heads_per_wg = (heads % 64 == 0 && rows * (heads / 64) >= kMinGroups64) ? 64 : kHG;
   if (heads % 128 == 0 && rows * (heads / 128) >= kMinGroups128) p.heads_per_wg = 128;
   const int64_t groups = rows * (heads / p.heads_per_wg);
-  // Enough workgroups to cover the 256 CUs once, but keep every split >= min_tiles tiles.
-  const int64_t min_keys = (p.heads_per_wg == kHG ? 4 : 2) * kTK;
-  int64_t splits = (keys + kMaxKeysPerSplit - 1) / kMaxKeysPerSplit;
-  while (groups * splits < 256 && (keys + 2 * splits - 1) / (2 * splits) >= min_keys) splits *= 2;
+  // Key splits: as many as still fit the 256 CUs in one round of workgroups (each takes a
+  // whole CU's LDS, so a 257th would wait for a second round), none shorter than two tiles,
+  // and at least enough that no split holds more than kMaxKeysPerSplit keys.  Doubling the
+  // split count while the grid was below 256 gave 384-496 workgroups at 12-31 and 40-96
+  // rows of 128 heads; one round instead measured 12-30 % faster there (1 and 2 rows 7-10 %
+  // faster with two-tile splits instead of four), and the same at 8, 16, 32 and 64 rows.
+  const int64_t min_keys = 2 * kTK;
+  const int64_t fit = groups > 0 ? 256 / groups : 1, longest = keys / min_keys;
+  int64_t splits = fit < longest ? fit : longest;
+  if (splits < 1) splits = 1;
+  const int64_t at_least = (keys + kMaxKeysPerSplit - 1) / kMaxKeysPerSplit;
+  if (splits < at_least) splits = at_least;
   int64_t kps = (keys + splits - 1) / splits;
   kps = (kps + kTK - 1) / kTK * kTK;
   splits = (keys + kps - 1) / kps;
