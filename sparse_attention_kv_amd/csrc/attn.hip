@@ -33,13 +33,14 @@ namespace hs {
 namespace {
 
 constexpr int kHG = 32;                       // heads per workgroup
-// (row, 64-head) groups from which attn64 runs.  With 128 heads, 16 and 24 rows measure
-// 7-10 % faster on the 32-head kernel; from 32 rows the 64-head one wins.
-constexpr int kMinGroups64 = 64;
-// (row, 128-head) groups from which attn128 runs.  It reads each KV row once per row instead
-// of twice, but with fewer workgroups than compute units (even after key splits) the 64-head
-// kernel measures faster.
-constexpr int kMinGroups128 = 256;
+// (row, 64-head) groups from which attn64 runs.  With 128 heads (top-k 2048) the 32-head
+// kernel measures faster up to 20 rows (8-20 rows: 4-9 %), the 64-head one from 24 rows
+// (24-31 rows: 6-10 %).
+constexpr int kMinGroups64 = 48;
+// (row, 128-head) groups from which attn128 runs: more than 128.  It reads each KV row once
+// per row instead of twice; above 128 groups the 64-head kernel needs a second round of
+// workgroups (160-224 rows: 15-21 % slower than attn128), at 128 the two measure the same.
+constexpr int kMinGroups128 = 129;
 constexpr int kThreads8 = 512;                // 8 waves: two per SIMD
 constexpr int kWaves8 = kThreads8 / 64;
 constexpr int kSlots8 = tile::kTK * tile::kRowChunks / kThreads8;  // 9 gather slots per wave

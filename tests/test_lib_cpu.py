@@ -197,14 +197,14 @@ def test_attn_plan_info():
                                                                    torch.bfloat16)
     assert plan(8) == (32, 8)        # 32 workgroups of (row, 32 heads) -> 8 key splits
     # splits fill the 256 CUs in one round of workgroups, each split at least two tiles
-    assert plan(1) == (32, 16) and plan(12) == (32, 5) and plan(24) == (32, 2)
+    assert plan(1) == (32, 16) and plan(12) == (32, 5) and plan(20) == (32, 3)
     assert plan(40) == (64, 3) and plan(96) == (64, 1)
     for rows in range(1, 256):
         hpw, splits = plan(rows)
         groups = rows * (128 // hpw)
         assert groups * splits <= 256 if groups <= 256 else splits == 1, rows
-    assert plan(24)[0] == 32 and plan(32)[0] == 64 and plan(255)[0] == 64 and plan(256)[0] == 128
-    assert plan(128) == (64, 1) and plan(256) == (128, 1)
+    assert plan(20)[0] == 32 and plan(24)[0] == 64 and plan(128)[0] == 64 and plan(129)[0] == 128
+    assert plan(128) == (64, 1) and plan(256) == (128, 1) and plan(192) == (128, 1)
     assert plan(8, topk=4500)[1] >= 3  # one split holds at most 2048 keys
     assert plan(40, heads=96)[0] == 32  # 96 heads: only the 32-head kernel
     assert hs.hs_attn_plan_info(4, 4, 64, 48, 16, torch.float32) == (1, 1)
