@@ -231,6 +231,31 @@ hs_status hs_sparse_decode_attn(const void *q, const void *kv, int64_t kv_rows,
                                 size_t workspace_bytes, void *stream);
 
 /*
+ * hs_sparse_decode_attn_cus -- hs_sparse_decode_attn sized for part of the GPU, for a call
+ * that runs beside another kernel on another stream: on the swap path the next wave's
+ * swap-in runs during this wave's attention (P1 "1. 启动阶段": the hot buffer is filled on
+ * an async stream), and that swap-in needs compute units of its own.  Every attention
+ * workgroup holds one compute unit (its LDS), so a whole-GPU launch takes all 256 and a
+ * kernel started beside it waits for them to drain.  This call computes exactly what
+ * hs_sparse_decode_attn computes (same arguments, same results up to the order in which
+ * fp32 partial sums are added), with its kernel and key splits chosen for `max_cus`
+ * compute units:
+ *
+ *   max_cus   > 0; 256 or more is the whole GPU (the plain call).  The launch takes at most
+ *             max_cus workgroups when the kernel chosen has at most max_cus (row,
+ *             head-group) units times ceil(topk / 2048) (a key split holds at most 2048
+ *             keys); larger batches take one workgroup per unit and split.
+ *   workspace the size hs_attn_workspace_bytes returns for the same sizes always suffices.
+ *
+ * Errors: as hs_sparse_decode_attn; HS_ERR_INVALID_ARG for max_cus <= 0.
+ */
+hs_status hs_sparse_decode_attn_cus(const void *q, const void *kv, int64_t kv_rows,
+                                    const int32_t *indices, int32_t num_rows, int32_t num_heads,
+                                    int32_t d_qk, int32_t d_v, int32_t topk, float scale,
+                                    int32_t dtype, void *out, float *lse, void *workspace,
+                                    size_t workspace_bytes, int32_t max_cus, void *stream);
+
+/*
  * hs_sparse_decode_attn_paged -- the fully resident batch in one call: P3 resolve_topk
  * listing (when every request's KV is resident, the top-k positions are converted to
  * cache rows through the block table and attention reads the paged cache directly).
@@ -271,6 +296,12 @@ hs_status hs_sparse_decode_attn_paged(const void *q, const void *kv_pool, int64_
 hs_status hs_attn_plan_info(int32_t num_rows, int32_t num_heads, int32_t d_qk, int32_t d_v,
                             int32_t topk, int32_t dtype, int32_t *heads_per_wg,
                             int32_t *splits);
+
+/* hs_attn_plan_info for hs_sparse_decode_attn_cus with `max_cus` compute units (> 0;
+ * HS_ERR_INVALID_ARG otherwise). */
+hs_status hs_attn_plan_info_cus(int32_t num_rows, int32_t num_heads, int32_t d_qk, int32_t d_v,
+                                int32_t topk, int32_t dtype, int32_t max_cus,
+                                int32_t *heads_per_wg, int32_t *splits);
 
 /*
  * hs_sparse_decode_attn_noalloc -- hs_sparse_decode_attn for callers that cannot allocate

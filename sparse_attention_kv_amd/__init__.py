@@ -24,8 +24,8 @@ NOALLOC_SCRATCH_BYTES = 32 << 20
 HS_BF16, HS_F32 = 0, 1
 
 EXPORTED = ("hs_resolve_topk", "hs_swap_in", "hs_sparse_decode_attn", "hs_sparse_decode_attn_paged",
-            "hs_sparse_decode_attn_mixed",
-            "hs_attn_workspace_bytes", "hs_attn_plan_info", "hs_finalize_accepted", "hs_backup_rows", "hs_apply_plan",
+            "hs_sparse_decode_attn_mixed", "hs_sparse_decode_attn_cus",
+            "hs_attn_workspace_bytes", "hs_attn_plan_info", "hs_attn_plan_info_cus", "hs_finalize_accepted", "hs_backup_rows", "hs_apply_plan",
             "hs_append_accepted", "hs_host_read", "hs_sparse_decode_attn_noalloc",
             "hs_greedy_argmax",
             "hs_status_string", "hs_version")
@@ -58,6 +58,9 @@ def _load() -> ctypes.CDLL:
     lib.hs_sparse_decode_attn.argtypes = [vp, vp, i64, vp, i32, i32, i32, i32, i32, f32, i32,
                                           vp, vp, vp, sz, vp]
     lib.hs_sparse_decode_attn.restype = i32
+    lib.hs_sparse_decode_attn_cus.argtypes = [vp, vp, i64, vp, i32, i32, i32, i32, i32, f32, i32,
+                                              vp, vp, vp, sz, i32, vp]
+    lib.hs_sparse_decode_attn_cus.restype = i32
     lib.hs_sparse_decode_attn_paged.argtypes = [vp, vp, i64, vp, vp, vp, i32, vp, i32, i32, i32,
                                                 i32, i32, i32, i32, i32, f32, i32, vp, vp, vp, sz,
                                                 vp]
@@ -68,6 +71,8 @@ def _load() -> ctypes.CDLL:
     lib.hs_attn_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32]
     lib.hs_attn_plan_info.argtypes = [i32, i32, i32, i32, i32, i32, vp, vp]
     lib.hs_attn_plan_info.restype = i32
+    lib.hs_attn_plan_info_cus.argtypes = [i32, i32, i32, i32, i32, i32, i32, vp, vp]
+    lib.hs_attn_plan_info_cus.restype = i32
     lib.hs_attn_workspace_bytes.restype = sz
     lib.hs_finalize_accepted.argtypes = [ctypes.POINTER(HsHotState), vp, i32, vp, vp, i32, vp, vp,
                                          i32, i32, i32, vp, vp, vp, vp]
@@ -249,6 +254,39 @@ def hs_attn_plan_info(num_rows: int, num_heads: int, d_qk: int, d_v: int, topk: 
                                                        _dtype_code(dtype), ctypes.byref(hpw),
                                                        ctypes.byref(spl)))
     return hpw.value, spl.value
+
+
+def hs_attn_plan_info_cus(num_rows: int, num_heads: int, d_qk: int, d_v: int, topk: int,
+                          dtype: torch.dtype, max_cus: int):
+    """hs_attn_plan_info for hs_sparse_decode_attn_cus with ``max_cus`` compute units."""
+    hpw, spl = ctypes.c_int32(0), ctypes.c_int32(0)
+    _check("hs_attn_plan_info_cus", _lib.hs_attn_plan_info_cus(
+        num_rows, num_heads, d_qk, d_v, topk, _dtype_code(dtype), max_cus, ctypes.byref(hpw),
+        ctypes.byref(spl)))
+    return hpw.value, spl.value
+
+
+def hs_sparse_decode_attn_cus(q: torch.Tensor, kv: torch.Tensor, indices: torch.Tensor,
+                              scale: float, d_v: int, out: torch.Tensor,
+                              lse: Optional[torch.Tensor] = None,
+                              workspace: Optional[torch.Tensor] = None, max_cus: int = 256,
+                              stream=None):
+    """hs_sparse_decode_attn sized for ``max_cus`` compute units, leaving the rest of the GPU
+    to a kernel running beside it (see include/hisparse.h)."""
+    _attn_shapes(q, kv, indices, d_v, out, lse)
+    _dev(q, "q"); _dev(kv, "kv"); _dev(indices, "indices", torch.int32); _dev(out, "out", q.dtype)
+    if kv.dtype != q.dtype:
+        raise ValueError("q and kv dtypes differ")
+    if lse is not None:
+        _dev(lse, "lse", torch.float32)
+    if workspace is not None:
+        _dev(workspace, "workspace")
+    rows, heads, d_qk = q.shape
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("hs_sparse_decode_attn_cus", _lib.hs_sparse_decode_attn_cus(
+        _ptr(q), _ptr(kv), kv.shape[0], _ptr(indices), rows, heads, d_qk, d_v, indices.shape[1],
+        float(scale), _dtype_code(q.dtype), _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes,
+        int(max_cus), _stream(stream)))
 
 
 def hs_sparse_decode_attn(q: torch.Tensor, kv: torch.Tensor, indices: torch.Tensor, scale: float,

@@ -166,6 +166,14 @@ hs_status hs_append_accepted(void *ctx_cache, int64_t ctx_rows, int32_t row_byte
 hs_status hs_attn_plan_info(int32_t num_rows, int32_t num_heads, int32_t d_qk, int32_t d_v,
                             int32_t topk, int32_t dtype, int32_t *heads_per_wg,
                             int32_t *splits) {
+  return hs_attn_plan_info_cus(num_rows, num_heads, d_qk, d_v, topk, dtype, hs::kNumCUs,
+                               heads_per_wg, splits);
+}
+
+hs_status hs_attn_plan_info_cus(int32_t num_rows, int32_t num_heads, int32_t d_qk, int32_t d_v,
+                                int32_t topk, int32_t dtype, int32_t max_cus,
+                                int32_t *heads_per_wg, int32_t *splits) {
+  if (max_cus <= 0) return HS_ERR_INVALID_ARG;
   if (num_rows <= 0 || num_heads <= 0 || d_qk <= 0 || d_v <= 0 || topk <= 0)
     return HS_ERR_INVALID_ARG;
   if (dtype == HS_F32) {
@@ -176,7 +184,7 @@ hs_status hs_attn_plan_info(int32_t num_rows, int32_t num_heads, int32_t d_qk, i
   if (dtype != HS_BF16) return HS_ERR_INVALID_ARG;
   if (d_qk != 576 || d_v != 512 || num_heads % 32 != 0) return HS_ERR_UNSUPPORTED;
   if (attn_too_large(num_rows, num_heads, topk)) return HS_ERR_UNSUPPORTED;
-  const hs::AttnPlan p = hs::plan_attn_bf16(num_rows, num_heads, topk);
+  const hs::AttnPlan p = hs::plan_attn_bf16(num_rows, num_heads, topk, max_cus);
   if (heads_per_wg) *heads_per_wg = p.heads_per_wg;
   if (splits) *splits = p.splits;
   return HS_OK;
@@ -197,7 +205,18 @@ hs_status hs_sparse_decode_attn(const void *q, const void *kv, int64_t kv_rows,
                                 size_t workspace_bytes, void *stream) {
   return hs::sparse_decode_attn_checked(q, kv, kv_rows, indices, num_rows, num_heads, d_qk, d_v,
                                         topk, scale, dtype, out, lse, workspace, workspace_bytes,
-                                        stream);
+                                        stream, hs::kNumCUs);
+}
+
+hs_status hs_sparse_decode_attn_cus(const void *q, const void *kv, int64_t kv_rows,
+                                    const int32_t *indices, int32_t num_rows, int32_t num_heads,
+                                    int32_t d_qk, int32_t d_v, int32_t topk, float scale,
+                                    int32_t dtype, void *out, float *lse, void *workspace,
+                                    size_t workspace_bytes, int32_t max_cus, void *stream) {
+  if (max_cus <= 0) return HS_ERR_INVALID_ARG;
+  return hs::sparse_decode_attn_checked(q, kv, kv_rows, indices, num_rows, num_heads, d_qk, d_v,
+                                        topk, scale, dtype, out, lse, workspace, workspace_bytes,
+                                        stream, max_cus);
 }
 
 }  // extern "C"
@@ -208,7 +227,8 @@ hs_status hs::sparse_decode_attn_checked(const void *q, const void *kv, int64_t 
                                          const int32_t *indices, int32_t num_rows,
                                          int32_t num_heads, int32_t d_qk, int32_t d_v, int32_t topk,
                                          float scale, int32_t dtype, void *out, float *lse,
-                                         void *workspace, size_t workspace_bytes, void *stream) {
+                                         void *workspace, size_t workspace_bytes, void *stream,
+                                         int32_t max_cus) {
   if (num_rows < 0 || num_heads <= 0 || d_qk <= 0 || d_v <= 0 || topk <= 0 || kv_rows < 0)
     return HS_ERR_INVALID_ARG;
   if (dtype != HS_BF16 && dtype != HS_F32) return HS_ERR_INVALID_ARG;
@@ -220,7 +240,7 @@ hs_status hs::sparse_decode_attn_checked(const void *q, const void *kv, int64_t 
   if (dtype == HS_BF16) {
     if (d_qk != 576 || d_v != 512 || num_heads % 32 != 0) return HS_ERR_UNSUPPORTED;
     if (!aligned16(q) || !aligned16(kv) || !aligned16(out)) return HS_ERR_INVALID_ARG;
-    const hs::AttnPlan plan = hs::plan_attn_bf16(num_rows, num_heads, topk);
+    const hs::AttnPlan plan = hs::plan_attn_bf16(num_rows, num_heads, topk, max_cus);
     if (plan.workspace > 0 && (workspace == nullptr || workspace_bytes < plan.workspace ||
                                !aligned16(workspace)))
       return HS_ERR_INVALID_ARG;

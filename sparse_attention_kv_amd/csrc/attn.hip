@@ -33,14 +33,14 @@ namespace hs {
 namespace {
 
 constexpr int kHG = 32;                       // heads per workgroup
-// (row, 64-head) groups from which attn64 runs.  With 128 heads (top-k 2048) the 32-head
-// kernel measures faster up to 20 rows (8-20 rows: 4-9 %), the 64-head one from 24 rows
-// (24-31 rows: 6-10 %).
+// (row, 64-head) groups from which attn64 runs on the whole GPU.  With 128 heads (top-k
+// 2048) the 32-head kernel measures faster up to 20 rows (8-20 rows: 4-9 %), the 64-head
+// one from 24 rows (24-31 rows: 6-10 %).  With fewer CUs the threshold scales with them.
 constexpr int kMinGroups64 = 48;
-// (row, 128-head) groups from which attn128 runs: more than 128.  It reads each KV row once
-// per row instead of twice; above 128 groups the 64-head kernel needs a second round of
-// workgroups (160-224 rows: 15-21 % slower than attn128), at 128 the two measure the same.
-constexpr int kMinGroups128 = 129;
+// attn128 runs with more (row, 128-head) groups than half the CUs the call may use.  It
+// reads each KV row once per row instead of twice; above 128 groups on the whole GPU the
+// 64-head kernel needs a second round of workgroups (160-224 rows: 15-21 % slower than
+// attn128), at 128 the two measure the same.
 constexpr int kThreads8 = 512;                // 8 waves: two per SIMD
 constexpr int kWaves8 = kThreads8 / 64;
 constexpr int kSlots8 = tile::kTK * tile::kRowChunks / kThreads8;  // 9 gather slots per wave
@@ -541,25 +541,27 @@ void launch_attn_combine(const __bf16 *ws_o, const float *ws_ml, int32_t splits,
                      ws_ml, splits, num_rows, num_heads, out, lse);
 }
 
-AttnPlan plan_attn_bf16(int32_t num_rows, int32_t num_heads, int32_t topk) {
+// The launch for `cus` compute units: every attention workgroup holds one CU (its LDS), so
+// the grid is sized for one round of `cus` workgroups where the batch allows.
+static AttnPlan plan_for(int64_t rows, int64_t heads, int64_t keys, int64_t cus,
+                         int64_t max_splits) {
   AttnPlan p;
   // 64 heads per workgroup (each gathered tile serves twice as many heads) once there are
   // enough (row, 64-head) groups; the 32-head kernel has the shorter critical path for
   // small batches.
-  // (64-bit arithmetic: the callers bound the sizes, this keeps any int32 input defined)
-  const int64_t rows = num_rows, heads = num_heads, keys = topk;
-  p.heads_per_wg = (heads % 64 == 0 && rows * (heads / 64) >= kMinGroups64) ? 64 : kHG;
-  if (heads % 128 == 0 && rows * (heads / 128) >= kMinGroups128) p.heads_per_wg = 128;
+  p.heads_per_wg = (heads % 64 == 0 && rows * (heads / 64) * kNumCUs >= kMinGroups64 * cus) ? 64 : kHG;
+  if (heads % 128 == 0 && 2 * rows * (heads / 128) > cus) p.heads_per_wg = 128;
   const int64_t groups = rows * (heads / p.heads_per_wg);
-  // Key splits: as many as still fit the 256 CUs in one round of workgroups (each takes a
-  // whole CU's LDS, so a 257th would wait for a second round), none shorter than two tiles,
-  // and at least enough that no split holds more than kMaxKeysPerSplit keys.  Doubling the
-  // split count while the grid was below 256 gave 384-496 workgroups at 12-31 and 40-96
-  // rows of 128 heads; one round instead measured 12-30 % faster there (1 and 2 rows 7-10 %
-  // faster with two-tile splits instead of four), and the same at 8, 16, 32 and 64 rows.
+  // Key splits: as many as still fit the CUs in one round of workgroups (a workgroup more
+  // would wait for a second round), none shorter than two tiles, and at least enough that
+  // no split holds more than kMaxKeysPerSplit keys.  Doubling the split count while the grid
+  // was below 256 gave 384-496 workgroups at 12-31 and 40-96 rows of 128 heads; one round
+  // instead measured 12-30 % faster there (1 and 2 rows 7-10 % faster with two-tile splits
+  // instead of four), and the same at 8, 16, 32 and 64 rows.
   const int64_t min_keys = 2 * kTK;
-  const int64_t fit = groups > 0 ? 256 / groups : 1, longest = keys / min_keys;
+  const int64_t fit = groups > 0 ? cus / groups : 1, longest = keys / min_keys;
   int64_t splits = fit < longest ? fit : longest;
+  if (splits > max_splits) splits = max_splits;
   if (splits < 1) splits = 1;
   const int64_t at_least = (keys + kMaxKeysPerSplit - 1) / kMaxKeysPerSplit;
   if (splits < at_least) splits = at_least;
@@ -571,6 +573,17 @@ AttnPlan plan_attn_bf16(int32_t num_rows, int32_t num_heads, int32_t topk) {
   // bf16 partial outputs, then fp32 (max, sum) pairs
   p.workspace = splits > 1 ? (size_t)splits * rows * heads * (kDV * 2 + 2 * sizeof(float)) : 0;
   return p;
+}
+
+AttnPlan plan_attn_bf16(int32_t num_rows, int32_t num_heads, int32_t topk, int32_t max_cus) {
+  // (64-bit arithmetic: the callers bound the sizes, this keeps any int32 input defined)
+  const int64_t rows = num_rows, heads = num_heads, keys = topk;
+  const AttnPlan whole = plan_for(rows, heads, keys, kNumCUs, keys);
+  if (max_cus >= kNumCUs) return whole;
+  // Fewer CUs: never more key splits than the whole-GPU plan (the workspace is splits x
+  // rows x heads partials for every kernel), so its workspace (hs_attn_workspace_bytes)
+  // serves every call.
+  return plan_for(rows, heads, keys, max_cus > 0 ? max_cus : 1, whole.splits);
 }
 
 template <bool kPaged>

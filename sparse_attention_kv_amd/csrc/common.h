@@ -49,7 +49,11 @@ struct AttnPlan {
   int keys_per_split;  // multiple of the key tile
   size_t workspace;    // bytes
 };
-AttnPlan plan_attn_bf16(int32_t num_rows, int32_t num_heads, int32_t topk);
+constexpr int kNumCUs = 256;  // compute units of the GPU (MI355X)
+// Kernel and key splits for these sizes, sized for `max_cus` compute units (kNumCUs: the
+// whole GPU; fewer leave the rest to a kernel running beside the call on another stream).
+AttnPlan plan_attn_bf16(int32_t num_rows, int32_t num_heads, int32_t topk,
+                        int32_t max_cus = kNumCUs);
 
 hipError_t launch_attn_bf16(const void *q, const void *kv, int64_t kv_rows, const int32_t *indices,
                             int32_t num_rows, int32_t num_heads, int32_t topk, float scale,

@@ -55,5 +55,5 @@ extern "C" hs_status hs_sparse_decode_attn_noalloc(const void *q, const void *kv
   const hs_status s = scratch_on_current_device(&ws);
   if (s != HS_OK) return s;
   return hs::sparse_decode_attn_checked(q, kv, kv_rows, indices, num_rows, num_heads, d_qk, d_v,
-                                        topk, scale, dtype, out, lse, ws, kScratchBytes, stream);
+                                        topk, scale, dtype, out, lse, ws, kScratchBytes, stream, hs::kNumCUs);
 }

@@ -63,12 +63,13 @@ hipError_t launch_append_accepted(void *ctx_cache, int64_t ctx_rows, int32_t row
                                   const int32_t *accept_len, int32_t num_reqs,
                                   int32_t rows_per_req, hipStream_t stream);
 
-// hs_sparse_decode_attn's validation and launch (every argument as in the C ABI).
+// hs_sparse_decode_attn's validation and launch (every argument as in the C ABI; max_cus
+// as for hs_sparse_decode_attn_cus).
 hs_status sparse_decode_attn_checked(const void *q, const void *kv, int64_t kv_rows,
                                      const int32_t *indices, int32_t num_rows, int32_t num_heads,
                                      int32_t d_qk, int32_t d_v, int32_t topk, float scale,
                                      int32_t dtype, void *out, float *lse, void *workspace,
-                                     size_t workspace_bytes, void *stream);
+                                     size_t workspace_bytes, void *stream, int32_t max_cus);
 
 // Streaming zero-copy read of pinned host memory (host_src_dev: its device address) into
 // device memory, chunks of 16 bytes; the host link's reference read rate.

@@ -38,8 +38,8 @@ import torch
 
 from . import (HotState, hs_append_accepted, hs_attn_workspace_bytes, hs_backup_rows,
                hs_finalize_accepted, hs_greedy_argmax,
-               hs_resolve_topk, hs_sparse_decode_attn, hs_sparse_decode_attn_mixed,
-               hs_sparse_decode_attn_paged, hs_swap_in)
+               hs_resolve_topk, hs_sparse_decode_attn, hs_sparse_decode_attn_cus,
+               hs_sparse_decode_attn_mixed, hs_sparse_decode_attn_paged, hs_swap_in)
 
 
 def build_hot_state(init_pos: torch.Tensor, init_stamp: torch.Tensor, seq_len: torch.Tensor,
@@ -118,6 +118,11 @@ class DecodeStep:
             slots_res=torch.empty((rows, topk), **i32) if (swap and mixed) else None,
         )
         self.copy_stream = torch.cuda.Stream(device=device) if swap else None
+        # An attention workgroup holds a whole CU and a swap-in workgroup (one per request)
+        # needs one too: an attention that runs beside the next wave's swap-in is sized for
+        # the CUs that swap leaves free, so the swap never waits for the attention to drain.
+        cus = torch.cuda.get_device_properties(device).multi_processor_count if swap else 0
+        self.cus_beside_swap = max(64, cus - num_reqs)
         self.e_resolve = torch.cuda.Event()
         self.e_swap = [torch.cuda.Event() for _ in range(rows_per_req)]
         self.e_attn = [torch.cuda.Event() for _ in range(rows_per_req)]
@@ -181,8 +186,13 @@ class DecodeStep:
             self.e_swap[r].record(copy)
             main.wait_event(self.e_swap[r])
             mark("attn", r, 0, main)
-            hs_sparse_decode_attn(q[lo:hi], state.hot_kv, b.hot_idx[lo:hi], scale, self.d_v,
-                                  b.out[lo:hi], b.lse[lo:hi], b.workspace, stream=main)
+            if r + 1 < R and not serialize:  # the next wave's swap-in runs beside it
+                hs_sparse_decode_attn_cus(q[lo:hi], state.hot_kv, b.hot_idx[lo:hi], scale,
+                                          self.d_v, b.out[lo:hi], b.lse[lo:hi], b.workspace,
+                                          self.cus_beside_swap, stream=main)
+            else:
+                hs_sparse_decode_attn(q[lo:hi], state.hot_kv, b.hot_idx[lo:hi], scale, self.d_v,
+                                      b.out[lo:hi], b.lse[lo:hi], b.workspace, stream=main)
             mark("attn", r, 1, main)
             self.e_attn[r].record(main)
         if finalize is not None:

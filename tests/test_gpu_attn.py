@@ -289,3 +289,40 @@ def test_attn_head_counts(H, rows):
     assert_close(out_f64(out[sample]), ref, BF16_TOL, f"H={H} rows={rows}")
     g = lse[sample].cpu().double().numpy()
     assert_close(g, rlse, LSE_TOL, f"H={H} rows={rows} lse")
+
+
+@pytest.mark.parametrize("rows,cus,topk", [(128, 128, 2048), (32, 224, 2048), (8, 64, 777),
+                                           (20, 192, 2048), (3, 16, 4500)])
+def test_attn_cus_matches_oracle_and_plain_call(rows, cus, topk):
+    """hs_sparse_decode_attn_cus: the launch sized for `cus` compute units (another kernel,
+    or none, in the others) gives the oracle's result on every row, with the plain call's
+    workspace size, and the plain call's result up to fp32 summation order."""
+    import sparse_attention_kv_amd as hs
+    H, kv_rows = 128, 9000
+    hpw, splits = hs.hs_attn_plan_info_cus(rows, H, 576, 512, topk, torch.bfloat16, cus)
+    if rows * (H // hpw) * -(-topk // 2048) <= cus:
+        assert rows * (H // hpw) * splits <= cus
+    rng = np.random.default_rng(rows * 1000 + cus)
+    q = _rand_bf16((rows, H, 576), 900 + rows)
+    kv = _rand_bf16((kv_rows, 576), 901 + rows)
+    idx = np.stack([rng.choice(kv_rows, topk, replace=False) for _ in range(rows)]).astype(np.int32)
+    idx[1, rng.random(topk) < 0.3] = -1
+    idx[2, :] = -1
+    idx = to_dev(idx)
+    ws_bytes = hs.hs_attn_workspace_bytes(rows, H, 576, 512, topk, torch.bfloat16)
+    ws = torch.empty((ws_bytes,), dtype=torch.uint8, device=dev()) if ws_bytes else None
+    out = torch.full((rows, H, 512), float("nan"), dtype=torch.bfloat16, device=dev())
+    lse = torch.full((rows, H), float("nan"), dtype=torch.float32, device=dev())
+    log(f"attn cus: rows={rows} cus={cus} topk={topk} plan=({hpw}, {splits})")
+    hs.hs_sparse_decode_attn_cus(q, kv, idx, 1 / 24, 512, out, lse, ws, cus)
+    torch.cuda.synchronize()
+    ref, rlse = oracle.sparse_decode_attn(raw(q.cpu()), raw(kv.cpu()), idx.cpu().numpy(), 1 / 24, 512)
+    assert_close(out_f64(out), ref, BF16_TOL, f"cus {cus}")
+    g = lse.cpu().double().numpy()
+    fin = np.isfinite(rlse)
+    assert np.array_equal(np.isfinite(g), fin)
+    assert_close(g[fin], rlse[fin], LSE_TOL, f"cus {cus} lse")
+    plain, plain_lse = _attn(q, kv, idx, 1 / 24, 512)
+    assert_close(out_f64(out), out_f64(plain), BF16_TOL, f"cus {cus} vs plain")
+    with pytest.raises(hs.HsError):
+        hs.hs_sparse_decode_attn_cus(q, kv, idx, 1 / 24, 512, out, lse, ws, 0)

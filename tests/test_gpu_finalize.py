@@ -380,7 +380,8 @@ def test_greedy_argmax_alone_then_finalize_from_it(vocab):
 
 
 def test_attention_identical_on_resident_and_swap_paths():
-    """Same rows, same index order: the paged pool and the hot buffer give equal bits."""
+    """Same rows, same index order, same launch: the paged pool and the hot buffer give
+    equal bits."""
     import sparse_attention_kv_amd as hs
     from sparse_attention_kv_amd.pipeline import DecodeStep
     for name, over in (("tiny", {}), ("mtp_swap", dict(num_reqs=4, seq_rule=("const", 5000)))):
@@ -391,6 +392,8 @@ def test_attention_identical_on_resident_and_swap_paths():
         step = DecodeStep(num_reqs=s.num_reqs, rows_per_req=s.rows_per_req, topk=s.topk,
                           num_heads=s.num_heads, d_qk=s.d_qk, d_v=s.d_v, dtype=w.q.dtype,
                           capacity=s.capacity, device=dev())
+        # waves followed by another swap-in run the attention sized for the CUs it leaves
+        overlap = step.overlaps(gst, s.tick0)
         log(f"cross-path {name}: swap path")
         step.run_swap(gst, g["topk_pos"], g["req_id"], g["causal_limit"], g["block_table"],
                       s.block_size, g["q"], s.scale, s.tick0)
@@ -408,7 +411,8 @@ def test_attention_identical_on_resident_and_swap_paths():
             lo, hi = r * B, (r + 1) * B
             ws_b = hs.hs_attn_workspace_bytes(B, s.num_heads, s.d_qk, s.d_v, s.topk, w.q.dtype)
             ws = torch.empty((max(ws_b, 16),), dtype=torch.uint8, device=dev()) if ws_b else None
-            hs.hs_sparse_decode_attn(g["q"][lo:hi], dev_pool, res.buf.slots[lo:hi], s.scale, s.d_v,
-                                     out_wave[lo:hi], None, ws)
+            cus = step.cus_beside_swap if (overlap and r + 1 < s.rows_per_req) else 256
+            hs.hs_sparse_decode_attn_cus(g["q"][lo:hi], dev_pool, res.buf.slots[lo:hi], s.scale,
+                                         s.d_v, out_wave[lo:hi], None, ws, cus)
         torch.cuda.synchronize()
         assert torch.equal(out_wave, step.buf.out), name

@@ -214,6 +214,34 @@ def test_attn_plan_info():
     assert lib.hs_attn_plan_info(8, 128, 576, 512, 2048, 9, None, None) == hs.HS_ERR_INVALID_ARG
 
 
+def test_attn_plan_info_cus():
+    """The launch sized for part of the GPU: at most max_cus workgroups when the chosen
+    kernel's (row, head-group) units fit in them with the fewest splits top-k needs, never
+    more key splits than the whole-GPU plan (its workspace is enough), and the whole-GPU
+    plan at 256 or more."""
+    import torch
+    hs, lib = _lib()
+    plan = lambda rows, heads=128, topk=2048: hs.hs_attn_plan_info(rows, heads, 576, 512, topk,
+                                                                   torch.bfloat16)
+    cus = lambda rows, c, heads=128, topk=2048: hs.hs_attn_plan_info_cus(
+        rows, heads, 576, 512, topk, torch.bfloat16, c)
+    assert cus(128, 128) == (128, 1)  # 128 workgroups: the other 128 CUs stay free
+    assert cus(64, 192) == (64, 1) and cus(32, 224) == (64, 3)
+    for heads in (32, 64, 128, 256):
+        for topk in (1, 65, 2048, 4500):
+            for rows in (1, 2, 3, 8, 12, 20, 24, 32, 40, 64, 100, 128, 129, 200, 256, 300):
+                whole = plan(rows, heads, topk)
+                assert cus(rows, 256, heads, topk) == whole and cus(rows, 999, heads, topk) == whole
+                for c in (1, 32, 64, 128, 192, 255):
+                    hpw, splits = cus(rows, c, heads, topk)
+                    units = rows * (heads // hpw)
+                    assert splits <= whole[1], (rows, heads, topk, c)
+                    if units * -(-topk // 2048) <= c:  # a split holds at most 2048 keys
+                        assert units * splits <= c, (rows, heads, topk, c)
+    h = ctypes.c_int32(0)
+    assert lib.hs_attn_plan_info_cus(8, 128, 576, 512, 2048, hs.HS_BF16, 0, ctypes.byref(h), None) == hs.HS_ERR_INVALID_ARG
+
+
 def test_binding_rejects_mis_sized_tensors_before_any_call():
     """The Python binding checks that argument shapes agree before it checks devices or calls
     the library, so a mis-sized buffer never reaches a kernel (no GPU needed: the tensors
