@@ -8,8 +8,9 @@ resident batch reads the paged device cache directly, otherwise KV is swapped in
   swap batch:      hs_resolve_topk(all rows) on the main stream, then for each wave r
                    (row r of every request): hs_swap_in on the copy stream, attention
                    of wave r on the main stream once that swap has landed; the swap of
-                   wave r+1 overlaps the attention of wave r.  hs_finalize_accepted
-                   closes the step when draft rows are verified.
+                   wave r+1 overlaps the attention of wave r, which is then sized for
+                   the CUs that swap leaves free (hs_sparse_decode_attn_cus).
+                   hs_finalize_accepted closes the step when draft rows are verified.
 
 The copy stream waits for the attention of wave r-2 before swapping wave r.  That is safe
 when capacity >= 2*topk and tick0 is above every stamp already in the state: wave r-1's
