@@ -247,10 +247,14 @@ class StepRig:
 
 
 def measure_step(rig, steps, warmup, b_host):
-    """W untimed steps, then K timed steps (each restored first, untimed).  Per step:
-    device time between events on the main stream (after it has waited for the copy
-    stream); per swap-in and attention launch: its own device time between events on its
-    own stream."""
+    """W untimed steps, then K timed steps (each restored first, untimed): device time
+    between events on the main stream, the second after it has waited for the copy stream.
+    The timed steps run the step exactly as a caller does, with no event inside it (an
+    event recorded between two launches on a stream is a packet of its own, and the
+    per-call events cost the step ≈50 µs).  Then K more steps record an event pair around
+    every swap-in, attention and finalize launch on the stream it runs on: those give each
+    launch's device time (the per-wave figures and the swap-in launch time of the
+    roofline), not the step time."""
     import numpy as np
     import torch
 
@@ -266,24 +270,28 @@ def measure_step(rig, steps, warmup, b_host):
         torch.cuda.synchronize()
         if first is None:
             first = rig.outputs()
-    step_ms, swap_us, attn_us, fin_us = [], [], [], []
-    for i in range(steps):
-        rig.restore()
-        torch.cuda.synchronize()
-        timing = {"swap": [(ev(), ev()) for _ in range(R)], "attn": [(ev(), ev()) for _ in range(R)],
-                  "finalize": (ev(), ev())}
-        e0, e1 = ev(), ev()
-        gpu_busy()
-        e0.record(main)
-        rig.run(timing)
-        main.wait_stream(step.copy_stream)
-        e1.record(main)
-        torch.cuda.synchronize()
-        step_ms.append(e0.elapsed_time(e1))
-        swap_us.append([a.elapsed_time(z) * 1e3 for a, z in timing["swap"]])
-        attn_us.append([a.elapsed_time(z) * 1e3 for a, z in timing["attn"]])
-        if rig.fin is not None:
-            fin_us.append(timing["finalize"][0].elapsed_time(timing["finalize"][1]) * 1e3)
+    step_ms, marked_ms, swap_us, attn_us, fin_us = [], [], [], [], []
+    for marked in (False, True):
+        for i in range(steps):
+            rig.restore()
+            torch.cuda.synchronize()
+            timing = {"swap": [(ev(), ev()) for _ in range(R)],
+                      "attn": [(ev(), ev()) for _ in range(R)],
+                      "finalize": (ev(), ev())} if marked else None
+            e0, e1 = ev(), ev()
+            gpu_busy()
+            e0.record(main)
+            rig.run(timing)
+            main.wait_stream(step.copy_stream)
+            e1.record(main)
+            torch.cuda.synchronize()
+            (marked_ms if marked else step_ms).append(e0.elapsed_time(e1))
+            if not marked:
+                continue
+            swap_us.append([a.elapsed_time(z) * 1e3 for a, z in timing["swap"]])
+            attn_us.append([a.elapsed_time(z) * 1e3 for a, z in timing["attn"]])
+            if rig.fin is not None:
+                fin_us.append(timing["finalize"][0].elapsed_time(timing["finalize"][1]) * 1e3)
     last = rig.outputs()
     if first is None:
         first = last
@@ -309,6 +317,9 @@ def measure_step(rig, steps, warmup, b_host):
         "workload": s.name, "rows_per_step": s.rows, "waves": R, "steps": steps, "warmup": warmup,
         "ms_per_step": ms, "step_ms_median": float(np.median(step_ms)),
         "step_ms_min": float(np.min(step_ms)), "step_ms_max": float(np.max(step_ms)),
+        "marked_steps_ms_mean": float(np.mean(marked_ms)),
+        "per_launch_timing": "per-launch figures (swap_*, attn_*, finalize_us_mean) come from "
+                             f"{steps} further steps with an event pair around each launch",
         "rows_per_s": s.rows / (ms / 1e3),
         "miss_bytes_per_step": total_miss, "wave_miss_bytes": wave_miss_bytes,
         "misses_per_row": float(miss.sum() / max(1, (valid > 0).sum())),
@@ -1059,8 +1070,8 @@ def main():
                    "rows_per_step": s.rows, "topk": s.topk, "heads": s.num_heads,
                    "timing": "per step: state restored (untimed), then device time between "
                              "events around resolve + 3 waves (swap-in on a copy stream under "
-                             "the previous wave's attention) + accept/finalize; ms_per_step = "
-                             "mean over the K timed steps"},
+                             "the previous wave's attention) + accept/finalize, with no event "
+                             "inside the step; ms_per_step = mean over the K timed steps"},
         "roofline": {"bound": "host_link", "achieved": achieved, "peak": HOST_LINK_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved / HOST_LINK_PEAK_GBS, "traffic": traffic,
                      "kernel": "swap_in_kernel (hs_swap_in): zero-copy gather of the missed "
@@ -1068,6 +1079,8 @@ def main():
                      "alg_bytes_per_launch": alg_per_launch,
                      "alg_bytes_read_and_write_per_launch": 2 * alg_per_launch,
                      "launch_us": head["swap_launch_us_mean"],
+                     "launch_us_from": "events around each swap-in launch on the copy stream, "
+                                       "in K steps run right after the timed ones",
                      "measured_B_host_GBps": b_host, "frac_of_B_host": achieved / b_host,
                      "peak_source": "PCIe 5.0 x16, 64 GB/s per direction (MI355X host interface)"},
         "hbm_roofline": {"bound": "hbm", "kernel": "attention dispatch of the step's last wave "

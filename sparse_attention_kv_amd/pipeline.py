@@ -156,11 +156,12 @@ class DecodeStep:
                  timing: Optional[dict] = None):
         """One swap-path step.  ``timing`` (optional): lists "swap" and "attn" of R
         (start, end) timing events each and a "finalize" pair, recorded around each call on
-        the stream it runs on (so their elapsed times are those calls' device durations)."""
+        the stream it runs on (so their elapsed times are those calls' device durations);
+        a kind left out is not recorded (each record is a packet on its stream)."""
         b, B, R = self.buf, self.B, self.R
 
         def mark(kind, r, i, stream):
-            if timing is not None:
+            if timing is not None and kind in timing:
                 ev = timing[kind][r] if r is not None else timing[kind]
                 ev[i].record(stream)
         main = torch.cuda.current_stream()
