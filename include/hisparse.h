@@ -247,6 +247,7 @@ hs_status hs_sparse_decode_attn(const void *q, const void *kv, int64_t kv_rows,
  *             keys); larger batches take one workgroup per unit and split.
  *   workspace the size hs_attn_workspace_bytes returns for the same sizes always suffices.
  *
+ * The fp32 path (dtype HS_F32) launches as the plain call does.
  * Errors: as hs_sparse_decode_attn; HS_ERR_INVALID_ARG for max_cus <= 0.
  */
 hs_status hs_sparse_decode_attn_cus(const void *q, const void *kv, int64_t kv_rows,
