@@ -80,6 +80,8 @@ int main() {
   expect("attn huge batch", hs_sparse_decode_attn(v, v, 10, p, 0x7fffffff, 0x7fffffe0, 576, 512, 2048, 0.1f, HS_BF16, v, nullptr, v, 1 << 30, nullptr), U);
   expect("attn huge topk", hs_sparse_decode_attn(v, v, 10, p, 4, 128, 576, 512, 0x7fffffff, 0.1f, HS_BF16, v, nullptr, v, 1 << 30, nullptr), U);
   expect("attn f32 d", hs_sparse_decode_attn(v, v, 10, p, 2, 4, 2048, 48, 16, 0.1f, HS_F32, v, nullptr, nullptr, 0, nullptr), U);
+  expect("cus zero", hs_sparse_decode_attn_cus(v, v, 10, p, 2, 128, 576, 512, 2048, 0.1f, HS_BF16, v, nullptr, v, 1 << 30, 0, nullptr), E);
+  expect("cus no workspace", hs_sparse_decode_attn_cus(v, v, 10, p, 2, 128, 576, 512, 2048, 0.1f, HS_BF16, v, nullptr, nullptr, 0, 128, nullptr), E);
   expect("noalloc scratch", hs_sparse_decode_attn_noalloc(v, v, 10, p, 256, 256, 576, 512, 4096, 0.1f, HS_BF16, v, nullptr, nullptr), HS_ERR_SCRATCH);
   expect("paged null table", hs_sparse_decode_attn_paged(v, v, 10, p, p, p, 1, nullptr, 4, 16, 16, 2, 128, 576, 512, 2048, 0.1f, HS_BF16, v, nullptr, v, 1 << 30, nullptr), E);
   expect("mixed f32", hs_sparse_decode_attn_mixed(v, v, 10, p, v, 10, p, p, 2, 128, 576, 512, 2048, 0.1f, HS_F32, v, nullptr, v, 1 << 30, nullptr), U);
@@ -106,6 +108,17 @@ int main() {
         } else if (ws != 0) {
           std::printf("FAIL plan %d %d %d: rejected (%d) but workspace %zu\n", r, h, k, st_, ws);
           ++failures;
+        }
+        // the plan for part of the GPU: accepted exactly when the whole-GPU one is, never
+        // more key splits (so the same workspace serves)
+        for (int32_t c : {1, 64, 128, 255, 256, 0x7fffffff}) {
+          int32_t hc = -1, sc = -1;
+          const int stc = hs_attn_plan_info_cus(r, h, 576, 512, k, HS_BF16, c, &hc, &sc);
+          if (stc != st_ || (stc == HS_OK && (!(hc == 32 || hc == 64 || hc == 128) || sc < 1 || sc > spl))) {
+            std::printf("FAIL plan cus %d %d %d %d: status %d heads/wg %d splits %d (whole %d)\n",
+                        r, h, k, c, stc, hc, sc, spl);
+            ++failures;
+          }
         }
       }
 
