@@ -326,3 +326,22 @@ def test_attn_cus_matches_oracle_and_plain_call(rows, cus, topk):
     assert_close(out_f64(out), out_f64(plain), BF16_TOL, f"cus {cus} vs plain")
     with pytest.raises(hs.HsError):
         hs.hs_sparse_decode_attn_cus(q, kv, idx, 1 / 24, 512, out, lse, ws, 0)
+
+
+# Plans with key-split counts that are not powers of two (the splits fill the CUs in one
+# round), on all three kernels; the last split of a row is shorter than the others.
+@pytest.mark.parametrize("rows,H,topk,plan", [(5, 128, 2048, (32, 11)), (9, 128, 2048, (32, 7)),
+                                              (5, 64, 3100, (32, 17)), (12, 256, 2048, (64, 5)),
+                                              (20, 256, 1000, (64, 3)), (72, 256, 3100, (128, 2))])
+def test_attn_uneven_split_counts(rows, H, topk, plan):
+    import sparse_attention_kv_amd as hs
+    assert hs.hs_attn_plan_info(rows, H, 576, 512, topk, torch.bfloat16) == plan
+    kv_rows = 7000
+    rng = np.random.default_rng(rows * 7 + H + topk)
+    q = _rand_bf16((rows, H, 576), 1000 + rows + H)
+    kv = _rand_bf16((kv_rows, 576), 1001 + rows + H)
+    idx = np.stack([rng.choice(kv_rows, topk, replace=False) for _ in range(rows)]).astype(np.int32)
+    idx[1, rng.random(topk) < 0.4] = -1
+    idx[2, topk // 3:] = -1  # only the leading splits hold keys
+    sample = sorted({0, 1, 2, rows // 2, rows - 1})
+    _check_sampled(q, kv, to_dev(idx), 1 / 24, 512, f"splits {plan}", sample)
