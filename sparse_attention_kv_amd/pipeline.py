@@ -196,7 +196,8 @@ class DecodeStep:
                 hs_sparse_decode_attn(q[lo:hi], state.hot_kv, b.hot_idx[lo:hi], scale, self.d_v,
                                       b.out[lo:hi], b.lse[lo:hi], b.workspace, stream=main)
             mark("attn", r, 1, main)
-            self.e_attn[r].record(main)
+            if r + (1 if serialize else 2) < R:  # a later swap-in waits for this attention
+                self.e_attn[r].record(main)
         if finalize is not None:
             mark("finalize", None, 0, main)
             hs_finalize_accepted(state, None, finalize["draft_ids"], finalize["new_kv"], R,
@@ -243,7 +244,8 @@ class DecodeStep:
             hs_sparse_decode_attn_mixed(q[lo:hi], kv_pool, b.slots_res[lo:hi], state.hot_kv,
                                         b.hot_idx[lo:hi], row_sel[lo:hi], scale, self.d_v,
                                         b.out[lo:hi], b.lse[lo:hi], b.workspace, stream=main)
-            self.e_attn[r].record(main)
+            if r + (1 if serialize else 2) < R:  # a later swap-in waits for this attention
+                self.e_attn[r].record(main)
 
 
 class ResidencyTracker:
