@@ -113,10 +113,10 @@ def test_swap_rejects_pageable_host_pool():
     assert e.value.status == hs.HS_ERR_INVALID_ARG
 
 
-def _pipeline_case(name, sample_rows_per_wave=6):
+def _pipeline_case(name, sample_rows_per_wave=6, **over):
     """Whole step through DecodeStep.run_swap (copy stream overlapped with attention)."""
     from sparse_attention_kv_amd.pipeline import DecodeStep
-    s, w = make(name)
+    s, w = make(name, **over)
     g = gpu_inputs(s, w)
     ost, gst, pool = _both_states(s, w, g)
     B, R = s.num_reqs, s.rows_per_req
@@ -206,6 +206,21 @@ def test_pipeline_step(name):
 
 def test_pipeline_step_with_finalize_full():
     _pipeline_case("mixed_finalize", sample_rows_per_wave=4)
+
+
+# The finalize step at other shapes: other batch sizes, verify-row counts, top-k and seeds;
+# hot buffers of at least 2 x top-k (waves overlapped, the attention beside each swap-in
+# planned for the CUs it leaves free) and of less (waves serialised).
+@pytest.mark.parametrize("over", [
+    dict(index=10, num_reqs=12, rows_per_req=4, topk=512, capacity=1024, bt_stride=256,
+         seq_rule=("uniform", 600, 16000), vocab=1000),
+    dict(index=11, num_reqs=24, rows_per_req=2, topk=300, capacity=500, bt_stride=128,
+         seq_rule=("loguniform", 200, 8000), vocab=4000),
+    dict(index=12, num_reqs=40, rows_per_req=3, topk=2048, capacity=4096, bt_stride=512,
+         seq_rule=("loguniform", 1024, 32768), vocab=2000),
+], ids=["12x4-k512", "24x2-k300-serial", "40x3-k2048"])
+def test_pipeline_step_with_finalize_varied(over):
+    _pipeline_case("mixed_finalize", sample_rows_per_wave=8, **over)
 
 
 @pytest.mark.parametrize("name,over", [
