@@ -359,6 +359,23 @@ hs_status hs_sparse_decode_attn_mixed(const void *q, const void *kv_a, int64_t k
                                       size_t workspace_bytes, void *stream);
 
 /*
+ * hs_sparse_decode_attn_mixed_cus -- hs_sparse_decode_attn_mixed planned for `max_cus`
+ * compute units, for a mixed batch whose attention runs beside the next wave's swap-in
+ * (P1 "1. 启动阶段": the hot buffer is filled on an async stream); as
+ * hs_sparse_decode_attn_cus is to hs_sparse_decode_attn (same results, the same workspace
+ * size serves).
+ * Errors: as hs_sparse_decode_attn_mixed; HS_ERR_INVALID_ARG for max_cus <= 0.
+ */
+hs_status hs_sparse_decode_attn_mixed_cus(const void *q, const void *kv_a, int64_t kv_a_rows,
+                                          const int32_t *indices_a, const void *kv_b,
+                                          int64_t kv_b_rows, const int32_t *indices_b,
+                                          const int32_t *row_sel, int32_t num_rows,
+                                          int32_t num_heads, int32_t d_qk, int32_t d_v,
+                                          int32_t topk, float scale, int32_t dtype, void *out,
+                                          float *lse, void *workspace, size_t workspace_bytes,
+                                          int32_t max_cus, void *stream);
+
+/*
  * hs_finalize_accepted -- P2 ④: the target verifies [anchor, drafts] in one causal pass;
  * row r's logits judge draft r+1; drafts are kept while they equal the target's greedy
  * choice; only the accepted prefix's KV is kept and the replacement (or bonus) token has

@@ -25,6 +25,7 @@ HS_BF16, HS_F32 = 0, 1
 
 EXPORTED = ("hs_resolve_topk", "hs_swap_in", "hs_sparse_decode_attn", "hs_sparse_decode_attn_paged",
             "hs_sparse_decode_attn_mixed", "hs_sparse_decode_attn_cus",
+            "hs_sparse_decode_attn_mixed_cus",
             "hs_attn_workspace_bytes", "hs_attn_plan_info", "hs_attn_plan_info_cus", "hs_finalize_accepted", "hs_backup_rows", "hs_apply_plan",
             "hs_append_accepted", "hs_host_read", "hs_sparse_decode_attn_noalloc",
             "hs_greedy_argmax",
@@ -68,6 +69,10 @@ def _load() -> ctypes.CDLL:
     lib.hs_sparse_decode_attn_mixed.argtypes = [vp, vp, i64, vp, vp, i64, vp, vp, i32, i32, i32,
                                                 i32, i32, f32, i32, vp, vp, vp, sz, vp]
     lib.hs_sparse_decode_attn_mixed.restype = i32
+    lib.hs_sparse_decode_attn_mixed_cus.argtypes = [vp, vp, i64, vp, vp, i64, vp, vp, i32, i32,
+                                                    i32, i32, i32, f32, i32, vp, vp, vp, sz, i32,
+                                                    vp]
+    lib.hs_sparse_decode_attn_mixed_cus.restype = i32
     lib.hs_attn_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32]
     lib.hs_attn_plan_info.argtypes = [i32, i32, i32, i32, i32, i32, vp, vp]
     lib.hs_attn_plan_info.restype = i32
@@ -534,8 +539,10 @@ def hs_sparse_decode_attn_mixed(q: torch.Tensor, kv_a: torch.Tensor, indices_a: 
                                 kv_b: torch.Tensor, indices_b: torch.Tensor,
                                 row_sel: torch.Tensor, scale: float, d_v: int, out: torch.Tensor,
                                 lse: Optional[torch.Tensor] = None,
-                                workspace: Optional[torch.Tensor] = None, stream=None):
-    """Attention whose rows read one of two caches (see include/hisparse.h)."""
+                                workspace: Optional[torch.Tensor] = None, stream=None,
+                                max_cus: Optional[int] = None):
+    """Attention whose rows read one of two caches (see include/hisparse.h); with
+    ``max_cus``, hs_sparse_decode_attn_mixed_cus (planned for that many compute units)."""
     i32 = torch.int32
     _attn_shapes(q, kv_a, indices_a, d_v, out, lse)
     _shape(kv_b.dim() == 2 and kv_b.shape[1] == q.shape[2], "kv_b rows must be d_qk wide")
@@ -550,10 +557,15 @@ def hs_sparse_decode_attn_mixed(q: torch.Tensor, kv_a: torch.Tensor, indices_a: 
     if indices_a.shape != indices_b.shape or indices_a.shape[0] != rows or row_sel.shape != (rows,):
         raise ValueError("indices_a, indices_b must be [rows, topk] and row_sel [rows]")
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check("hs_sparse_decode_attn_mixed", _lib.hs_sparse_decode_attn_mixed(
-        _ptr(q), _ptr(kv_a), kv_a.shape[0], _ptr(indices_a), _ptr(kv_b), kv_b.shape[0],
-        _ptr(indices_b), _ptr(row_sel), rows, heads, d_qk, d_v, indices_a.shape[1], float(scale),
-        _dtype_code(q.dtype), _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes, _stream(stream)))
+    args = (_ptr(q), _ptr(kv_a), kv_a.shape[0], _ptr(indices_a), _ptr(kv_b), kv_b.shape[0],
+            _ptr(indices_b), _ptr(row_sel), rows, heads, d_qk, d_v, indices_a.shape[1],
+            float(scale), _dtype_code(q.dtype), _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes)
+    if max_cus is None:
+        _check("hs_sparse_decode_attn_mixed", _lib.hs_sparse_decode_attn_mixed(*args,
+                                                                               _stream(stream)))
+    else:
+        _check("hs_sparse_decode_attn_mixed_cus", _lib.hs_sparse_decode_attn_mixed_cus(
+            *args, int(max_cus), _stream(stream)))
 
 
 

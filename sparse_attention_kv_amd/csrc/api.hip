@@ -295,6 +295,21 @@ hs_status hs_sparse_decode_attn_mixed(const void *q, const void *kv_a, int64_t k
                                       int32_t d_qk, int32_t d_v, int32_t topk, float scale,
                                       int32_t dtype, void *out, float *lse, void *workspace,
                                       size_t workspace_bytes, void *stream) {
+  return hs_sparse_decode_attn_mixed_cus(q, kv_a, kv_a_rows, indices_a, kv_b, kv_b_rows,
+                                         indices_b, row_sel, num_rows, num_heads, d_qk, d_v, topk,
+                                         scale, dtype, out, lse, workspace, workspace_bytes,
+                                         hs::kNumCUs, stream);
+}
+
+hs_status hs_sparse_decode_attn_mixed_cus(const void *q, const void *kv_a, int64_t kv_a_rows,
+                                          const int32_t *indices_a, const void *kv_b,
+                                          int64_t kv_b_rows, const int32_t *indices_b,
+                                          const int32_t *row_sel, int32_t num_rows,
+                                          int32_t num_heads, int32_t d_qk, int32_t d_v,
+                                          int32_t topk, float scale, int32_t dtype, void *out,
+                                          float *lse, void *workspace, size_t workspace_bytes,
+                                          int32_t max_cus, void *stream) {
+  if (max_cus <= 0) return HS_ERR_INVALID_ARG;
   if (num_rows < 0 || num_heads <= 0 || d_qk <= 0 || d_v <= 0 || topk <= 0 || kv_a_rows < 0 ||
       kv_b_rows < 0)
     return HS_ERR_INVALID_ARG;
@@ -308,7 +323,7 @@ hs_status hs_sparse_decode_attn_mixed(const void *q, const void *kv_a, int64_t k
   if (attn_too_large(num_rows, num_heads, topk)) return HS_ERR_UNSUPPORTED;
   if (!aligned16(q) || !aligned16(kv_a) || !aligned16(kv_b) || !aligned16(out))
     return HS_ERR_INVALID_ARG;
-  const hs::AttnPlan plan = hs::plan_attn_bf16(num_rows, num_heads, topk);
+  const hs::AttnPlan plan = hs::plan_attn_bf16(num_rows, num_heads, topk, max_cus);
   if (plan.workspace > 0 &&
       (workspace == nullptr || workspace_bytes < plan.workspace || !aligned16(workspace)))
     return HS_ERR_INVALID_ARG;

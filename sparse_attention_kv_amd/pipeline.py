@@ -241,9 +241,11 @@ class DecodeStep:
                        None if b.miss_pos is None else b.miss_pos[lo:hi], stream=copy)
             self.e_swap[r].record(copy)
             main.wait_event(self.e_swap[r])
+            beside = r + 1 < R and not serialize  # the next wave's swap-in runs beside it
             hs_sparse_decode_attn_mixed(q[lo:hi], kv_pool, b.slots_res[lo:hi], state.hot_kv,
                                         b.hot_idx[lo:hi], row_sel[lo:hi], scale, self.d_v,
-                                        b.out[lo:hi], b.lse[lo:hi], b.workspace, stream=main)
+                                        b.out[lo:hi], b.lse[lo:hi], b.workspace, stream=main,
+                                        max_cus=self.cus_beside_swap if beside else None)
             if r + (1 if serialize else 2) < R:  # a later swap-in waits for this attention
                 self.e_attn[r].record(main)
 

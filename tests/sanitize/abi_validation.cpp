@@ -84,6 +84,7 @@ int main() {
   expect("cus no workspace", hs_sparse_decode_attn_cus(v, v, 10, p, 2, 128, 576, 512, 2048, 0.1f, HS_BF16, v, nullptr, nullptr, 0, 128, nullptr), E);
   expect("noalloc scratch", hs_sparse_decode_attn_noalloc(v, v, 10, p, 256, 256, 576, 512, 4096, 0.1f, HS_BF16, v, nullptr, nullptr), HS_ERR_SCRATCH);
   expect("paged null table", hs_sparse_decode_attn_paged(v, v, 10, p, p, p, 1, nullptr, 4, 16, 16, 2, 128, 576, 512, 2048, 0.1f, HS_BF16, v, nullptr, v, 1 << 30, nullptr), E);
+  expect("mixed cus zero", hs_sparse_decode_attn_mixed_cus(v, v, 10, p, v, 10, p, p, 2, 128, 576, 512, 2048, 0.1f, HS_BF16, v, nullptr, v, 1 << 30, 0, nullptr), E);
   expect("mixed f32", hs_sparse_decode_attn_mixed(v, v, 10, p, v, 10, p, p, 2, 128, 576, 512, 2048, 0.1f, HS_F32, v, nullptr, v, 1 << 30, nullptr), U);
 
   // plan arithmetic over extreme sizes (no launch): workspace and plan must stay defined

@@ -21,25 +21,32 @@ def _rand_bf16(shape, seed):
     return torch.randn(shape, generator=gen).to(torch.bfloat16).to(dev())
 
 
-def _mixed(q, kv_a, ia, kv_b, ib, sel, scale=1 / 24):
+def _mixed(q, kv_a, ia, kv_b, ib, sel, scale=1 / 24, max_cus=None):
     import sparse_attention_kv_amd as hs
     rows, H, D = q.shape
     out = torch.full((rows, H, 512), float("nan"), dtype=q.dtype, device=dev())
     lse = torch.full((rows, H), float("nan"), dtype=torch.float32, device=dev())
     wsb = hs.hs_attn_workspace_bytes(rows, H, D, 512, ia.shape[1], q.dtype)
     ws = torch.empty((wsb,), dtype=torch.uint8, device=dev()) if wsb else None
-    hs.hs_sparse_decode_attn_mixed(q, kv_a, ia, kv_b, ib, sel, scale, 512, out, lse, ws)
+    hs.hs_sparse_decode_attn_mixed(q, kv_a, ia, kv_b, ib, sel, scale, 512, out, lse, ws,
+                                   max_cus=max_cus)
     torch.cuda.synchronize()
     return out, lse
 
 
-@pytest.mark.parametrize("rows,topk,sample", [(8, 2048, None), (40, 700, None),
-                                              (256, 600, [0, 1, 2, 3, 100, 255])])
-def test_mixed_attention_matches_oracle(rows, topk, sample):
-    """8 rows take the 32-head kernel, 40 the 64-head one, 256 the 128-head one."""
+@pytest.mark.parametrize("rows,topk,sample,cus", [(8, 2048, None, None), (40, 700, None, None),
+                                                  (256, 600, [0, 1, 2, 3, 100, 255], None),
+                                                  (8, 2048, None, 64), (128, 900, None, 128)])
+def test_mixed_attention_matches_oracle(rows, topk, sample, cus):
+    """8 rows take the 32-head kernel, 40 the 64-head one, 256 the 128-head one; with `cus`
+    the call is planned for that many compute units (8 rows: the 64-head kernel, 4 splits;
+    128 rows: the 128-head kernel, one split)."""
     import sparse_attention_kv_amd as hs
     H = 128
-    assert hs.hs_attn_plan_info(rows, H, 576, 512, topk, torch.bfloat16)[0] == {8: 32, 40: 64, 256: 128}[rows]
+    if cus is None:
+        assert hs.hs_attn_plan_info(rows, H, 576, 512, topk, torch.bfloat16)[0] == {8: 32, 40: 64, 256: 128}[rows]
+    else:
+        assert hs.hs_attn_plan_info_cus(rows, H, 576, 512, topk, torch.bfloat16, cus) == {64: (64, 4), 128: (128, 1)}[cus]
     rng = np.random.default_rng(rows)
     q = _rand_bf16((rows, H, 576), rows)
     kv_a = _rand_bf16((3000, 576), rows + 1)
@@ -50,8 +57,8 @@ def test_mixed_attention_matches_oracle(rows, topk, sample):
     ib[2, rng.random(topk) < 0.2] = 2500 + 5  # past kv_b end
     sel = (rng.random(rows) < 0.5).astype(np.int32)
     sel[:4] = [0, 1, 1, 0]
-    log(f"mixed attention rows={rows} topk={topk}")
-    out, lse = _mixed(q, kv_a, to_dev(ia), kv_b, to_dev(ib), to_dev(sel))
+    log(f"mixed attention rows={rows} topk={topk} cus={cus}")
+    out, lse = _mixed(q, kv_a, to_dev(ia), kv_b, to_dev(ib), to_dev(sel), max_cus=cus)
     rs = list(range(rows)) if sample is None else sample
     ref, rlse = oracle.sparse_decode_attn_mixed(raw(q.cpu()[rs]), raw(kv_a.cpu()), ia[rs],
                                                 raw(kv_b.cpu()), ib[rs], sel[rs], 1 / 24, 512)
