@@ -106,6 +106,9 @@ def stored_int(profile, kind, key):
         return None
 
 
+STEP_SPIN_US = 1000.0
+
+
 def gpu_busy(us=100.0):
     """Keep the GPU busy for about ``us`` microseconds, so that an event recorded after it
     times the device work of the calls enqueued meanwhile, not their host-side marshalling."""
@@ -279,7 +282,10 @@ def measure_step(rig, steps, warmup, b_host):
                       "attn": [(ev(), ev()) for _ in range(R)],
                       "finalize": (ev(), ev())} if marked else None
             e0, e1 = ev(), ev()
-            gpu_busy()
+            # a spin long enough that the host has enqueued the whole step (≈15 calls)
+            # before the first event: a host-side pause while enqueueing cannot then show
+            # up as device idle time inside the step
+            gpu_busy(STEP_SPIN_US)
             e0.record(main)
             rig.run(timing)
             main.wait_stream(step.copy_stream)
