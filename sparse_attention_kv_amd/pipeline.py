@@ -171,9 +171,11 @@ class DecodeStep:
                         b.slots, b.valid)
         self.e_resolve.record(main)
         copy.wait_event(self.e_resolve)
-        if finalize is not None:
-            # the greedy choice needs only the logits: it runs while wave 0's swap-in holds
-            # the host link, and finalize later reads its result
+        # The greedy choice needs only the logits; finalize reads its result at the end.  It
+        # runs beside a swap-in: after wave 0's attention when another wave follows (then
+        # wave 0's swap-in does not start behind its 384 workgroups), else after resolve.
+        argmax_after = 0 if R > 1 else -1
+        if finalize is not None and argmax_after < 0:
             hs_greedy_argmax(finalize["logits"], b.argmax, stream=main)
         for r in range(R):
             lo, hi = r * B, (r + 1) * B
@@ -198,6 +200,8 @@ class DecodeStep:
             mark("attn", r, 1, main)
             if r + (1 if serialize else 2) < R:  # a later swap-in waits for this attention
                 self.e_attn[r].record(main)
+            if finalize is not None and r == argmax_after:
+                hs_greedy_argmax(finalize["logits"], b.argmax, stream=main)
         if finalize is not None:
             mark("finalize", None, 0, main)
             hs_finalize_accepted(state, None, finalize["draft_ids"], finalize["new_kv"], R,
