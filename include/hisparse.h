@@ -9,7 +9,8 @@
  *                         victim choice, copy of the misses from the pinned host pool
  *   hs_sparse_decode_attn attention over only the selected latent KV rows
  *                         (_paged: positions resolved in the same call; _mixed: each
- *                         row reads one of two caches)
+ *                         row reads one of two caches; _cus: planned for part of the
+ *                         GPU, beside the next wave's swap-in)
  *   hs_finalize_accepted  greedy acceptance of the draft rows, then keep exactly the
  *                         target-verified prefix's KV (host pool + hot buffer)
  *
@@ -34,7 +35,8 @@
  *       build_offload_command (per-batch residency).
  *
  * Conventions for every call:
- *   - All pointers are caller-owned; the library allocates nothing and keeps no state.
+ *   - All pointers are caller-owned; the library allocates nothing and keeps no state
+ *     (hs_sparse_decode_attn_noalloc's fixed scratch array aside).
  *     Pointers are DEVICE pointers unless marked HOST or PINNED HOST.
  *   - Every call is asynchronous on `stream` (a hipStream_t; NULL = the null stream) and
  *     returns after the launches are queued.  Validation failures return before any
